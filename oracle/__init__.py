@@ -1,0 +1,22 @@
+"""fp64 CPU oracle for split-KV single-query decode attention.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or link
+this package: only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline
+leg of ``bench.py`` use it. It shares no code with the HIP library; both sides
+consume the same seeded bf16 bytes from ``workloads``.
+
+Every function is plain NumPy in float64, written from the definition the pages
+give (tinydecode README, "how the decode step is put together"; llm-decode-cuda,
+attention section and design notes). Where the pages leave a step open the
+reading taken is stated in the function's docstring.
+"""
+from .attention import (  # noqa: F401
+    bf16_bits_to_f64,
+    decode_attention,
+    decode_attention_f64,
+    chunk_attention,
+    chunk_attention_f64,
+    split_kv_attention_f64,
+    kv_head_of,
+)
+from .bf16 import bf16_bracket, f64_to_bf16_bits_rne  # noqa: F401

@@ -1,0 +1,156 @@
+"""Seeded synthetic inputs for split-KV decode attention.
+
+This module only draws random numbers and lays them out; it holds none of the
+attention arithmetic. Both the fp64 oracle (through the tests) and the HIP path
+consume exactly the bytes produced here.
+
+Shapes follow the models the pages measure or name:
+
+* SmolLM2-360M (15 query heads, 5 kv heads, head dim 64, 32 layers): the model
+  of the llm-decode-cuda write-up, whose KV cache is laid out per layer as
+  [sequence][kv_head][position][64] (design notes of that page).
+* TinyLlama-1.1B (32/4 heads, dim 64, 22 layers) and Llama-3 shapes: the models
+  tinydecode loads (tinydecode README, "using it").
+* Llama-3.2-3B (24/8 heads, dim 128) for the speculative verify chunk of k+1
+  query tokens (tinydecode README, "speculative decoding").
+
+The pages measure whole models on real text; here every tensor is bf16 drawn
+from N(0, 1) (fp32 normal samples rounded to nearest-even bf16), which stands in
+for real activations. Cache slots at or past a sequence's length hold random
+data too, unless a test overwrites them.
+
+Seeds: seed = 100000*cfg + 10*layer + t with t = 1 (q), 2 (K), 3 (V),
+4 (outlier mask), 5 (lengths).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+import math
+
+import numpy as np
+import torch
+
+__all__ = [
+    "Workload", "CONFIGS", "bf16_randn", "make_case", "make_config",
+    "seed_for", "bf16_scale", "BF16_NAN",
+]
+
+# A quiet-NaN bf16 pattern, used by tests to poison cache slots that must never be read.
+BF16_NAN = 0x7FC0
+
+T_Q, T_K, T_V, T_OUTLIER, T_LENS = 1, 2, 3, 4, 5
+
+
+def seed_for(cfg: int, layer: int, t: int) -> int:
+    return 100000 * cfg + 10 * layer + t
+
+
+def bf16_randn(shape, seed: int) -> np.ndarray:
+    """bf16 bit patterns (uint16) of N(0,1) samples from a seeded CPU generator."""
+    g = torch.Generator().manual_seed(int(seed))
+    x = torch.randn(tuple(shape), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    return x.view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_scale(x_bits: np.ndarray, mask: np.ndarray, factor: float) -> np.ndarray:
+    """Multiply the bf16 values selected by ``mask`` by ``factor`` (a power of two: exact)."""
+    t = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).float()
+    m = torch.from_numpy(np.broadcast_to(mask, t.shape).copy())
+    t = torch.where(m, t * factor, t)
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One of the five measured shapes."""
+    cfg: int
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    S_max: int
+    lens: tuple            # candidate lengths (decode) or context lengths (chunk)
+    layers: int = 1
+    T: int = 1             # query tokens per sequence (chunk/verify when > 1)
+    chunk: int = 0         # keys per split tile; 0 = library default
+    outlier_frac: float = 0.0
+    outlier_factor: float = 8.0
+    ragged: bool = False   # lengths drawn per sequence from U[1, S_max]
+    notes: str = field(default="", compare=False)
+
+    @property
+    def G(self) -> int:
+        return self.Hq // self.Hkv
+
+    @property
+    def scale(self) -> float:
+        # the softmax scale travels through the C ABI as fp32
+        return float(np.float32(1.0 / math.sqrt(self.D)))
+
+
+CONFIGS = {
+    1: Workload(1, "smollm2-360m-single-call", B=1, Hq=15, Hkv=5, D=64, S_max=128,
+                lens=(64,), chunk=32,
+                notes="one call, fp32 and bf16 output"),
+    2: Workload(2, "smollm2-360m-32-layer-decode", B=1, Hq=15, Hkv=5, D=64, S_max=4096,
+                lens=(64, 1024, 2048, 4096), layers=32,
+                notes="32 independent calls per step, one graph replay"),
+    3: Workload(3, "tinyllama-1.1b-22-layer-decode", B=1, Hq=32, Hkv=4, D=64, S_max=8192,
+                lens=(1024, 4096, 8192), layers=22, outlier_frac=0.05,
+                notes="5% of keys scaled x8"),
+    4: Workload(4, "llama3-8b-batched-ragged-decode", B=8, Hq=32, Hkv=8, D=128, S_max=32768,
+                lens=(), ragged=True,
+                notes="seq_lens ~ U[1, 32768] per sequence"),
+    5: Workload(5, "llama3.2-3b-verify-chunk", B=1, Hq=24, Hkv=8, D=128, S_max=16384,
+                lens=(8192,), T=6,
+                notes="T = k+1 = 6 query tokens on 8192 keys of context"),
+}
+
+
+def make_case(B, Hq, Hkv, D, S_max, lens, *, T=1, seed=0, outlier_frac=0.0,
+              outlier_factor=8.0):
+    """Random bf16 q/K/V for arbitrary shapes.
+
+    Returns a dict with bf16 bit arrays ``q`` ([B,Hq,D] when T == 1, else
+    [B,T,Hq,D]), ``k`` and ``v`` ([B,Hkv,S_max,D]), int32 ``lens`` [B] and the
+    fp32 ``scale`` 1/sqrt(D).
+    """
+    qshape = (B, Hq, D) if T == 1 else (B, T, Hq, D)
+    q = bf16_randn(qshape, seed * 10 + T_Q)
+    k = bf16_randn((B, Hkv, S_max, D), seed * 10 + T_K)
+    v = bf16_randn((B, Hkv, S_max, D), seed * 10 + T_V)
+    if outlier_frac > 0:
+        g = torch.Generator().manual_seed(int(seed * 10 + T_OUTLIER))
+        mask = (torch.rand((B, Hkv, S_max), generator=g) < outlier_frac).numpy()
+        k = bf16_scale(k, mask[..., None], outlier_factor)
+    lens = np.asarray(lens, dtype=np.int32).reshape(B)
+    return {"q": q, "k": k, "v": v, "lens": lens,
+            "scale": float(np.float32(1.0 / math.sqrt(D)))}
+
+
+def ragged_lens(cfg: int, B: int, S_max: int, layer: int = 0) -> np.ndarray:
+    g = torch.Generator().manual_seed(seed_for(cfg, layer, T_LENS))
+    return torch.randint(1, S_max + 1, (B,), generator=g, dtype=torch.int64).numpy().astype(np.int32)
+
+
+def make_config(cfg: int, layer: int = 0, n: int | None = None) -> dict:
+    """Inputs of workload ``cfg`` for one layer.
+
+    ``n`` picks the sequence (decode) or context (chunk) length; by default the
+    largest listed length, or ragged per-sequence lengths for workload 4.
+    """
+    w = CONFIGS[cfg]
+    qshape = (w.B, w.Hq, w.D) if w.T == 1 else (w.B, w.T, w.Hq, w.D)
+    q = bf16_randn(qshape, seed_for(cfg, layer, T_Q))
+    k = bf16_randn((w.B, w.Hkv, w.S_max, w.D), seed_for(cfg, layer, T_K))
+    v = bf16_randn((w.B, w.Hkv, w.S_max, w.D), seed_for(cfg, layer, T_V))
+    if w.outlier_frac > 0:
+        g = torch.Generator().manual_seed(seed_for(cfg, layer, T_OUTLIER))
+        mask = (torch.rand((w.B, w.Hkv, w.S_max), generator=g) < w.outlier_frac).numpy()
+        k = bf16_scale(k, mask[..., None], w.outlier_factor)
+    if w.ragged:
+        lens = ragged_lens(cfg, w.B, w.S_max, layer)
+    else:
+        lens = np.full((w.B,), max(w.lens) if n is None else n, dtype=np.int32)
+    return {"q": q, "k": k, "v": v, "lens": lens, "scale": w.scale, "workload": w}
