@@ -1,0 +1,144 @@
+/*
+ * libdecattn — split-KV single-query decode attention ("flash-decoding") for
+ * AMD Instinct MI355X (gfx950), as a plain C ABI.
+ *
+ * The operation (tinydecode README, "how the decode step is put together"):
+ * for every batch row b and query head h, with G = Hq / Hkv query heads per kv
+ * head and kvh = h / G,
+ *
+ *     out[b,h,:] = sum_{j < n_b} softmax_j(scale * <q[b,h,:], K[b,kvh,j,:]>) V[b,kvh,j,:]
+ *
+ * where n_b = seq_lens[b] is read on the device. The work is split over tiles
+ * of `chunk` keys: each workgroup takes one (b, kvh, chunk) tile, serves all G
+ * query heads of that kv head and writes partial softmax state (m, l, acc);
+ * a second kernel merges the tiles with the log-sum-exp rule (llm-decode-cuda,
+ * attention section). The grid depends only on S_max, never on seq_lens, and
+ * tiles past a row's length exit at once, so a call can be captured in a
+ * hipGraph and replayed after seq_lens changes on the device.
+ *
+ * Conventions shared by every entry point
+ *  - Pointers are DEVICE pointers owned by the caller (q, caches, lengths,
+ *    out, workspace), except where a comment says otherwise. The library
+ *    allocates nothing, keeps no device state and never synchronizes; every
+ *    launch is asynchronous on `stream` (a hipStream_t; NULL = null stream).
+ *  - bf16 tensors are raw bf16 bit patterns (uint16), contiguous row-major,
+ *    16-byte aligned. The KV cache of one layer is [B][Hkv][S_max][D] (one
+ *    layer's slice of the [layer][sequence][kv_head][position][dim] layout of
+ *    llm-decode-cuda's design notes).
+ *  - Arguments are checked on the host before anything is launched; a failed
+ *    check returns a status and launches nothing. Device-resident lengths are
+ *    not validated (that would need a host sync): the kernels clamp them to
+ *    [0, S_max], and a row with no keys outputs zeros.
+ *  - Supported: D in {64, 128}; G = Hq / Hkv in 1..8; T in 1..16; chunk 0
+ *    (library default) or a power of two in [16, 2^20] (a chunk >= S_max
+ *    means one tile per row).
+ *  - Errors are returned, never thrown; no C++ exception crosses this ABI.
+ */
+#ifndef DECATTN_H
+#define DECATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DECATTN_ABI_VERSION 1
+
+typedef enum {
+    DECATTN_OK = 0,
+    DECATTN_ERR_INVALID_ARG = 1,   /* null pointer, bad dimension, misalignment, Hq % Hkv != 0 */
+    DECATTN_ERR_UNSUPPORTED = 2,   /* D, G, T or chunk outside the supported set */
+    DECATTN_ERR_WORKSPACE = 3,     /* workspace smaller than decattn_workspace_bytes() */
+    DECATTN_ERR_HIP = 4            /* the HIP runtime rejected a launch */
+} decattn_status;
+
+typedef enum {
+    DECATTN_OUT_BF16 = 0,          /* fp32 result rounded to nearest-even bf16 */
+    DECATTN_OUT_F32 = 1
+} decattn_out_dtype;
+
+/* DECATTN_ABI_VERSION of the built library. */
+int decattn_abi_version(void);
+
+/* Static, NUL-terminated description of a status code (unknown codes included). */
+const char* decattn_status_str(int status);
+
+/* Keys per tile the library picks when `chunk` is 0, for these shapes.
+ * Returns 0 when the shapes are invalid or unsupported. */
+int decattn_default_chunk(int B, int T, int Hq, int Hkv, int D, int S_max);
+
+/* Bytes of device workspace a call with these shapes needs (T = 1 for decode):
+ * the partial state of every tile, B*T*Hq*ceil(S_max/chunk)*(D+2)*4 bytes plus
+ * alignment. Returns 0 when the shapes are invalid or unsupported. */
+size_t decattn_workspace_bytes(int B, int T, int Hq, int Hkv, int D, int S_max, int chunk);
+
+/* Single-query decode attention (the flash-decoding step of tinydecode's
+ * README and llm-decode-cuda's attention section).
+ *   q          bf16 [B][Hq][D]
+ *   k_cache    bf16 [B][Hkv][S_max][D]
+ *   v_cache    bf16 [B][Hkv][S_max][D]
+ *   seq_lens   int32 [B], device; row b attends keys j < seq_lens[b]
+ *   scale      softmax scale (typically 1/sqrt(D)), applied to q.k
+ *   out        [B][Hq][D], bf16 or fp32 per out_dtype
+ *   workspace  >= decattn_workspace_bytes(B, 1, Hq, Hkv, D, S_max, chunk) bytes,
+ *              16-byte aligned; overwritten, may be reused between calls on the
+ *              same stream
+ *   chunk      keys per split tile; 0 = decattn_default_chunk()
+ * Launches two kernels (partial tiles, then the merge) on `stream`. */
+int decode_attn(const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* seq_lens,
+                int B, int Hq, int Hkv, int D, int S_max, float scale,
+                void* out, int out_dtype,
+                void* workspace, size_t workspace_bytes, int chunk,
+                void* stream);
+
+/* Causal multi-query "chunk" attention for verifying T speculative tokens
+ * (tinydecode README, "speculative decoding": the verify pass runs k+1 tokens
+ * on top of the existing context, reading the cache once for all of them).
+ *   q          bf16 [B][T][Hq][D]
+ *   ctx_lens   int32 [B], device; query token i of row b attends keys
+ *              j < ctx_lens[b] + i + 1 (the T tokens' own K/V must already be
+ *              at positions ctx .. ctx+T-1; the caller keeps ctx + T <= S_max,
+ *              and the kernels clamp every limit to S_max)
+ *   out        [B][T][Hq][D]
+ *   workspace  >= decattn_workspace_bytes(B, T, Hq, Hkv, D, S_max, chunk)
+ * Other arguments as decode_attn. Row (i, h) is bit-identical to decode_attn
+ * on the same cache with seq_lens = ctx + i + 1 and the same chunk. */
+int chunk_attn(const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* ctx_lens,
+               int B, int T, int Hq, int Hkv, int D, int S_max, float scale,
+               void* out, int out_dtype,
+               void* workspace, size_t workspace_bytes, int chunk,
+               void* stream);
+
+/* The two phases of decode_attn / chunk_attn as separate launches, for callers
+ * that time them apart or merge partial state produced elsewhere.
+ * `causal` = 0 gives decode (T must be 1, lens = seq_lens); 1 gives chunk
+ * (lens = ctx_lens). attn_partial writes the workspace; attn_merge reads it and
+ * must be given the same shapes, lens, causal flag and chunk. */
+int attn_partial(const void* q, const void* k_cache, const void* v_cache,
+                 const int32_t* lens,
+                 int B, int T, int Hq, int Hkv, int D, int S_max, float scale, int causal,
+                 void* workspace, size_t workspace_bytes, int chunk,
+                 void* stream);
+
+int attn_merge(const int32_t* lens,
+               int B, int T, int Hq, int Hkv, int D, int S_max, int causal,
+               void* out, int out_dtype,
+               void* workspace, size_t workspace_bytes, int chunk,
+               void* stream);
+
+/* Measurement helpers (the streaming-read probe of llm-decode-cuda's roofline
+ * section). decattn_probe_read reads `bytes` (a multiple of 16) from `buf`
+ * with 16-byte loads and writes at most 4 bytes to `sink`; decattn_probe_copy
+ * copies `bytes` (a multiple of 16) from src to dst. Both 16-byte aligned. */
+int decattn_probe_read(const void* buf, size_t bytes, void* sink, void* stream);
+int decattn_probe_copy(void* dst, const void* src, size_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DECATTN_H */

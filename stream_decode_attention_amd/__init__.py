@@ -1,0 +1,203 @@
+"""Python binding of libdecattn (split-KV decode attention for MI355X).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libdecattn.so, reached through its C ABI (include/decattn.h) with
+ctypes. PyTorch supplies device memory and the current stream. If the library
+has not been built, every call raises; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "DecattnError", "load_library", "abi_version", "status_str", "default_chunk",
+    "workspace_bytes", "decode_attn", "chunk_attn", "attn_partial", "attn_merge",
+    "probe_read", "probe_copy", "OUT_BF16", "OUT_F32", "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdecattn.so")
+OUT_BF16, OUT_F32 = 0, 1
+_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small", 4: "HIP error"}
+
+_lib: Optional[ctypes.CDLL] = None
+
+_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+
+_SIGNATURES = {
+    "decattn_abi_version": ([], _i),
+    "decattn_status_str": ([_i], ctypes.c_char_p),
+    "decattn_default_chunk": ([_i] * 6, _i),
+    "decattn_workspace_bytes": ([_i] * 7, _sz),
+    "decode_attn": ([_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _i, _vp, _sz, _i, _vp], _i),
+    "chunk_attn": ([_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp, _i, _vp, _sz, _i, _vp], _i),
+    "attn_partial": ([_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _i, _vp], _i),
+    "attn_merge": ([_vp, _i, _i, _i, _i, _i, _i, _i, _vp, _i, _vp, _sz, _i, _vp], _i),
+    "decattn_probe_read": ([_vp, _sz, _vp, _vp], _i),
+    "decattn_probe_copy": ([_vp, _vp, _sz, _vp], _i),
+}
+
+
+class DecattnError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {status_str(status)} (status {status})")
+        self.status = status
+
+
+def load_library() -> ctypes.CDLL:
+    """The loaded libdecattn.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m stream_decode_attention_amd.build` "
+                "(or __graft_entry__.build()); there is no non-HIP fallback")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = lib
+    return _lib
+
+
+def abi_version() -> int:
+    return load_library().decattn_abi_version()
+
+
+def status_str(status: int) -> str:
+    try:
+        return load_library().decattn_status_str(status).decode()
+    except Exception:
+        return _STATUS.get(status, "unknown status")
+
+
+def default_chunk(B: int, T: int, Hq: int, Hkv: int, D: int, S_max: int) -> int:
+    return load_library().decattn_default_chunk(B, T, Hq, Hkv, D, S_max)
+
+
+def workspace_bytes(B: int, T: int, Hq: int, Hkv: int, D: int, S_max: int, chunk: int = 0) -> int:
+    return load_library().decattn_workspace_bytes(B, T, Hq, Hkv, D, S_max, chunk)
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise DecattnError(fn, status)
+
+
+def _ptr(t: torch.Tensor, name: str, dtypes) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _stream(stream, dev) -> int:
+    if stream is None:
+        return torch.cuda.current_stream(dev).cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _out_dtype(out: torch.Tensor) -> int:
+    if out.dtype == torch.float32:
+        return OUT_F32
+    if out.dtype in _BF16:
+        return OUT_BF16
+    raise TypeError(f"out has dtype {out.dtype}; expected float32 or bfloat16")
+
+
+def decode_attn(q, k_cache, v_cache, seq_lens, scale: float, out, workspace, chunk: int = 0,
+                stream=None):
+    """out[b,h] = softmax(scale q[b,h].K[b,h//G,:n_b]^T) V[b,h//G,:n_b]; see include/decattn.h.
+
+    q bf16 [B,Hq,D]; caches bf16 [B,Hkv,S_max,D]; seq_lens int32 [B] (device);
+    out fp32 or bf16 [B,Hq,D]; workspace uint8 device tensor of at least
+    workspace_bytes(B, 1, Hq, Hkv, D, S_max, chunk) bytes.
+    """
+    B, Hq, D = q.shape
+    _, Hkv, S_max, Dk = k_cache.shape
+    if Dk != D or tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(out.shape) != (B, Hq, D) \
+            or k_cache.shape[0] != B or tuple(seq_lens.shape) != (B,):
+        raise ValueError("shape mismatch between q, caches, seq_lens and out")
+    st = load_library().decode_attn(
+        _ptr(q, "q", _BF16), _ptr(k_cache, "k_cache", _BF16), _ptr(v_cache, "v_cache", _BF16),
+        _ptr(seq_lens, "seq_lens", (torch.int32,)), B, Hq, Hkv, D, S_max, float(scale),
+        _ptr(out, "out", (torch.float32,) + _BF16), _out_dtype(out),
+        _ptr(workspace, "workspace", (torch.uint8,)), workspace.numel(), int(chunk),
+        _stream(stream, q.device))
+    _check("decode_attn", st)
+    return out
+
+
+def chunk_attn(q, k_cache, v_cache, ctx_lens, scale: float, out, workspace, chunk: int = 0,
+               stream=None):
+    """Causal verify attention: q bf16 [B,T,Hq,D]; token i attends keys j < ctx_lens[b]+i+1."""
+    B, T, Hq, D = q.shape
+    _, Hkv, S_max, Dk = k_cache.shape
+    if Dk != D or tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(out.shape) != (B, T, Hq, D) \
+            or k_cache.shape[0] != B or tuple(ctx_lens.shape) != (B,):
+        raise ValueError("shape mismatch between q, caches, ctx_lens and out")
+    st = load_library().chunk_attn(
+        _ptr(q, "q", _BF16), _ptr(k_cache, "k_cache", _BF16), _ptr(v_cache, "v_cache", _BF16),
+        _ptr(ctx_lens, "ctx_lens", (torch.int32,)), B, T, Hq, Hkv, D, S_max, float(scale),
+        _ptr(out, "out", (torch.float32,) + _BF16), _out_dtype(out),
+        _ptr(workspace, "workspace", (torch.uint8,)), workspace.numel(), int(chunk),
+        _stream(stream, q.device))
+    _check("chunk_attn", st)
+    return out
+
+
+def attn_partial(q, k_cache, v_cache, lens, scale: float, workspace, causal: bool = False,
+                 chunk: int = 0, stream=None):
+    """First phase only: per-tile partial softmax state into ``workspace``."""
+    if q.dim() == 3:
+        B, Hq, D = q.shape
+        T = 1
+    else:
+        B, T, Hq, D = q.shape
+    _, Hkv, S_max, _ = k_cache.shape
+    st = load_library().attn_partial(
+        _ptr(q, "q", _BF16), _ptr(k_cache, "k_cache", _BF16), _ptr(v_cache, "v_cache", _BF16),
+        _ptr(lens, "lens", (torch.int32,)), B, T, Hq, Hkv, D, S_max, float(scale), int(bool(causal)),
+        _ptr(workspace, "workspace", (torch.uint8,)), workspace.numel(), int(chunk),
+        _stream(stream, q.device))
+    _check("attn_partial", st)
+
+
+def attn_merge(lens, out, workspace, *, T: int, Hq: int, Hkv: int, S_max: int, causal: bool = False,
+               chunk: int = 0, stream=None):
+    """Second phase only: log-sum-exp merge of ``workspace`` into ``out``."""
+    B = lens.shape[0]
+    D = out.shape[-1]
+    st = load_library().attn_merge(
+        _ptr(lens, "lens", (torch.int32,)), B, T, Hq, Hkv, D, S_max, int(bool(causal)),
+        _ptr(out, "out", (torch.float32,) + _BF16), _out_dtype(out),
+        _ptr(workspace, "workspace", (torch.uint8,)), workspace.numel(), int(chunk),
+        _stream(stream, out.device))
+    _check("attn_merge", st)
+
+
+def probe_read(buf: torch.Tensor, sink: torch.Tensor, stream=None):
+    """Stream-read every byte of ``buf`` (16-byte loads); writes at most 4 bytes of ``sink``."""
+    st = load_library().decattn_probe_read(buf.data_ptr(), buf.numel() * buf.element_size(),
+                                           sink.data_ptr(), _stream(stream, buf.device))
+    _check("decattn_probe_read", st)
+
+
+def probe_copy(dst: torch.Tensor, src: torch.Tensor, stream=None):
+    st = load_library().decattn_probe_copy(dst.data_ptr(), src.data_ptr(),
+                                           src.numel() * src.element_size(), _stream(stream, src.device))
+    _check("decattn_probe_copy", st)

@@ -1,0 +1,261 @@
+// libdecattn host side: argument checks, launch shapes and the C ABI.
+//
+// The C ABI is declared in include/decattn.h. Nothing here allocates device
+// memory, synchronizes or keeps state, so every entry point can be captured in
+// a hipGraph; all checks happen before the first launch.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/decattn.h"
+#include "merge_kernel.hpp"
+#include "partial_kernel.hpp"
+#include "probe_kernel.hpp"
+
+namespace decattn {
+namespace {
+
+constexpr int kMaxG = 8;
+constexpr int kMaxT = 16;
+constexpr int kMaxRowsPerWave = 8;
+constexpr int kMaxWavesPerBlock = 8;       // matches __launch_bounds__(512)
+constexpr size_t kMaxLdsBytes = 64 * 1024;
+constexpr int kMinChunk = 16;
+constexpr int kMaxChunk = 1 << 20;
+constexpr size_t kAlign = 256;
+
+bool is_pow2(long long x) { return x > 0 && (x & (x - 1)) == 0; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Plan {
+    int B, T, Hq, Hkv, G, D, S_max, chunk, NC, RT;
+    int R, NR, nwk, rg_per_block, n_row_blocks;
+    size_t ml_bytes, acc_bytes, total_bytes, lds_bytes;
+};
+
+int pick_default_chunk(int B, int Hkv, int S_max) {
+    // Enough tiles to occupy the 256 compute units several times over while
+    // S_max is the only length the host knows; larger tiles cut partial-state
+    // traffic (about G*(D+2)*4 bytes per tile against 4*D bytes per key).
+    int c = 256;
+    while (c > 32 && (long long)B * Hkv * ((S_max + c - 1) / c) < 2048) c >>= 1;
+    return c;
+}
+
+// Fills `pl` for the given shapes; returns a status. No pointer is touched.
+int make_plan(int B, int T, int Hq, int Hkv, int D, int S_max, int chunk, Plan* pl) {
+    if (B <= 0 || T <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || S_max <= 0) return DECATTN_ERR_INVALID_ARG;
+    if (Hq % Hkv != 0) return DECATTN_ERR_INVALID_ARG;
+    if (D != 64 && D != 128) return DECATTN_ERR_UNSUPPORTED;
+    const int G = Hq / Hkv;
+    if (G > kMaxG || T > kMaxT) return DECATTN_ERR_UNSUPPORTED;
+    if (chunk == 0) chunk = pick_default_chunk(B, Hkv, S_max);
+    // a chunk >= S_max gives one tile per row
+    if (chunk < kMinChunk || chunk > kMaxChunk || !is_pow2(chunk)) return DECATTN_ERR_UNSUPPORTED;
+    const long long nc = ((long long)S_max + chunk - 1) / chunk;
+    if ((long long)B * Hkv * S_max * (long long)D > (1LL << 46)) return DECATTN_ERR_UNSUPPORTED;
+    if (B > 65535 || nc > 0x7FFFFFFF || (long long)B * T * Hq > 0x7FFFFFFF) return DECATTN_ERR_UNSUPPORTED;
+
+    Plan p{};
+    p.B = B; p.T = T; p.Hq = Hq; p.Hkv = Hkv; p.G = G; p.D = D; p.S_max = S_max;
+    p.chunk = chunk; p.NC = (int)nc; p.RT = T * G;
+    p.NR = (p.RT + kMaxRowsPerWave - 1) / kMaxRowsPerWave;
+    p.R = (p.RT + p.NR - 1) / p.NR;
+    int nwk = chunk / kKeysPerWave;
+    p.nwk = nwk < 1 ? 1 : (nwk > 4 ? 4 : nwk);
+    const size_t lds_per_rg = (size_t)p.nwk * p.R * (D + 2) * sizeof(float);
+    int rgb = kMaxWavesPerBlock / p.nwk;
+    if ((size_t)rgb * lds_per_rg > kMaxLdsBytes) rgb = (int)(kMaxLdsBytes / lds_per_rg);
+    if (rgb > p.NR) rgb = p.NR;
+    if (rgb < 1) return DECATTN_ERR_UNSUPPORTED;
+    p.rg_per_block = rgb;
+    p.n_row_blocks = (p.NR + rgb - 1) / rgb;
+    if ((long long)Hkv * p.n_row_blocks > 65535) return DECATTN_ERR_UNSUPPORTED;
+    p.lds_bytes = (size_t)rgb * lds_per_rg;
+
+    const size_t tiles_rows = (size_t)B * Hkv * p.NC * p.RT;
+    p.ml_bytes = round_up(tiles_rows * 2 * sizeof(float), kAlign);
+    p.acc_bytes = round_up(tiles_rows * (size_t)D * sizeof(float), kAlign);
+    p.total_bytes = p.ml_bytes + p.acc_bytes;
+    *pl = p;
+    return DECATTN_OK;
+}
+
+template <int D>
+hipError_t launch_partial_d(const Plan& pl, const PartialParams& pp, hipStream_t s) {
+    const dim3 grid(pl.NC, pl.Hkv * pl.n_row_blocks, pl.B);
+    const dim3 block(64 * pl.nwk * pl.rg_per_block);
+    switch (pl.R) {
+#define DECATTN_CASE(RR) \
+        case RR: hipLaunchKernelGGL((split_kv_partial<D, RR>), grid, block, pl.lds_bytes, s, pp); break;
+        DECATTN_CASE(1) DECATTN_CASE(2) DECATTN_CASE(3) DECATTN_CASE(4)
+        DECATTN_CASE(5) DECATTN_CASE(6) DECATTN_CASE(7) DECATTN_CASE(8)
+#undef DECATTN_CASE
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+int run_partial(const Plan& pl, const void* q, const void* k, const void* v, const int32_t* lens,
+                float scale, int causal, void* ws, hipStream_t s) {
+    PartialParams pp{};
+    pp.q = static_cast<const uint16_t*>(q);
+    pp.k = static_cast<const uint16_t*>(k);
+    pp.v = static_cast<const uint16_t*>(v);
+    pp.lens = lens;
+    pp.ws_ml = static_cast<float*>(ws);
+    pp.ws_acc = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.ml_bytes);
+    pp.T = pl.T; pp.Hq = pl.Hq; pp.Hkv = pl.Hkv; pp.G = pl.G; pp.S_max = pl.S_max;
+    pp.chunk = pl.chunk; pp.NC = pl.NC; pp.RT = pl.RT; pp.causal = causal;
+    pp.nwk = pl.nwk; pp.rg_per_block = pl.rg_per_block; pp.n_row_blocks = pl.n_row_blocks;
+    // log2(e) folded into the query: scores come out in log2 units for exp2
+    pp.qscale = (float)((double)scale * 1.4426950408889634);
+    const hipError_t e = pl.D == 64 ? launch_partial_d<64>(pl, pp, s) : launch_partial_d<128>(pl, pp, s);
+    return e == hipSuccess ? DECATTN_OK : DECATTN_ERR_HIP;
+}
+
+int run_merge(const Plan& pl, const int32_t* lens, int causal, void* out, int out_dtype, void* ws,
+              hipStream_t s) {
+    MergeParams mp{};
+    mp.ws_ml = static_cast<const float*>(ws);
+    mp.ws_acc = reinterpret_cast<const float*>(static_cast<const char*>(ws) + pl.ml_bytes);
+    mp.lens = lens;
+    mp.out = out;
+    mp.out_bf16 = out_dtype == DECATTN_OUT_BF16;
+    mp.T = pl.T; mp.Hq = pl.Hq; mp.Hkv = pl.Hkv; mp.G = pl.G; mp.S_max = pl.S_max;
+    mp.chunk = pl.chunk; mp.NC = pl.NC; mp.RT = pl.RT; mp.causal = causal;
+    const dim3 grid(pl.B * pl.T * pl.Hq);
+    if (pl.D == 64) hipLaunchKernelGGL(lse_merge<64>, grid, dim3(kMergeThreads), 0, s, mp);
+    else hipLaunchKernelGGL(lse_merge<128>, grid, dim3(kMergeThreads), 0, s, mp);
+    return hipGetLastError() == hipSuccess ? DECATTN_OK : DECATTN_ERR_HIP;
+}
+
+int check_common(const void* q, const void* k, const void* v, const int32_t* lens, float scale,
+                 void* ws, size_t ws_bytes, const Plan& pl) {
+    if (!q || !k || !v || !lens || !ws) return DECATTN_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(ws) ||
+        (reinterpret_cast<uintptr_t>(lens) & 3u))
+        return DECATTN_ERR_INVALID_ARG;
+    if (!std::isfinite(scale)) return DECATTN_ERR_INVALID_ARG;
+    if (ws_bytes < pl.total_bytes) return DECATTN_ERR_WORKSPACE;
+    return DECATTN_OK;
+}
+
+int check_out(void* out, int out_dtype) {
+    if (!out || !aligned16(out)) return DECATTN_ERR_INVALID_ARG;
+    if (out_dtype != DECATTN_OUT_BF16 && out_dtype != DECATTN_OUT_F32) return DECATTN_ERR_INVALID_ARG;
+    return DECATTN_OK;
+}
+
+int attention(const void* q, const void* k, const void* v, const int32_t* lens, int B, int T, int Hq,
+              int Hkv, int D, int S_max, float scale, int causal, void* out, int out_dtype, void* ws,
+              size_t ws_bytes, int chunk, void* stream) {
+    Plan pl;
+    int st = make_plan(B, T, Hq, Hkv, D, S_max, chunk, &pl);
+    if (st != DECATTN_OK) return st;
+    if ((st = check_common(q, k, v, lens, scale, ws, ws_bytes, pl)) != DECATTN_OK) return st;
+    if ((st = check_out(out, out_dtype)) != DECATTN_OK) return st;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = run_partial(pl, q, k, v, lens, scale, causal, ws, s)) != DECATTN_OK) return st;
+    return run_merge(pl, lens, causal, out, out_dtype, ws, s);
+}
+
+}  // namespace
+}  // namespace decattn
+
+using namespace decattn;
+
+extern "C" {
+
+int decattn_abi_version(void) { return DECATTN_ABI_VERSION; }
+
+const char* decattn_status_str(int status) {
+    switch (status) {
+        case DECATTN_OK: return "ok";
+        case DECATTN_ERR_INVALID_ARG: return "invalid argument";
+        case DECATTN_ERR_UNSUPPORTED: return "unsupported shape or chunk size";
+        case DECATTN_ERR_WORKSPACE: return "workspace too small";
+        case DECATTN_ERR_HIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+int decattn_default_chunk(int B, int T, int Hq, int Hkv, int D, int S_max) {
+    Plan pl;
+    return make_plan(B, T, Hq, Hkv, D, S_max, 0, &pl) == DECATTN_OK ? pl.chunk : 0;
+}
+
+size_t decattn_workspace_bytes(int B, int T, int Hq, int Hkv, int D, int S_max, int chunk) {
+    Plan pl;
+    return make_plan(B, T, Hq, Hkv, D, S_max, chunk, &pl) == DECATTN_OK ? pl.total_bytes : 0;
+}
+
+int decode_attn(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens, int B,
+                int Hq, int Hkv, int D, int S_max, float scale, void* out, int out_dtype, void* workspace,
+                size_t workspace_bytes, int chunk, void* stream) {
+    return attention(q, k_cache, v_cache, seq_lens, B, 1, Hq, Hkv, D, S_max, scale, 0, out, out_dtype,
+                     workspace, workspace_bytes, chunk, stream);
+}
+
+int chunk_attn(const void* q, const void* k_cache, const void* v_cache, const int32_t* ctx_lens, int B,
+               int T, int Hq, int Hkv, int D, int S_max, float scale, void* out, int out_dtype,
+               void* workspace, size_t workspace_bytes, int chunk, void* stream) {
+    return attention(q, k_cache, v_cache, ctx_lens, B, T, Hq, Hkv, D, S_max, scale, 1, out, out_dtype,
+                     workspace, workspace_bytes, chunk, stream);
+}
+
+int attn_partial(const void* q, const void* k_cache, const void* v_cache, const int32_t* lens, int B, int T,
+                 int Hq, int Hkv, int D, int S_max, float scale, int causal, void* workspace,
+                 size_t workspace_bytes, int chunk, void* stream) {
+    if (causal != 0 && causal != 1) return DECATTN_ERR_INVALID_ARG;
+    if (!causal && T != 1) return DECATTN_ERR_INVALID_ARG;
+    Plan pl;
+    int st = make_plan(B, T, Hq, Hkv, D, S_max, chunk, &pl);
+    if (st != DECATTN_OK) return st;
+    if ((st = check_common(q, k_cache, v_cache, lens, scale, workspace, workspace_bytes, pl)) != DECATTN_OK)
+        return st;
+    return run_partial(pl, q, k_cache, v_cache, lens, scale, causal, workspace,
+                       static_cast<hipStream_t>(stream));
+}
+
+int attn_merge(const int32_t* lens, int B, int T, int Hq, int Hkv, int D, int S_max, int causal, void* out,
+               int out_dtype, void* workspace, size_t workspace_bytes, int chunk, void* stream) {
+    if (causal != 0 && causal != 1) return DECATTN_ERR_INVALID_ARG;
+    if (!causal && T != 1) return DECATTN_ERR_INVALID_ARG;
+    Plan pl;
+    int st = make_plan(B, T, Hq, Hkv, D, S_max, chunk, &pl);
+    if (st != DECATTN_OK) return st;
+    if (!lens || !workspace || !aligned16(workspace) || (reinterpret_cast<uintptr_t>(lens) & 3u))
+        return DECATTN_ERR_INVALID_ARG;
+    if (workspace_bytes < pl.total_bytes) return DECATTN_ERR_WORKSPACE;
+    if ((st = check_out(out, out_dtype)) != DECATTN_OK) return st;
+    return run_merge(pl, lens, causal, out, out_dtype, workspace, static_cast<hipStream_t>(stream));
+}
+
+int decattn_probe_read(const void* buf, size_t bytes, void* sink, void* stream) {
+    if (!buf || !sink || !aligned16(buf) || (bytes & 15u) || bytes == 0) return DECATTN_ERR_INVALID_ARG;
+    const size_t n16 = bytes / 16;
+    size_t blocks = (n16 + kProbeThreads - 1) / kProbeThreads;
+    if (blocks > 256 * 16) blocks = 256 * 16;
+    hipLaunchKernelGGL(probe_read, dim3((unsigned)blocks), dim3(kProbeThreads), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const uint4*>(buf), n16,
+                       static_cast<uint32_t*>(sink));
+    return hipGetLastError() == hipSuccess ? DECATTN_OK : DECATTN_ERR_HIP;
+}
+
+int decattn_probe_copy(void* dst, const void* src, size_t bytes, void* stream) {
+    if (!dst || !src || !aligned16(dst) || !aligned16(src) || (bytes & 15u) || bytes == 0)
+        return DECATTN_ERR_INVALID_ARG;
+    const size_t n16 = bytes / 16;
+    size_t blocks = (n16 + kProbeThreads - 1) / kProbeThreads;
+    if (blocks > 256 * 16) blocks = 256 * 16;
+    hipLaunchKernelGGL(probe_copy, dim3((unsigned)blocks), dim3(kProbeThreads), 0,
+                       static_cast<hipStream_t>(stream), static_cast<uint4*>(dst),
+                       static_cast<const uint4*>(src), n16);
+    return hipGetLastError() == hipSuccess ? DECATTN_OK : DECATTN_ERR_HIP;
+}
+
+}  // extern "C"

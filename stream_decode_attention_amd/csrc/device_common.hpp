@@ -1,0 +1,80 @@
+// Device helpers shared by the libdecattn kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace decattn {
+
+constexpr float kNegInf = -__builtin_inff();
+
+// bf16 holds the upper 16 bits of a binary32, so widening is a shift.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ void bf16x8_to_f32(const uint4 r, float f[8]) {
+    f[0] = bf16_lo(r.x); f[1] = bf16_hi(r.x);
+    f[2] = bf16_lo(r.y); f[3] = bf16_hi(r.y);
+    f[4] = bf16_lo(r.z); f[5] = bf16_hi(r.z);
+    f[6] = bf16_lo(r.w); f[7] = bf16_hi(r.w);
+}
+
+// Round binary32 to the nearest bf16, ties to even: add half an output step
+// (minus one when the kept low bit is 0) and truncate. NaN maps to a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0;
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// One DPP lane move inside a 16-lane row (bound_ctrl off, all rows/banks on).
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+        0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <- lane 7-i within each 8 lanes
+constexpr int kDppMirror = 0x140;     // lane i <- lane 15-i within each 16 lanes
+constexpr int kDppRor8 = 0x128;       // lane i <- lane (i+8) mod 16
+
+// Sum over aligned groups of N (8 or 16) lanes; every lane of a group ends with
+// the same bits (each step adds a pair in both orders, and + commutes).
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+    static_assert(N == 8 || N == 16, "group of 8 or 16 lanes");
+    x += dpp_move<kDppXor1>(x);
+    x += dpp_move<kDppXor2>(x);
+    x += dpp_move<kDppHalfMirror>(x);
+    if constexpr (N == 16) x += dpp_move<kDppMirror>(x);
+    return x;
+}
+
+// Reduce across the 64/N lane groups of a wave (lanes with equal index inside
+// their group). N = 8 or 16.
+template <int N>
+__device__ __forceinline__ float across_groups_sum(float x) {
+    if constexpr (N == 8) x += dpp_move<kDppRor8>(x);
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    return x;
+}
+
+template <int N>
+__device__ __forceinline__ float across_groups_max(float x) {
+    if constexpr (N == 8) x = fmaxf(x, dpp_move<kDppRor8>(x));
+    x = fmaxf(x, __shfl_xor(x, 16));
+    x = fmaxf(x, __shfl_xor(x, 32));
+    return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ int clamp_len(int n, int s_max) {
+    return n < 0 ? 0 : (n > s_max ? s_max : n);
+}
+
+}  // namespace decattn

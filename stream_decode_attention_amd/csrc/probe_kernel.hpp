@@ -1,0 +1,42 @@
+// Streaming probes: the achievable HBM read rate (the measured streaming peak
+// llm-decode-cuda sets its roofline against) and a plain copy of known size,
+// whose counter readings calibrate the fetch/write byte counters.
+#pragma once
+
+#include "device_common.hpp"
+
+namespace decattn {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kProbeThreads = 256;
+constexpr int kProbeUnroll = 4;
+
+__global__ void __launch_bounds__(kProbeThreads)
+probe_read(const uint4* __restrict__ buf, size_t n16, uint32_t* sink) {
+    const size_t stride = (size_t)gridDim.x * kProbeThreads;
+    size_t i = (size_t)blockIdx.x * kProbeThreads + threadIdx.x;
+    uint32_t x = 0;
+    for (; i + (kProbeUnroll - 1) * stride < n16; i += kProbeUnroll * stride) {
+        u32x4 v[kProbeUnroll];
+#pragma unroll
+        for (int u = 0; u < kProbeUnroll; ++u)
+            v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(buf + i + u * stride));
+#pragma unroll
+        for (int u = 0; u < kProbeUnroll; ++u) x ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    for (; i < n16; i += stride) {
+        const uint4 v = buf[i];
+        x ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    // a data-dependent store that almost never happens keeps the loads alive
+    if (x == 0x9E3779B9u) *sink = x;
+}
+
+__global__ void __launch_bounds__(kProbeThreads)
+probe_copy(uint4* __restrict__ dst, const uint4* __restrict__ src, size_t n16) {
+    const size_t stride = (size_t)gridDim.x * kProbeThreads;
+    for (size_t i = (size_t)blockIdx.x * kProbeThreads + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
+}  // namespace decattn

@@ -1,0 +1,126 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol, and
+rejects bad arguments on the host before anything is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import stream_decode_attention_amd as sda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "decattn.h")
+
+
+def _ensure_built():
+    if not os.path.exists(sda.LIB_PATH):
+        from stream_decode_attention_amd.build import build_library
+        build_library()
+
+
+@pytest.fixture(scope="module")
+def lib():
+    _ensure_built()
+    return sda.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:int|size_t|const char\s*\*)\s*(\w+)\s*\(", text, flags=re.M)
+
+
+def test_header_declares_the_boundary():
+    names = set(declared_functions())
+    assert {"decode_attn", "chunk_attn", "attn_partial", "attn_merge", "decattn_workspace_bytes",
+            "decattn_default_chunk", "decattn_status_str", "decattn_abi_version",
+            "decattn_probe_read", "decattn_probe_copy"} <= names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    raw = ctypes.CDLL(sda.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+    # and the binding knows a signature for every one of them
+    assert set(declared_functions()) == set(sda._SIGNATURES)
+
+
+def test_version_and_status_strings(lib):
+    assert sda.abi_version() == 1
+    assert sda.status_str(0) == "ok"
+    for s in (1, 2, 3, 4, 99, -1):
+        assert isinstance(sda.status_str(s), str) and sda.status_str(s)
+
+
+def _ws(B, T, Hq, Hkv, D, S, C):
+    NC = -(-S // C)
+    rows = B * Hkv * NC * T * (Hq // Hkv)
+    up = lambda x: -(-x // 256) * 256
+    return up(rows * 2 * 4) + up(rows * D * 4)
+
+
+@pytest.mark.parametrize("shape", [
+    (1, 1, 15, 5, 64, 128, 32), (8, 1, 32, 8, 128, 32768, 256), (1, 6, 24, 8, 128, 16384, 64),
+    (2, 3, 4, 4, 64, 100, 16), (1, 1, 8, 1, 128, 50, 1024),
+])
+def test_workspace_bytes_formula(lib, shape):
+    B, T, Hq, Hkv, D, S, C = shape
+    assert sda.workspace_bytes(B, T, Hq, Hkv, D, S, C) == _ws(B, T, Hq, Hkv, D, S, C)
+
+
+def test_default_chunk_is_supported_power_of_two(lib):
+    for shape in [(1, 1, 15, 5, 64, 128), (1, 1, 15, 5, 64, 4096), (1, 1, 32, 4, 64, 8192),
+                  (8, 1, 32, 8, 128, 32768), (1, 6, 24, 8, 128, 16384)]:
+        c = sda.default_chunk(*shape)
+        assert c >= 16 and c & (c - 1) == 0
+        assert sda.workspace_bytes(*shape, 0) == sda.workspace_bytes(*shape, c)
+
+
+FAKE = 0x100000  # 16-byte aligned, never dereferenced: every call below fails its host checks
+
+
+def _decode(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, lens=FAKE, B=1, Hq=8, Hkv=2, D=64, S=64, scale=0.125,
+             out=FAKE, od=1, ws=FAKE, wsb=1 << 20, chunk=0, stream=None)
+    a.update(kw)
+    return lib.decode_attn(a["q"], a["k"], a["v"], a["lens"], a["B"], a["Hq"], a["Hkv"], a["D"], a["S"],
+                           a["scale"], a["out"], a["od"], a["ws"], a["wsb"], a["chunk"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hq=9, Hkv=2), 1),                 # Hq not a multiple of Hkv
+    (dict(B=0), 1), (dict(S=-1), 1), (dict(Hkv=0), 1),
+    (dict(D=96), 2), (dict(D=256), 2),      # head dim
+    (dict(Hq=18, Hkv=2), 2),                # G = 9 > 8
+    (dict(chunk=48), 2), (dict(chunk=8), 2), (dict(chunk=-32), 2), (dict(chunk=1 << 21), 2),
+    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(lens=None), 1),
+    (dict(out=None), 1), (dict(ws=None), 1),
+    (dict(q=FAKE + 2), 1), (dict(k=FAKE + 8), 1), (dict(out=FAKE + 4), 1), (dict(lens=FAKE + 2), 1),
+    (dict(od=7), 1),
+    (dict(scale=float("nan")), 1), (dict(scale=float("inf")), 1),
+    (dict(wsb=16), 3),
+])
+def test_decode_rejects_bad_arguments(lib, kw, status):
+    assert _decode(lib, **kw) == status
+
+
+def test_chunk_rejects_bad_arguments(lib):
+    args = lambda T, wsb=1 << 24: (FAKE, FAKE, FAKE, FAKE, 1, T, 24, 8, 128, 16384, 0.088, FAKE, 1,
+                                   FAKE, wsb, 0, None)
+    assert lib.chunk_attn(*args(17)) == 2           # T > 16
+    assert lib.chunk_attn(*args(0)) == 1
+    assert lib.chunk_attn(*args(6, wsb=1024)) == 3
+
+
+def test_phase_entry_points_reject_bad_arguments(lib):
+    # decode (causal = 0) requires T == 1; causal must be 0 or 1
+    assert lib.attn_partial(FAKE, FAKE, FAKE, FAKE, 1, 2, 8, 2, 64, 64, 0.1, 0, FAKE, 1 << 20, 0, None) == 1
+    assert lib.attn_partial(FAKE, FAKE, FAKE, FAKE, 1, 1, 8, 2, 64, 64, 0.1, 2, FAKE, 1 << 20, 0, None) == 1
+    assert lib.attn_merge(FAKE, 1, 1, 8, 2, 64, 64, 0, FAKE, 1, FAKE, 16, 0, None) == 3
+    assert lib.attn_merge(None, 1, 1, 8, 2, 64, 64, 0, FAKE, 1, FAKE, 1 << 20, 0, None) == 1
+
+
+def test_probes_reject_bad_arguments(lib):
+    assert lib.decattn_probe_read(FAKE, 100, FAKE, None) == 1      # not a multiple of 16
+    assert lib.decattn_probe_read(None, 1024, FAKE, None) == 1
+    assert lib.decattn_probe_copy(FAKE, FAKE + 8, 1024, None) == 1

@@ -1,0 +1,272 @@
+"""HIP path vs the fp64 oracle on the same seeded bytes, through the C ABI.
+
+Tolerances: max-abs 1e-4 for fp32 output and 1e-2 for bf16 output (bf16
+elements beyond 1e-2 must be adjacent to the exact value); masks, indices,
+early exits and batch/head isolation are checked bit-exactly.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import stream_decode_attention_amd as sda
+import workloads
+from workloads import BF16_NAN
+from tests.gpu_util import (assert_bf16_close, assert_f32_close, bits_of, dev_bits, dev_lens,
+                            run_chunk, run_decode, workspace)
+
+pytestmark = pytest.mark.gpu
+
+
+def _both_modes(c, ref, **kw):
+    out32 = run_decode(c, out_dtype=torch.float32, **kw)
+    assert_f32_close(out32, ref)
+    out16 = run_decode(c, out_dtype=torch.bfloat16, **kw)
+    assert_bf16_close(out16, ref)
+    return out32, out16
+
+
+# ------------------------------------------------------------- the five workloads
+
+def test_workload1_single_call_both_modes():
+    c = workloads.make_config(1)
+    ref = oracle.decode_attention(c["q"], c["k"], c["v"], c["lens"], c["scale"])
+    _both_modes(c, ref, chunk=32)
+
+
+@pytest.mark.parametrize("n", [64, 1024, 2048, 4096])
+def test_workload2_smollm_layer(n):
+    c = workloads.make_config(2, layer=n % 7, n=n)
+    ref = oracle.decode_attention(c["q"], c["k"], c["v"], c["lens"], c["scale"])
+    _both_modes(c, ref)
+
+
+@pytest.mark.parametrize("n", [1024, 4096, 8192])
+def test_workload3_tinyllama_outlier_keys(n):
+    c = workloads.make_config(3, layer=1, n=n)
+    ref = oracle.decode_attention(c["q"], c["k"], c["v"], c["lens"], c["scale"])
+    _both_modes(c, ref)
+
+
+def test_workload4_batched_ragged_full_size_sampled_rows():
+    c = workloads.make_config(4)
+    rng = np.random.default_rng(4)
+    rows = [(b, h) for b in range(8) for h in sorted(rng.choice(32, size=6, replace=False))]
+    ref = oracle.decode_attention(c["q"], c["k"], c["v"], c["lens"], c["scale"], rows=rows)
+    mask = np.zeros(ref.shape, bool)
+    for b, h in rows:
+        mask[b, h] = True
+    tensors = (dev_bits(c["q"]), dev_bits(c["k"]), dev_bits(c["v"]))
+    out32 = run_decode(c, tensors=tensors)
+    assert_f32_close(out32, ref, mask=mask)
+    out16 = run_decode(c, tensors=tensors, out_dtype=torch.bfloat16)
+    assert_bf16_close(out16, ref, mask=mask)
+    # the bf16 output is the fp32 output rounded to nearest even
+    rne = out32.to(torch.bfloat16)
+    assert torch.equal(rne.view(torch.int16), out16.view(torch.int16))
+
+
+def test_workload5_verify_chunk_vs_oracle_and_sequential_decodes():
+    c = workloads.make_config(5)
+    ref = oracle.chunk_attention(c["q"], c["k"], c["v"], c["lens"], c["scale"])
+    tensors = (dev_bits(c["q"]), dev_bits(c["k"]), dev_bits(c["v"]))
+    out32 = run_chunk(c, tensors=tensors)
+    assert_f32_close(out32, ref)
+    out16 = run_chunk(c, tensors=tensors, out_dtype=torch.bfloat16)
+    assert_bf16_close(out16, ref)
+    # six sequential decode calls: token i with seq_len = ctx + i + 1, same chunk
+    chunk = sda.default_chunk(1, 6, 24, 8, 128, 16384)
+    T = c["q"].shape[1]
+    for i in range(T):
+        ci = dict(c, q=np.ascontiguousarray(c["q"][:, i]), lens=c["lens"] + i + 1)
+        dec = run_decode(ci, chunk=chunk, tensors=(dev_bits(ci["q"]), tensors[1], tensors[2]))
+        assert torch.equal(dec, out32[:, i]), f"token {i}: chunk row differs from its decode call"
+
+
+# ----------------------------------------------------------- shapes and chunking
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("chunk", [16, 32, 64, 128, 256, 2048])
+def test_multi_tile_ragged_lengths_all_chunk_sizes(D, chunk):
+    c = workloads.make_case(3, 8, 2, D, 1000, [1, 333, 1000], seed=D + chunk)
+    ref = oracle.decode_attention(c["q"], c["k"], c["v"], c["lens"], c["scale"])
+    assert_f32_close(run_decode(c, chunk=chunk), ref)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_every_group_size(D, G):
+    Hkv = 3
+    c = workloads.make_case(2, G * Hkv, Hkv, D, 300, [300, 129], seed=10 * G + D)
+    ref = oracle.decode_attention(c["q"], c["k"], c["v"], c["lens"], c["scale"])
+    _both_modes(c, ref, chunk=64)
+
+
+@pytest.mark.parametrize("n", [1, 31, 32, 33, 63, 64, 65, 255, 256])
+def test_length_boundaries(n):
+    c = workloads.make_case(1, 6, 2, 64, 256, [n], seed=n)
+    ref = oracle.decode_attention(c["q"], c["k"], c["v"], c["lens"], c["scale"])
+    for chunk in (32, 64):
+        assert_f32_close(run_decode(c, chunk=chunk), ref)
+
+
+def test_empty_negative_and_oversized_lengths():
+    c = workloads.make_case(4, 8, 2, 128, 96, [0, -7, 500, 96], seed=5)
+    for dt in (torch.float32, torch.bfloat16):
+        out = run_decode(c, out_dtype=dt, chunk=32)
+        o = out.view(torch.int16).cpu().numpy() if dt == torch.bfloat16 else out.cpu().numpy()
+        assert np.all(o[0] == 0) and np.all(o[1] == 0)
+        # lengths beyond S_max are clamped to S_max
+        assert torch.equal(out[2], out[3])
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_single_key_returns_v0_bit_exactly(D):
+    c = workloads.make_case(2, 8, 4, D, 64, [1, 1], seed=6)
+    v0 = c["v"][:, :, 0, :]                              # [B, Hkv, D] bf16 bits
+    expect = np.repeat(v0, 2, axis=1)                    # G = 2
+    out16 = run_decode(c, out_dtype=torch.bfloat16)
+    assert np.array_equal(bits_of(out16), expect)
+    out32 = run_decode(c, out_dtype=torch.float32)
+    assert np.array_equal(out32.cpu().numpy(), oracle.bf16_bits_to_f64(expect).astype(np.float32))
+
+
+# ------------------------------------------------------------ never-read slots
+
+@pytest.mark.parametrize("D,chunk", [(64, 32), (128, 64), (128, 256)])
+def test_nan_poison_past_length_is_never_read(D, chunk):
+    lens = [1, 37, 64, 200]
+    c = workloads.make_case(4, 8, 2, D, 256, lens, seed=7 + D)
+    poisoned = dict(c, k=c["k"].copy(), v=c["v"].copy())
+    for b, n in enumerate(lens):
+        poisoned["k"][b, :, n:] = BF16_NAN
+        poisoned["v"][b, :, n:] = BF16_NAN
+    for dt in (torch.float32, torch.bfloat16):
+        a = run_decode(c, chunk=chunk, out_dtype=dt)
+        p = run_decode(poisoned, chunk=chunk, out_dtype=dt)
+        assert torch.equal(a.view(torch.int16), p.view(torch.int16))
+        assert not torch.isnan(p.float()).any()
+
+
+def test_chunk_nan_poison_past_context_plus_t():
+    c = workloads.make_case(2, 6, 2, 128, 300, [100, 257], T=5, seed=8)
+    poisoned = dict(c, k=c["k"].copy(), v=c["v"].copy())
+    for b, ctx in enumerate(c["lens"]):
+        poisoned["k"][b, :, ctx + 5:] = BF16_NAN
+        poisoned["v"][b, :, ctx + 5:] = BF16_NAN
+    a = run_chunk(c, chunk=64)
+    p = run_chunk(poisoned, chunk=64)
+    assert torch.equal(a, p) and not torch.isnan(p).any()
+
+
+def test_rollback_shrinking_length_ignores_stale_tail():
+    c = workloads.make_case(1, 8, 2, 128, 512, [512], seed=9)
+    full = run_decode(c, chunk=64)
+    short = run_decode(c, chunk=64, lens=np.array([300], np.int32))
+    ref = oracle.decode_attention(c["q"], c["k"], c["v"], [300], c["scale"])
+    assert_f32_close(short, ref)
+    assert not torch.equal(full, short)
+
+
+# ------------------------------------------------------- isolation, bit-exact
+
+def test_gqa_perturbing_one_kv_head_changes_only_its_group():
+    G, Hkv = 4, 4
+    c = workloads.make_case(2, G * Hkv, Hkv, 128, 200, [200, 150], seed=10)
+    base = run_decode(c, chunk=64)
+    for kp in range(Hkv):
+        pert = dict(c, v=c["v"].copy())
+        pert["v"][1, kp, :150] ^= np.uint16(0x0040)          # flip a mantissa bit of every value
+        out = run_decode(pert, chunk=64)
+        changed = (out != base).any(-1).cpu().numpy()        # [B, Hq]
+        expect = np.zeros_like(changed)
+        expect[1, kp * G:(kp + 1) * G] = True
+        assert np.array_equal(changed, expect)
+
+
+def test_batch_rows_bit_identical_to_batch_one_calls():
+    lens = [700, 5, 1024, 333]
+    c = workloads.make_case(4, 16, 4, 64, 1024, lens, seed=11)
+    full = run_decode(c, chunk=128)
+    for b in range(4):
+        cb = dict(c, q=c["q"][b:b + 1], k=c["k"][b:b + 1], v=c["v"][b:b + 1], lens=c["lens"][b:b + 1])
+        one = run_decode(cb, chunk=128)
+        assert torch.equal(one[0], full[b])
+
+
+def test_chunk_row_unchanged_by_later_key():
+    c = workloads.make_case(1, 6, 2, 128, 200, [120], T=4, seed=12)
+    a = run_chunk(c, chunk=64)
+    pert = dict(c, k=c["k"].copy())
+    pert["k"][0, :, 122] ^= np.uint16(0x0100)                # key ctx+2: seen by tokens 2, 3
+    b = run_chunk(pert, chunk=64)
+    assert torch.equal(a[0, :2], b[0, :2])
+    assert (a[0, 2:] != b[0, 2:]).any(-1).all()
+
+
+@pytest.mark.parametrize("T,ctx", [(1, [50]), (3, [0]), (6, [8192]), (9, [300]), (16, [40])])
+def test_chunk_shapes_vs_oracle(T, ctx):
+    S = 8192 + 16 if ctx == [8192] else 512
+    c = workloads.make_case(1, 24, 8, 128, S, ctx, T=T, seed=13 + T)
+    ref = oracle.chunk_attention(c["q"], c["k"], c["v"], c["lens"], c["scale"])
+    assert_f32_close(run_chunk(c), ref)
+
+
+def test_chunk_context_reaching_s_max_clamps():
+    c = workloads.make_case(2, 8, 4, 64, 128, [125, 128], T=6, seed=14)
+    ref = oracle.chunk_attention(c["q"], c["k"], c["v"], c["lens"], c["scale"])
+    assert_f32_close(run_chunk(c, chunk=32), ref)
+
+
+def test_phases_separately_equal_decode_attn():
+    c = workloads.make_case(2, 32, 8, 128, 2048, [2048, 999], seed=15)
+    q, k, v = dev_bits(c["q"]), dev_bits(c["k"]), dev_bits(c["v"])
+    lens = dev_lens(c["lens"])
+    ws = workspace(2, 1, 32, 8, 128, 2048, 128)
+    out = torch.empty((2, 32, 128), device="cuda")
+    sda.attn_partial(q, k, v, lens, c["scale"], ws, chunk=128)
+    sda.attn_merge(lens, out, ws, T=1, Hq=32, Hkv=8, S_max=2048, chunk=128)
+    torch.cuda.synchronize()
+    assert torch.equal(out, run_decode(c, chunk=128, tensors=(q, k, v)))
+
+
+# ------------------------------------------------------------------ hipGraph
+
+def test_graph_replay_follows_device_lengths():
+    c = workloads.make_case(1, 15, 5, 64, 4096, [4096], seed=16)
+    q, k, v = dev_bits(c["q"]), dev_bits(c["k"]), dev_bits(c["v"])
+    lens = dev_lens([64])
+    ws = workspace(1, 1, 15, 5, 64, 4096, 0, poison=False)
+    out = torch.zeros((1, 15, 64), device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(2):
+            sda.decode_attn(q, k, v, lens, c["scale"], out, ws)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sda.decode_attn(q, k, v, lens, c["scale"], out, ws)
+    for n in (64, 1024, 2048, 4096, 1, 3000, 64):
+        lens.copy_(torch.tensor([n], dtype=torch.int32))
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        eager = run_decode(c, lens=np.array([n], np.int32), tensors=(q, k, v))
+        assert torch.equal(got, eager), f"replay at n={n} differs from eager"
+        ref = oracle.decode_attention(c["q"], c["k"], c["v"], [n], c["scale"])
+        assert_f32_close(got, ref)
+
+
+# ------------------------------------------------------------------- probes
+
+def test_probe_copy_and_read():
+    src = torch.randint(-2**31, 2**31 - 1, (1 << 20,), dtype=torch.int32, device="cuda")
+    dst = torch.zeros_like(src)
+    sda.probe_copy(dst, src)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    sda.probe_read(src, sink)
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)

@@ -15,24 +15,25 @@ Shapes follow the models the pages measure or name:
   query tokens (tinydecode README, "speculative decoding").
 
 The pages measure whole models on real text; here every tensor is bf16 drawn
-from N(0, 1) (fp32 normal samples rounded to nearest-even bf16), which stands in
-for real activations. Cache slots at or past a sequence's length hold random
-data too, unless a test overwrites them.
+from N(0, 1) (float32 normal samples from NumPy's PCG64, rounded to
+nearest-even bf16), which stands in for real activations. Cache slots at or
+past a sequence's length hold random data too, unless a test overwrites them.
 
 Seeds: seed = 100000*cfg + 10*layer + t with t = 1 (q), 2 (K), 3 (V),
 4 (outlier mask), 5 (lengths).
 """
 from __future__ import annotations
 
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 import math
+import os
 
 import numpy as np
-import torch
 
 __all__ = [
     "Workload", "CONFIGS", "bf16_randn", "make_case", "make_config",
-    "seed_for", "bf16_scale", "BF16_NAN",
+    "seed_for", "bf16_scale", "uniform_mask", "ragged_lens", "BF16_NAN",
 ]
 
 # A quiet-NaN bf16 pattern, used by tests to poison cache slots that must never be read.
@@ -45,19 +46,66 @@ def seed_for(cfg: int, layer: int, t: int) -> int:
     return 100000 * cfg + 10 * layer + t
 
 
+_BLOCK = 1 << 20          # elements per independently seeded block
+
+
+def _round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Nearest-even bf16 bit patterns of finite float32 samples."""
+    u = x.view(np.uint32)
+    u += np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return (u >> np.uint32(16)).astype(np.uint16)
+
+
+def _fill_blocks(n: int, seed: int, make_block, dtype) -> np.ndarray:
+    """Run make_block(rng, count) over fixed 1 Mi-element blocks, block i drawing
+    from its own child of SeedSequence(seed); the bytes do not depend on the
+    number of worker threads."""
+    out = np.empty(n, dtype=dtype)
+    nblk = -(-n // _BLOCK)
+    children = np.random.SeedSequence(int(seed)).spawn(nblk)
+
+    def work(i):
+        lo, hi = i * _BLOCK, min((i + 1) * _BLOCK, n)
+        out[lo:hi] = make_block(np.random.default_rng(children[i]), hi - lo)
+
+    if nblk == 1:
+        work(0)
+    else:
+        with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+            list(ex.map(work, range(nblk)))
+    return out
+
+
+def _normal_block(rng, count):
+    return _round_to_bf16_bits(rng.standard_normal(count, dtype=np.float32))
+
+
 def bf16_randn(shape, seed: int) -> np.ndarray:
-    """bf16 bit patterns (uint16) of N(0,1) samples from a seeded CPU generator."""
-    g = torch.Generator().manual_seed(int(seed))
-    x = torch.randn(tuple(shape), generator=g, dtype=torch.float32).to(torch.bfloat16)
-    return x.view(torch.int16).numpy().view(np.uint16)
+    """bf16 bit patterns (uint16) of N(0,1) samples: float32 normals from NumPy's
+    PCG64, rounded to nearest-even bf16."""
+    n = int(np.prod(shape))
+    return _fill_blocks(n, seed, _normal_block, np.uint16).reshape(shape)
+
+
+def uniform_mask(shape, frac: float, seed: int) -> np.ndarray:
+    """Boolean mask with each entry True with probability ``frac``."""
+    n = int(np.prod(shape))
+    return _fill_blocks(n, seed, lambda rng, k: rng.random(k) < frac, np.bool_).reshape(shape)
 
 
 def bf16_scale(x_bits: np.ndarray, mask: np.ndarray, factor: float) -> np.ndarray:
-    """Multiply the bf16 values selected by ``mask`` by ``factor`` (a power of two: exact)."""
-    t = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).float()
-    m = torch.from_numpy(np.broadcast_to(mask, t.shape).copy())
-    t = torch.where(m, t * factor, t)
-    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    """Multiply the bf16 values selected by ``mask`` (broadcast over the last
+    axis) by ``factor``, a power of two, which is exact in bf16."""
+    e = int(round(np.log2(factor)))
+    assert 2.0 ** e == factor, "factor must be a power of two"
+    out = x_bits.copy()
+    sel = np.broadcast_to(mask, x_bits.shape)
+    bits = out[sel].astype(np.int32)
+    exp = (bits >> 7) & 0xFF
+    nz = exp != 0                     # zeros and subnormals never occur in N(0,1) bf16 draws
+    bits[nz] += e << 7
+    out[sel] = bits.astype(np.uint16)
+    return out
 
 
 @dataclass(frozen=True)
@@ -121,8 +169,7 @@ def make_case(B, Hq, Hkv, D, S_max, lens, *, T=1, seed=0, outlier_frac=0.0,
     k = bf16_randn((B, Hkv, S_max, D), seed * 10 + T_K)
     v = bf16_randn((B, Hkv, S_max, D), seed * 10 + T_V)
     if outlier_frac > 0:
-        g = torch.Generator().manual_seed(int(seed * 10 + T_OUTLIER))
-        mask = (torch.rand((B, Hkv, S_max), generator=g) < outlier_frac).numpy()
+        mask = uniform_mask((B, Hkv, S_max), outlier_frac, seed * 10 + T_OUTLIER)
         k = bf16_scale(k, mask[..., None], outlier_factor)
     lens = np.asarray(lens, dtype=np.int32).reshape(B)
     return {"q": q, "k": k, "v": v, "lens": lens,
@@ -130,8 +177,9 @@ def make_case(B, Hq, Hkv, D, S_max, lens, *, T=1, seed=0, outlier_frac=0.0,
 
 
 def ragged_lens(cfg: int, B: int, S_max: int, layer: int = 0) -> np.ndarray:
-    g = torch.Generator().manual_seed(seed_for(cfg, layer, T_LENS))
-    return torch.randint(1, S_max + 1, (B,), generator=g, dtype=torch.int64).numpy().astype(np.int32)
+    """Per-sequence lengths drawn uniformly from [1, S_max]."""
+    rng = np.random.default_rng(seed_for(cfg, layer, T_LENS))
+    return rng.integers(1, S_max + 1, size=B).astype(np.int32)
 
 
 def make_config(cfg: int, layer: int = 0, n: int | None = None) -> dict:
@@ -146,8 +194,7 @@ def make_config(cfg: int, layer: int = 0, n: int | None = None) -> dict:
     k = bf16_randn((w.B, w.Hkv, w.S_max, w.D), seed_for(cfg, layer, T_K))
     v = bf16_randn((w.B, w.Hkv, w.S_max, w.D), seed_for(cfg, layer, T_V))
     if w.outlier_frac > 0:
-        g = torch.Generator().manual_seed(seed_for(cfg, layer, T_OUTLIER))
-        mask = (torch.rand((w.B, w.Hkv, w.S_max), generator=g) < w.outlier_frac).numpy()
+        mask = uniform_mask((w.B, w.Hkv, w.S_max), w.outlier_frac, seed_for(cfg, layer, T_OUTLIER))
         k = bf16_scale(k, mask[..., None], w.outlier_factor)
     if w.ragged:
         lens = ragged_lens(cfg, w.B, w.S_max, layer)
