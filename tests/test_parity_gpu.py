@@ -114,12 +114,16 @@ def test_length_boundaries(n):
 
 def test_empty_negative_and_oversized_lengths():
     c = workloads.make_case(4, 8, 2, 128, 96, [0, -7, 500, 96], seed=5)
+    clamped = np.array([0, 0, 96, 96], np.int32)
+    ref = oracle.decode_attention(c["q"], c["k"], c["v"], clamped, c["scale"])
     for dt in (torch.float32, torch.bfloat16):
         out = run_decode(c, out_dtype=dt, chunk=32)
         o = out.view(torch.int16).cpu().numpy() if dt == torch.bfloat16 else out.cpu().numpy()
         assert np.all(o[0] == 0) and np.all(o[1] == 0)
-        # lengths beyond S_max are clamped to S_max
-        assert torch.equal(out[2], out[3])
+        # a length beyond S_max behaves exactly as S_max
+        same = run_decode(c, out_dtype=dt, chunk=32, lens=clamped)
+        assert torch.equal(out.view(torch.int16), same.view(torch.int16))
+    assert_f32_close(run_decode(c, chunk=32), ref)
 
 
 @pytest.mark.parametrize("D", [64, 128])
@@ -210,6 +214,7 @@ def test_chunk_row_unchanged_by_later_key():
 def test_chunk_shapes_vs_oracle(T, ctx):
     S = 8192 + 16 if ctx == [8192] else 512
     c = workloads.make_case(1, 24, 8, 128, S, ctx, T=T, seed=13 + T)
+    c["q"] = c["q"].reshape(1, T, 24, 128)
     ref = oracle.chunk_attention(c["q"], c["k"], c["v"], c["lens"], c["scale"])
     assert_f32_close(run_chunk(c), ref)
 
