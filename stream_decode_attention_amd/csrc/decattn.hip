@@ -1,13 +1,18 @@
 // libdecattn host side: argument checks, launch shapes and the C ABI.
 //
 // The C ABI is declared in include/decattn.h. Nothing here allocates device
-// memory, synchronizes or keeps state, so every entry point can be captured in
-// a hipGraph; all checks happen before the first launch.
+// memory or synchronizes, so every entry point can be captured in a hipGraph;
+// all checks happen before the first launch. The only state is a host-side
+// cache of per-device occupancy figures.
 #include <hip/hip_runtime.h>
 
+#include <cfloat>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
+#include <utility>
+#include <vector>
 
 #include "../../include/decattn.h"
 #include "merge_kernel.hpp"
@@ -19,6 +24,7 @@ namespace {
 
 constexpr int kMaxG = 8;
 constexpr int kMaxT = 16;
+constexpr int kMaxB = 4096;                // lengths are staged in LDS
 constexpr int kMaxRowsPerWave = 8;
 constexpr int kMaxWavesPerBlock = 8;       // matches __launch_bounds__(512)
 constexpr size_t kMaxLdsBytes = 64 * 1024;
@@ -40,7 +46,7 @@ int pick_default_chunk(int B, int Hkv, int S_max) {
     // Enough tiles to occupy the 256 compute units several times over while
     // S_max is the only length the host knows; larger tiles cut partial-state
     // traffic (about G*(D+2)*4 bytes per tile against 4*D bytes per key).
-    int c = 256;
+    int c = 512;
     while (c > 32 && (long long)B * Hkv * ((S_max + c - 1) / c) < 2048) c >>= 1;
     return c;
 }
@@ -57,7 +63,7 @@ int make_plan(int B, int T, int Hq, int Hkv, int D, int S_max, int chunk, Plan* 
     if (chunk < kMinChunk || chunk > kMaxChunk || !is_pow2(chunk)) return DECATTN_ERR_UNSUPPORTED;
     const long long nc = ((long long)S_max + chunk - 1) / chunk;
     if ((long long)B * Hkv * S_max * (long long)D > (1LL << 46)) return DECATTN_ERR_UNSUPPORTED;
-    if (B > 65535 || nc > 0x7FFFFFFF || (long long)B * T * Hq > 0x7FFFFFFF) return DECATTN_ERR_UNSUPPORTED;
+    if (B > kMaxB || nc > 0x7FFFFFFF || (long long)B * T * Hq > 0x7FFFFFFF) return DECATTN_ERR_UNSUPPORTED;
 
     Plan p{};
     p.B = B; p.T = T; p.Hq = Hq; p.Hkv = Hkv; p.G = G; p.D = D; p.S_max = S_max;
@@ -67,14 +73,16 @@ int make_plan(int B, int T, int Hq, int Hkv, int D, int S_max, int chunk, Plan* 
     int nwk = chunk / kKeysPerWave;
     p.nwk = nwk < 1 ? 1 : (nwk > 4 ? 4 : nwk);
     const size_t lds_per_rg = (size_t)p.nwk * p.R * (D + 2) * sizeof(float);
+    const size_t lds_lens = (size_t)B * sizeof(int);
     int rgb = kMaxWavesPerBlock / p.nwk;
-    if ((size_t)rgb * lds_per_rg > kMaxLdsBytes) rgb = (int)(kMaxLdsBytes / lds_per_rg);
+    if ((size_t)rgb * lds_per_rg + lds_lens > kMaxLdsBytes) rgb = (int)((kMaxLdsBytes - lds_lens) / lds_per_rg);
     if (rgb > p.NR) rgb = p.NR;
     if (rgb < 1) return DECATTN_ERR_UNSUPPORTED;
     p.rg_per_block = rgb;
     p.n_row_blocks = (p.NR + rgb - 1) / rgb;
-    if ((long long)Hkv * p.n_row_blocks > 65535) return DECATTN_ERR_UNSUPPORTED;
-    p.lds_bytes = (size_t)rgb * lds_per_rg;
+    // work items (b, kvh, row block, tile) must fit the kernel's int counters
+    if ((long long)B * Hkv * p.n_row_blocks * nc > 0x7FFFFFFF) return DECATTN_ERR_UNSUPPORTED;
+    p.lds_bytes = (size_t)rgb * lds_per_rg + lds_lens;
 
     const size_t tiles_rows = (size_t)B * Hkv * p.NC * p.RT;
     p.ml_bytes = round_up(tiles_rows * 2 * sizeof(float), kAlign);
@@ -84,19 +92,61 @@ int make_plan(int B, int T, int Hq, int Hkv, int D, int S_max, int chunk, Plan* 
     return DECATTN_OK;
 }
 
+// Workgroups of `kernel` that fit on the current device at once (all compute
+// units times the per-unit occupancy), cached per device and launch shape.
+// Host-side queries only: nothing is enqueued, so this is safe under capture.
+int resident_blocks(const void* kernel, int threads, size_t lds) {
+    struct Key {
+        int dev;
+        const void* fn;
+        int threads;
+        size_t lds;
+    };
+    static std::mutex mu;
+    static std::vector<std::pair<Key, int>> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        for (const auto& e : cache)
+            if (e.first.dev == dev && e.first.fn == kernel && e.first.threads == threads && e.first.lds == lds)
+                return e.second;
+    }
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds) != hipSuccess) return 0;
+    const int n = cus * (per_cu > 0 ? per_cu : 1);
+    std::lock_guard<std::mutex> lock(mu);
+    cache.push_back({Key{dev, kernel, threads, lds}, n});
+    return n;
+}
+
+template <int D, int R>
+hipError_t launch_partial_dr(const Plan& pl, const PartialParams& pp, hipStream_t s) {
+    // persistent: one wave of resident workgroups walks all attended tiles
+    const int threads = 64 * pl.nwk * pl.rg_per_block;
+    const void* fn = reinterpret_cast<const void*>(&split_kv_partial<D, R>);
+    long long grid = resident_blocks(fn, threads, pl.lds_bytes);
+    if (grid <= 0) return hipErrorInvalidDeviceFunction;
+    const long long items = (long long)pl.B * pl.Hkv * pl.n_row_blocks * pl.NC;   // upper bound
+    if (grid > items) grid = items;
+    hipLaunchKernelGGL((split_kv_partial<D, R>), dim3((unsigned)grid), dim3(threads), pl.lds_bytes, s, pp);
+    return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_partial_d(const Plan& pl, const PartialParams& pp, hipStream_t s) {
-    const dim3 grid(pl.NC, pl.Hkv * pl.n_row_blocks, pl.B);
-    const dim3 block(64 * pl.nwk * pl.rg_per_block);
     switch (pl.R) {
-#define DECATTN_CASE(RR) \
-        case RR: hipLaunchKernelGGL((split_kv_partial<D, RR>), grid, block, pl.lds_bytes, s, pp); break;
-        DECATTN_CASE(1) DECATTN_CASE(2) DECATTN_CASE(3) DECATTN_CASE(4)
-        DECATTN_CASE(5) DECATTN_CASE(6) DECATTN_CASE(7) DECATTN_CASE(8)
-#undef DECATTN_CASE
+        case 1: return launch_partial_dr<D, 1>(pl, pp, s);
+        case 2: return launch_partial_dr<D, 2>(pl, pp, s);
+        case 3: return launch_partial_dr<D, 3>(pl, pp, s);
+        case 4: return launch_partial_dr<D, 4>(pl, pp, s);
+        case 5: return launch_partial_dr<D, 5>(pl, pp, s);
+        case 6: return launch_partial_dr<D, 6>(pl, pp, s);
+        case 7: return launch_partial_dr<D, 7>(pl, pp, s);
+        case 8: return launch_partial_dr<D, 8>(pl, pp, s);
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 int run_partial(const Plan& pl, const void* q, const void* k, const void* v, const int32_t* lens,
@@ -111,8 +161,13 @@ int run_partial(const Plan& pl, const void* q, const void* k, const void* v, con
     pp.T = pl.T; pp.Hq = pl.Hq; pp.Hkv = pl.Hkv; pp.G = pl.G; pp.S_max = pl.S_max;
     pp.chunk = pl.chunk; pp.NC = pl.NC; pp.RT = pl.RT; pp.causal = causal;
     pp.nwk = pl.nwk; pp.rg_per_block = pl.rg_per_block; pp.n_row_blocks = pl.n_row_blocks;
-    // log2(e) folded into the query: scores come out in log2 units for exp2
-    pp.qscale = (float)((double)scale * 1.4426950408889634);
+    pp.B = pl.B;
+    // scores are taken in log2 units (softmax on exp2): the kernel multiplies
+    // q.k by |scale|*log2(e) and negates q when scale < 0; a zero scale
+    // becomes the smallest normal float, whose scores all round to 2^0
+    const double qs = std::fabs((double)scale) * 1.4426950408889634;
+    pp.qscale = qs < (double)FLT_MIN ? FLT_MIN : (float)qs;
+    pp.qsign = scale < 0.f ? 0x80008000u : 0u;
     const hipError_t e = pl.D == 64 ? launch_partial_d<64>(pl, pp, s) : launch_partial_d<128>(pl, pp, s);
     return e == hipSuccess ? DECATTN_OK : DECATTN_ERR_HIP;
 }
@@ -238,8 +293,8 @@ int attn_merge(const int32_t* lens, int B, int T, int Hq, int Hkv, int D, int S_
 int decattn_probe_read(const void* buf, size_t bytes, void* sink, void* stream) {
     if (!buf || !sink || !aligned16(buf) || (bytes & 15u) || bytes == 0) return DECATTN_ERR_INVALID_ARG;
     const size_t n16 = bytes / 16;
-    size_t blocks = (n16 + kProbeThreads - 1) / kProbeThreads;
-    if (blocks > 256 * 16) blocks = 256 * 16;
+    const size_t blocks = (n16 + kProbeBlockWords - 1) / kProbeBlockWords;
+    if (blocks > 0x7FFFFFFF) return DECATTN_ERR_INVALID_ARG;
     hipLaunchKernelGGL(probe_read, dim3((unsigned)blocks), dim3(kProbeThreads), 0,
                        static_cast<hipStream_t>(stream), static_cast<const uint4*>(buf), n16,
                        static_cast<uint32_t*>(sink));

@@ -28,11 +28,22 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     return (uint16_t)(u >> 16);
 }
 
-// One DPP lane move inside a 16-lane row (bound_ctrl off, all rows/banks on).
+// One DPP lane move inside a 16-lane row, all rows and banks written. Every
+// pattern used here (quad permutes, mirrors, rotations) gives each lane a
+// source inside its row. dpp_move feeds an add, which the compiler fuses into
+// one v_add_f32_dpp; dpp_copy is a bare move (v_mov_b32_dpp, no "old" value).
 template <int CTRL>
 __device__ __forceinline__ float dpp_move(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
         0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_copy(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_copy_i(int x) {
+    return __builtin_amdgcn_mov_dpp(x, CTRL, 0xF, 0xF, false);
 }
 
 constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
@@ -51,6 +62,18 @@ __device__ __forceinline__ float group_sum(float x) {
     x += dpp_move<kDppHalfMirror>(x);
     if constexpr (N == 16) x += dpp_move<kDppMirror>(x);
     return x;
+}
+
+// Lane moves by XOR inside 32-lane halves (ds_swizzle bitmask mode: LDS
+// crossbar, no LDS memory and no VALU slot).
+template <int XOR>
+__device__ __forceinline__ float swizzle_xor(float x) {
+    static_assert(XOR > 0 && XOR < 32, "xor inside 32 lanes");
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x1F | (XOR << 10)));
+}
+template <int XOR>
+__device__ __forceinline__ int swizzle_xor_i(int x) {
+    return __builtin_amdgcn_ds_swizzle(x, 0x1F | (XOR << 10));
 }
 
 // Reduce across the 64/N lane groups of a wave (lanes with equal index inside
@@ -72,6 +95,30 @@ __device__ __forceinline__ float across_groups_max(float x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// acc + a.lo*b.lo + a.hi*b.hi on two packed bf16 pairs (v_dot2c_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), acc, false);
+}
+
+// Raw buffer resource over [base, base + bytes): 16-byte loads at offsets at
+// or past `bytes` return zeros, so rows past a length need no exec masking.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// Cache-policy bits of a gfx950 buffer load: "nt" marks streaming data that
+// is read once. On MI355X it lifts a pure streaming read from about 6.3 to
+// about 7.1 TB/s (measured).
+constexpr int kLoadStream = 2;
+
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kLoadStream);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
 
 __device__ __forceinline__ int clamp_len(int n, int s_max) {
     return n < 0 ? 0 : (n > s_max ? s_max : n);

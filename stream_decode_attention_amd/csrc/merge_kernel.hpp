@@ -8,9 +8,14 @@
 //     out = sum_c w_c acc_c / sum_c w_c l_c,
 // then stored as fp32 or rounded to bf16. Rows with n = 0 store zeros.
 //
-// 256 threads: each handles 4 consecutive dims (one 16-byte load of acc) of a
-// strided subset of the tiles; the per-thread sums are then added in a fixed
-// order through LDS, so the result does not depend on scheduling.
+// The partial state was written by another kernel, so every read misses the
+// reading compute unit's L2; the loads are therefore issued in batches (each
+// thread fetches up to kMergeUnroll tiles at once: 256 tiles of a 128-dim row
+// in one round trip) instead of one dependent round trip per tile.
+// 512 threads: thread (cl, q4) owns 4 dims (one 16-byte load) of the tiles
+// c = cl, cl + NCL, ...; it folds them into a running (m, l, acc) with the
+// same rule, and the NCL tile lanes are combined once in LDS in a fixed order,
+// so the result does not depend on scheduling.
 #pragma once
 
 #include "device_common.hpp"
@@ -26,15 +31,16 @@ struct MergeParams {
     int T, Hq, Hkv, G, S_max, chunk, NC, RT, causal;
 };
 
-constexpr int kMergeThreads = 256;
+constexpr int kMergeThreads = 512;
+constexpr int kMergeUnroll = 16;
 
 template <int D>
 __global__ void __launch_bounds__(kMergeThreads)
 lse_merge(const MergeParams p) {
     constexpr int QPR = D / 4;                    // float4 quads per row
     constexpr int NCL = kMergeThreads / QPR;      // tile lanes working in parallel
-    __shared__ float s_red[kMergeThreads / 64];
     __shared__ float4 s_acc[NCL][QPR];
+    __shared__ float s_m[NCL];
     __shared__ float s_l[NCL];
 
     const int row = blockIdx.x;                   // (b, i, h) flattened
@@ -62,49 +68,69 @@ lse_merge(const MergeParams p) {
     const size_t head0 = (size_t)(b * p.Hkv + kvh) * p.NC * p.RT;   // tile 0, row 0
     const float* ml = p.ws_ml + head0 * 2;
     const float* accp = p.ws_acc + head0 * D;
-
-    // pass 1: M = max over the row's tiles
-    float mx = kNegInf;
-    for (int c = tid; c < na; c += kMergeThreads) mx = fmaxf(mx, ml[((size_t)c * p.RT + r) * 2]);
-    mx = fmaxf(mx, __shfl_xor(mx, 1));
-    mx = fmaxf(mx, __shfl_xor(mx, 2));
-    mx = fmaxf(mx, __shfl_xor(mx, 4));
-    mx = fmaxf(mx, __shfl_xor(mx, 8));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    if ((tid & 63) == 0) s_red[tid >> 6] = mx;
-    __syncthreads();
-    float M = s_red[0];
-#pragma unroll
-    for (int w = 1; w < kMergeThreads / 64; ++w) M = fmaxf(M, s_red[w]);
-
-    // pass 2: weighted sums
     const int q4 = tid % QPR;
     const int cl = tid / QPR;
-    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-    float l = 0.f;
-    for (int c = cl; c < na; c += NCL) {
-        const size_t tr = (size_t)c * p.RT + r;
-        const float wt = fast_exp2(ml[tr * 2] - M);
-        l = __builtin_fmaf(wt, ml[tr * 2 + 1], l);
-        const float4 x = *reinterpret_cast<const float4*>(accp + tr * D + q4 * 4);
-        a.x = __builtin_fmaf(wt, x.x, a.x);
-        a.y = __builtin_fmaf(wt, x.y, a.y);
-        a.z = __builtin_fmaf(wt, x.z, a.z);
-        a.w = __builtin_fmaf(wt, x.w, a.w);
+
+    float m_t = kNegInf, l_t = 0.f;
+    float4 a_t = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int c0 = cl; c0 < na; c0 += NCL * kMergeUnroll) {
+        float mv[kMergeUnroll], lv[kMergeUnroll];
+        float4 av[kMergeUnroll];
+#pragma unroll
+        for (int u = 0; u < kMergeUnroll; ++u) {
+            const int c = c0 + u * NCL;
+            if (c < na) {
+                const size_t tr = (size_t)c * p.RT + r;
+                const float2 x = *reinterpret_cast<const float2*>(ml + tr * 2);
+                mv[u] = x.x;
+                lv[u] = x.y;
+                av[u] = *reinterpret_cast<const float4*>(accp + tr * D + q4 * 4);
+            } else {
+                mv[u] = kNegInf;
+                lv[u] = 0.f;
+                av[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        }
+        float mb = mv[0];
+#pragma unroll
+        for (int u = 1; u < kMergeUnroll; ++u) mb = fmaxf(mb, mv[u]);
+        const float m_new = fmaxf(m_t, mb);           // finite: tile c0 < na is valid
+        const float sc = fast_exp2(m_t - m_new);
+        l_t *= sc;
+        a_t.x *= sc; a_t.y *= sc; a_t.z *= sc; a_t.w *= sc;
+#pragma unroll
+        for (int u = 0; u < kMergeUnroll; ++u) {
+            const float wt = fast_exp2(mv[u] - m_new);
+            l_t = __builtin_fmaf(wt, lv[u], l_t);
+            a_t.x = __builtin_fmaf(wt, av[u].x, a_t.x);
+            a_t.y = __builtin_fmaf(wt, av[u].y, a_t.y);
+            a_t.z = __builtin_fmaf(wt, av[u].z, a_t.z);
+            a_t.w = __builtin_fmaf(wt, av[u].w, a_t.w);
+        }
+        m_t = m_new;
     }
-    s_acc[cl][q4] = a;
-    if (q4 == 0) s_l[cl] = l;
+    s_acc[cl][q4] = a_t;
+    if (q4 == 0) {
+        s_m[cl] = m_t;
+        s_l[cl] = l_t;
+    }
     __syncthreads();
 
     if (cl == 0) {
-        float4 t = s_acc[0][q4];
-        float L = s_l[0];
+        float M = s_m[0];
 #pragma unroll
-        for (int k = 1; k < NCL; ++k) {
+        for (int k = 1; k < NCL; ++k) M = fmaxf(M, s_m[k]);
+        float L = 0.f;
+        float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int k = 0; k < NCL; ++k) {
+            const float wt = fast_exp2(s_m[k] - M);    // lanes with no tile: 2^-inf = 0
             const float4 u = s_acc[k][q4];
-            t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
-            L += s_l[k];
+            L = __builtin_fmaf(wt, s_l[k], L);
+            t.x = __builtin_fmaf(wt, u.x, t.x);
+            t.y = __builtin_fmaf(wt, u.y, t.y);
+            t.z = __builtin_fmaf(wt, u.z, t.z);
+            t.w = __builtin_fmaf(wt, u.w, t.w);
         }
         const float o0 = t.x / L, o1 = t.y / L, o2 = t.z / L, o3 = t.w / L;
         const size_t o = (size_t)row * D + q4 * 4;

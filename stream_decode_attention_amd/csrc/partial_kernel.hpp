@@ -7,31 +7,59 @@
 // kernel merges the chunks. Tiles at or past a row's length exit at once.
 //
 // Work split inside a tile (gfx950, wave64):
-//  * A wave owns R query rows and walks "sub-tiles" of KPW = 32 keys. A key row
-//    of D bf16 (128 or 256 bytes) is spread over LPK = D/8 lanes, 16 bytes per
-//    lane, so one wave-wide 16-byte load covers 64/LPK whole keys: fully
-//    coalesced, no lane reads a byte another lane reads.
-//  * q.k: each lane multiplies its 8 dims by the row's query slice (pre-scaled
-//    by scale*log2(e), kept in VGPRs) and the LPK lanes of a key sum with DPP
-//    moves inside their 16-lane row.
-//  * softmax: an online (running max) softmax over the wave's sub-tiles in the
-//    log2 domain; each lane keeps partial l and acc for the keys of its lane
-//    group, summed across groups once at the end.
-//  * Up to NWK "key waves" split the tile's keys (sub-tile s of wave w covers
-//    keys t0 + (s*NWK + w)*KPW ...); their states are combined once through LDS.
-//  * Waves of the same workgroup may also hold different row groups (the chunk
-//    path has T*G rows per kv head); every row group reads the same K/V tile.
+//  * A wave owns R query rows (padded to RP, a power of two) and walks
+//    "sub-tiles" of KPW keys. A key row of D bf16 (128 or 256 bytes) is spread
+//    over a group of LPK = D/8 lanes, 16 bytes per lane, so one wave-wide
+//    16-byte load covers 64/LPK whole keys: fully coalesced, no byte read
+//    twice. Loads go through a range-checked buffer resource that ends at the
+//    tile's last attended key, so keys past a length read as zeros and are
+//    never touched in memory.
+//  * While a sub-tile is computed, the next NBUF-1 are already being loaded
+//    into other register sets (software pipeline): at full load the HBM
+//    latency is several microseconds, so each compute unit needs on the order
+//    of 128 KB in flight to stream at the roofline.
+//  * q.k: v_dot2c_f32_bf16 on the raw bf16 pairs of q and k gives each lane a
+//    partial dot product over its 8 dims for every row; a butterfly
+//    reduce-scatter over the lane group (DPP moves, halving the rows held at
+//    each stage) leaves each lane with the complete score of ONE row (its
+//    "own" row), so the mask, the exponential and the row sum run once per
+//    lane instead of once per row. p of the other rows is gathered back from
+//    the lanes that own them (DPP row rotations, or ds_swizzle for 8-lane
+//    groups) into "slots": slot k of a lane holds row slot_row[k].
+//  * softmax: online (running-max) softmax over the wave's sub-tiles in log2
+//    units; accumulators are rescaled only when some row's maximum grew.
+//  * Up to NWK "key waves" split the tile (sub-tile s of wave w covers keys
+//    t0 + (s*NWK + w)*KPW ...); their states are combined once through LDS.
+//  * Waves of the same workgroup may hold different row groups (the verify
+//    chunk has T*G rows per kv head); all row groups share the tile's K/V.
 //
 // Every row is computed with the same sequence of floating-point operations
-// whatever R is and whatever other rows share its wave, so a verify-chunk row
-// is bit-identical to the decode call with the same key limit.
+// whatever R is and whatever other rows share its wave (the butterfly pairs
+// lanes in the same fixed order for every row count, and a rescale by an
+// unchanged maximum multiplies by exactly 1), so a verify-chunk row is
+// bit-identical to the decode call with the same key limit.
 #pragma once
 
 #include "device_common.hpp"
 
+#ifndef DECATTN_KEYS_PER_WAVE
+#define DECATTN_KEYS_PER_WAVE 16
+#endif
+#ifndef DECATTN_PREFETCH_FENCE
+#define DECATTN_PREFETCH_FENCE 1
+#endif
+#ifndef DECATTN_NBUF
+#define DECATTN_NBUF 2
+#endif
+#ifndef DECATTN_WAVES_PER_EU
+#define DECATTN_WAVES_PER_EU 1
+#endif
+
 namespace decattn {
 
-constexpr int kKeysPerWave = 32;   // keys a wave handles per sub-tile (KPW)
+constexpr int kKeysPerWave = DECATTN_KEYS_PER_WAVE;   // keys a wave handles per sub-tile (KPW)
+constexpr int kNumBuf = DECATTN_NBUF;                 // sub-tiles in registers: 1 computed + (NBUF-1) in flight
+static_assert(kNumBuf >= 2, "the load pointer must run ahead of the compute pointer");
 
 struct PartialParams {
     const uint16_t* q;      // bf16 [B][T][Hq][D]
@@ -44,193 +72,399 @@ struct PartialParams {
     int nwk;                // key waves per workgroup
     int rg_per_block;       // row groups per workgroup
     int n_row_blocks;       // workgroups per tile along the row axis
-    float qscale;           // scale * log2(e)
+    float qscale;           // |scale| * log2(e), at least FLT_MIN
+    uint32_t qsign;         // 0x80008000 negates both bf16 of a q word (scale < 0), else 0
+    int B;                  // batch rows (lengths staged in LDS)
 };
 
+constexpr int pad_rows(int r) { return r <= 1 ? 1 : r <= 2 ? 2 : r <= 4 ? 4 : 8; }
+constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
+
+// One butterfly stage over bit BIT of the lane's index in its group: holding
+// H rows, a lane keeps the upper H/2 rows if its bit is set (else the lower
+// half) and adds its partner's partial sums of the rows it keeps; with one row
+// left it just adds the partner's value. Partners: BIT 3 row_mirror (l, 15-l),
+// BIT 2 row_half_mirror (l, 7-l), BIT 1 and 0 quad permutes (l^2, l^1).
+template <int BIT, int H>
+__device__ __forceinline__ void butterfly_stage(float (&x)[8], int db) {
+    constexpr int CTRL = BIT == 3 ? kDppMirror : BIT == 2 ? kDppHalfMirror : BIT == 1 ? kDppXor2 : kDppXor1;
+    if constexpr (H > 1) {
+        const bool up = (db >> BIT) & 1;
+#pragma unroll
+        for (int i = 0; i < H / 2; ++i) {
+            const float lo = x[i], hi = x[i + H / 2];
+            const float send = up ? lo : hi;
+            const float keep = up ? hi : lo;
+            x[i] = keep + dpp_move<CTRL>(send);
+        }
+    } else {
+        x[0] = x[0] + dpp_move<CTRL>(x[0]);
+    }
+}
+
+// Reduce-scatter of RP row partials over a group of LPK lanes: returns the
+// full sum of the lane's own row, whose index is the top log2(RP) bits of db.
+template <int LPK, int RP>
+__device__ __forceinline__ float reduce_scatter(float (&x)[8], int db) {
+    constexpr int H2 = LPK == 16 ? (RP > 1 ? RP / 2 : 1) : RP;   // rows held entering bit 2
+    constexpr int H1 = H2 > 1 ? H2 / 2 : 1;
+    constexpr int H0 = H1 > 1 ? H1 / 2 : 1;
+    if constexpr (LPK == 16) butterfly_stage<3, RP>(x, db);
+    butterfly_stage<2, H2>(x, db);
+    butterfly_stage<1, H1>(x, db);
+    butterfly_stage<0, H0>(x, db);
+    return x[0];
+}
+
+// Value of slot K: the same quantity held by the lanes owning row slot_row[K].
+// 16-lane groups rotate inside the DPP row by K row-sets; 8-lane groups swap
+// row-sets by XOR with ds_swizzle.
+template <int LPK, int RP, int K>
+__device__ __forceinline__ float gather_slot(float x) {
+    constexpr int SET = LPK / RP;                       // lanes per row-set
+    if constexpr (K == 0) return x;
+    else if constexpr (LPK == 16) return dpp_copy<0x120 + K * SET>(x);   // row_ror
+    else return swizzle_xor<K * SET>(x);
+}
+template <int LPK, int RP, int K>
+__device__ __forceinline__ int gather_slot_i(int x) {
+    constexpr int SET = LPK / RP;
+    if constexpr (K == 0) return x;
+    else if constexpr (LPK == 16) return dpp_copy_i<0x120 + K * SET>(x);
+    else return swizzle_xor_i<K * SET>(x);
+}
+
+template <int LPK, int RP, int K = 0>
+__device__ __forceinline__ void gather_all(float x, float (&out)[8]) {
+    if constexpr (K < RP) {
+        out[K] = gather_slot<LPK, RP, K>(x);
+        gather_all<LPK, RP, K + 1>(x, out);
+    }
+}
+template <int LPK, int RP, int K = 0>
+__device__ __forceinline__ void gather_all_i(int x, int (&out)[8]) {
+    if constexpr (K < RP) {
+        out[K] = gather_slot_i<LPK, RP, K>(x);
+        gather_all_i<LPK, RP, K + 1>(x, out);
+    }
+}
+
 template <int D, int R>
-__global__ void __launch_bounds__(512)
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(DECATTN_WAVES_PER_EU)))
 split_kv_partial(const PartialParams p) {
     constexpr int LPK = D / 8;              // lanes per key row
     constexpr int KPL = 64 / LPK;           // keys per wave-wide load
     constexpr int NSTEP = kKeysPerWave / KPL;
+    constexpr int RP = pad_rows(R);         // rows per wave, padded
+    constexpr int SET_BITS = ilog2(LPK) - ilog2(RP);
     static_assert(D == 64 || D == 128, "head dim 64 or 128");
+    static_assert(R >= 1 && R <= 8, "1..8 rows per wave");
+    static_assert(NSTEP >= 1 && NSTEP * KPL == kKeysPerWave, "keys per wave must be a multiple of keys per load");
 
     extern __shared__ float smem[];
+    __shared__ int s_count[16];
 
-    const int c = blockIdx.x;
-    const int kvh = blockIdx.y / p.n_row_blocks;
-    const int rblk = blockIdx.y - kvh * p.n_row_blocks;
-    const int b = blockIdx.z;
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
     const int kw = wave % p.nwk;
     const int rgl = wave / p.nwk;
-    const int rg = rblk * p.rg_per_block + rgl;
-
-    const int len = p.lens[b];
-    const int t0 = c * p.chunk;
-    const int t1 = min(t0 + p.chunk, p.S_max);
-    const int lim_tile = clamp_len(p.causal ? len + p.T : len, p.S_max);
-    if (t0 >= lim_tile) return;             // whole workgroup: nothing to attend
-    const int lim_all = min(lim_tile, t1);
-
     const int kk = lane / LPK;              // key slot inside one load
     const int db = lane % LPK;              // 8-dim block of this lane
+    const int own = db >> SET_BITS;         // the row this lane completes
+    int slot_row[8];
+    gather_all_i<LPK, RP>(own, slot_row);
 
-    // ---- stage this wave's query rows (fp32, pre-scaled) and key limits
-    float qf[R][8];
-    int row_lim[R];
-#pragma unroll
-    for (int j = 0; j < R; ++j) {
-        const int r = rg * R + j;
-        if (r < p.RT) {
-            const int i = r / p.G;
-            const int h = kvh * p.G + (r - i * p.G);
-            const int n = clamp_len(p.causal ? len + i + 1 : len, p.S_max);
-            row_lim[j] = min(n, t1);
-            const uint4 raw = *reinterpret_cast<const uint4*>(
-                p.q + ((size_t)(b * p.T + i) * p.Hq + h) * D + db * 8);
-            float f[8];
-            bf16x8_to_f32(raw, f);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) qf[j][e] = f[e] * p.qscale;
-        } else {
-            row_lim[j] = 0;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) qf[j][e] = 0.f;
-        }
+    // ---- lengths into LDS; count the tiles that hold attended keys
+    float* s_acc = smem;                                    // [rgb][nwk][R][D]
+    float* s_ml = smem + (size_t)p.rg_per_block * p.nwk * R * D;   // [rgb][nwk][R][2]
+    int* s_len = reinterpret_cast<int*>(s_ml + (size_t)p.rg_per_block * p.nwk * R * 2);   // [B]
+    int my_tiles = 0;
+    for (int i = tid; i < p.B; i += blockDim.x) {
+        const int len = p.lens[i];
+        s_len[i] = len;
+        const int lim = clamp_len(p.causal ? len + p.T : len, p.S_max);
+        my_tiles += (lim + p.chunk - 1) / p.chunk;
     }
-
-    float m_run[R], l_run[R], acc[R][8];
-#pragma unroll
-    for (int j = 0; j < R; ++j) {
-        m_run[j] = kNegInf;
-        l_run[j] = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
-    }
-
-    const size_t head_base = (size_t)(b * p.Hkv + kvh) * p.S_max * D + db * 8;
-    const uint16_t* kbase = p.k + head_base;
-    const uint16_t* vbase = p.v + head_base;
-    const int sub_stride = p.nwk * kKeysPerWave;
-
-    for (int base = t0 + kw * kKeysPerWave; base < lim_all; base += sub_stride) {
-        uint4 kr[NSTEP], vr[NSTEP];
-#pragma unroll
-        for (int st = 0; st < NSTEP; ++st) {
-            const int j = base + st * KPL + kk;
-            if (j < lim_all) {
-                kr[st] = *reinterpret_cast<const uint4*>(kbase + (size_t)j * D);
-                vr[st] = *reinterpret_cast<const uint4*>(vbase + (size_t)j * D);
-            } else {
-                kr[st] = make_uint4(0, 0, 0, 0);
-                vr[st] = make_uint4(0, 0, 0, 0);
-            }
-        }
-
-        // scores in log2 units; keys at or past a row's limit get -inf
-        float s[NSTEP][R];
-#pragma unroll
-        for (int st = 0; st < NSTEP; ++st) {
-            float kf[8];
-            bf16x8_to_f32(kr[st], kf);
-            const int j = base + st * KPL + kk;
-#pragma unroll
-            for (int jr = 0; jr < R; ++jr) {
-                float part = qf[jr][0] * kf[0];
-#pragma unroll
-                for (int e = 1; e < 8; ++e) part = __builtin_fmaf(qf[jr][e], kf[e], part);
-                part = group_sum<LPK>(part);
-                s[st][jr] = (j < row_lim[jr]) ? part : kNegInf;
-            }
-        }
-
-        float vf[NSTEP][8];
-#pragma unroll
-        for (int st = 0; st < NSTEP; ++st) bf16x8_to_f32(vr[st], vf[st]);
-
-#pragma unroll
-        for (int jr = 0; jr < R; ++jr) {
-            float mx = s[0][jr];
-#pragma unroll
-            for (int st = 1; st < NSTEP; ++st) mx = fmaxf(mx, s[st][jr]);
-            mx = across_groups_max<LPK>(mx);
-            const float m_new = fmaxf(m_run[jr], mx);
-            const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-            const float alpha = fast_exp2(m_run[jr] - m_use);
-            m_run[jr] = m_new;
-            float l = l_run[jr] * alpha;
-            float a[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) a[e] = acc[jr][e] * alpha;
-#pragma unroll
-            for (int st = 0; st < NSTEP; ++st) {
-                const float pj = fast_exp2(s[st][jr] - m_use);
-                l += pj;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) a[e] = __builtin_fmaf(pj, vf[st][e], a[e]);
-            }
-            l_run[jr] = l;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[jr][e] = a[e];
-        }
-    }
-
-    // ---- sum the lane groups of the wave, then combine the key waves in LDS
-#pragma unroll
-    for (int jr = 0; jr < R; ++jr) {
-        l_run[jr] = across_groups_sum<LPK>(l_run[jr]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[jr][e] = across_groups_sum<LPK>(acc[jr][e]);
-    }
-
-    // LDS: [rg_per_block][nwk][R] x (D acc floats), then [rg_per_block][nwk][R] x (m, l)
-    float* s_acc = smem;
-    float* s_ml = smem + (size_t)p.rg_per_block * p.nwk * R * D;
-    const int slot = (rgl * p.nwk + kw) * R;
-    if (kk == 0) {
-#pragma unroll
-        for (int jr = 0; jr < R; ++jr) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) s_acc[(size_t)(slot + jr) * D + db * 8 + e] = acc[jr][e];
-        }
-    }
-    if (lane == 0) {
-#pragma unroll
-        for (int jr = 0; jr < R; ++jr) {
-            s_ml[(slot + jr) * 2 + 0] = m_run[jr];
-            s_ml[(slot + jr) * 2 + 1] = l_run[jr];
-        }
-    }
+    for (int o = 32; o > 0; o >>= 1) my_tiles += __shfl_xor(my_tiles, o);
+    if (lane == 0) s_count[wave] = my_tiles;
     __syncthreads();
+    int n_tiles = 0;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) n_tiles += s_count[w];
+    const int per_tile = p.Hkv * p.n_row_blocks;            // work items per (b, tile)
+    const int n_items = n_tiles * per_tile;
 
-    const int total = p.rg_per_block * R * D;
-    const size_t tile_row0 = ((size_t)(b * p.Hkv + kvh) * p.NC + c) * p.RT;
-    for (int idx = threadIdx.x; idx < total; idx += blockDim.x) {
-        const int rg2 = idx / (R * D);
-        const int rem = idx - rg2 * (R * D);
-        const int jr = rem / D;
-        const int d = rem - jr * D;
-        const int r = (rblk * p.rg_per_block + rg2) * R + jr;
-        if (r >= p.RT) continue;
-        const int base_slot = rg2 * p.nwk * R + jr;     // slot of key wave 0 for this row
-        float M = kNegInf;
-        for (int w = 0; w < p.nwk; ++w) M = fmaxf(M, s_ml[(base_slot + w * R) * 2]);
-        float A = 0.f, L = 0.f;
-        if (M != kNegInf) {
-            for (int w = 0; w < p.nwk; ++w) {
-                const int sl = base_slot + w * R;
-                const float wt = fast_exp2(s_ml[sl * 2] - M);
-                A = __builtin_fmaf(wt, s_acc[(size_t)sl * D + d], A);
-                L = __builtin_fmaf(wt, s_ml[sl * 2 + 1], L);
+    // Work item t enumerates (b, kvh, row block, tile c) over attended tiles
+    // only, b-major; workgroup w takes items w, w + P, w + 2P, ... (P = grid),
+    // so every workgroup gets the same number of items to within one. The
+    // walk over b only moves forward.
+    int b_cur = 0, pre_cur = 0;
+    auto tiles_of = [&](int b) {
+        const int len = s_len[b];
+        return (clamp_len(p.causal ? len + p.T : len, p.S_max) + p.chunk - 1) / p.chunk;
+    };
+
+    struct Tile {
+        int b, kvh, rblk, c, len, t0, t1, lim_all;
+    };
+    auto locate = [&](int t) {
+        while (t >= pre_cur + tiles_of(b_cur) * per_tile) {
+            pre_cur += tiles_of(b_cur) * per_tile;
+            ++b_cur;
+        }
+        Tile tl;
+        const int na = tiles_of(b_cur);
+        const int u = t - pre_cur;
+        tl.b = b_cur;
+        tl.c = u % na;
+        const int rest = u / na;
+        tl.rblk = rest % p.n_row_blocks;
+        tl.kvh = rest / p.n_row_blocks;
+        tl.len = s_len[b_cur];
+        tl.t0 = tl.c * p.chunk;
+        tl.t1 = min(tl.t0 + p.chunk, p.S_max);
+        tl.lim_all = min(clamp_len(p.causal ? tl.len + p.T : tl.len, p.S_max), tl.t1);
+        return tl;
+    };
+
+    // this wave's query rows of a tile (raw bf16 pairs) and its own row's key limit
+    auto load_q = [&](const Tile& tl, uint4 (&qraw)[RP], int& my_lim) {
+        const int rg = tl.rblk * p.rg_per_block + rgl;
+        my_lim = 0;
+#pragma unroll
+        for (int j = 0; j < RP; ++j) {
+            const int r = rg * R + j;
+            if (j < R && r < p.RT) {
+                const int i = r / p.G;
+                const int h = tl.kvh * p.G + (r - i * p.G);
+                const int n = min(clamp_len(p.causal ? tl.len + i + 1 : tl.len, p.S_max), tl.t1);
+                if (j == own) my_lim = n;
+                uint4 qv = *reinterpret_cast<const uint4*>(
+                    p.q + ((size_t)(tl.b * p.T + i) * p.Hq + h) * D + db * 8);
+                qv.x ^= p.qsign; qv.y ^= p.qsign; qv.z ^= p.qsign; qv.w ^= p.qsign;
+                qraw[j] = qv;
+            } else {
+                qraw[j] = make_uint4(0, 0, 0, 0);
             }
         }
-        p.ws_acc[(tile_row0 + r) * D + d] = A;
-        if (d == 0) {
-            p.ws_ml[(tile_row0 + r) * 2 + 0] = M;
-            p.ws_ml[(tile_row0 + r) * 2 + 1] = L;
+    };
+
+    const uint32_t lane_off = (uint32_t)(kk * D + db * 8) * 2;
+    const int sub_stride = p.nwk * kKeysPerWave;
+    const float qs = p.qscale;
+
+    // K/V of a tile's (b, kvh): rows [0, lim_all) are in range, the rest read as 0
+    struct Rsrc {
+        __amdgpu_buffer_rsrc_t k, v;
+    };
+    auto make_tile_rsrc = [&](const Tile& tl) {
+        const size_t head_base = (size_t)(tl.b * p.Hkv + tl.kvh) * p.S_max * D;
+        const uint32_t range = (uint32_t)tl.lim_all * D * 2;
+        return Rsrc{make_rsrc(p.k + head_base, range), make_rsrc(p.v + head_base, range)};
+    };
+
+    auto load = [&](const Rsrc& rs, uint4 (&kb)[NSTEP], uint4 (&vb)[NSTEP], int base) {
+        // keys at or past lim_all (including a whole sub-tile past the tile)
+        // are outside the resource and load zeros; base < S_max + chunk keeps
+        // the byte offset far below 2^32
+        const uint32_t off = (uint32_t)base * (D * 2) + lane_off;
+#pragma unroll
+        for (int st = 0; st < NSTEP; ++st) {
+            kb[st] = buffer_load16(rs.k, off + st * KPL * D * 2);
+            vb[st] = buffer_load16(rs.v, off + st * KPL * D * 2);
         }
+    };
+
+    float m_run, l_run;                     // own row
+    float acc[RP][8];                       // slot k, this lane's 8 dims
+
+    auto compute = [&](const uint4 (&qraw)[RP], int my_lim, const uint4 (&kb)[NSTEP],
+                       const uint4 (&vb)[NSTEP], int base) {
+        // own-row scores in log2 units, -inf past the row's limit
+        float dm[NSTEP];
+#pragma unroll
+        for (int st = 0; st < NSTEP; ++st) {
+            float x[8];
+#pragma unroll
+            for (int j = 0; j < RP; ++j) {
+                float d = dot2_bf16(qraw[j].x, kb[st].x, 0.f);
+                d = dot2_bf16(qraw[j].y, kb[st].y, d);
+                d = dot2_bf16(qraw[j].z, kb[st].z, d);
+                x[j] = dot2_bf16(qraw[j].w, kb[st].w, d);
+            }
+            const float d = reduce_scatter<LPK, RP>(x, db);
+            const int j = base + st * KPL + kk;
+            // the score is rounded once here and the maximum is taken over the
+            // same values, so the largest key gets 2^0 = 1 exactly
+            dm[st] = (j < my_lim) ? d * qs : kNegInf;
+        }
+        float mx = dm[0];
+#pragma unroll
+        for (int st = 1; st < NSTEP; ++st) mx = fmaxf(mx, dm[st]);
+        mx = across_groups_max<LPK>(mx);
+        const float m_new = fmaxf(m_run, mx);
+        const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+        if (__any(m_run != kNegInf && m_new > m_run)) {   // some row's maximum grew
+            const float alpha = fast_exp2(m_run - m_use);
+            l_run *= alpha;
+            float al[8];
+            gather_all<LPK, RP>(alpha, al);
+#pragma unroll
+            for (int k = 0; k < RP; ++k)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[k][e] *= al[k];
+        }
+        m_run = m_new;
+#pragma unroll
+        for (int st = 0; st < NSTEP; ++st) {
+            const float pj = fast_exp2(dm[st] - m_use);
+            l_run += pj;
+            float ps[8];
+            gather_all<LPK, RP>(pj, ps);
+            float vf[8];
+            bf16x8_to_f32(vb[st], vf);
+#pragma unroll
+            for (int k = 0; k < RP; ++k)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[k][e] = __builtin_fmaf(ps[k], vf[e], acc[k][e]);
+        }
+    };
+
+    auto reset_state = [&]() {
+        m_run = kNegInf;
+        l_run = 0.f;
+#pragma unroll
+        for (int k = 0; k < RP; ++k)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[k][e] = 0.f;
+    };
+
+    // Sum the lane groups of the wave, combine the key waves of the workgroup
+    // in LDS and write the tile's partial state. Every wave calls this once per
+    // work item, in the same order (two workgroup barriers).
+    auto finish = [&](const Tile& tl) {
+        l_run = across_groups_sum<LPK>(l_run);
+#pragma unroll
+        for (int k = 0; k < RP; ++k)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[k][e] = across_groups_sum<LPK>(acc[k][e]);
+
+        const int slot = (rgl * p.nwk + kw) * R;
+        if (kk == 0) {
+#pragma unroll
+            for (int k = 0; k < RP; ++k) {
+                const int row = slot_row[k];
+                if (row < R) {
+                    float4* dst = reinterpret_cast<float4*>(s_acc + (size_t)(slot + row) * D + db * 8);
+                    dst[0] = make_float4(acc[k][0], acc[k][1], acc[k][2], acc[k][3]);
+                    dst[1] = make_float4(acc[k][4], acc[k][5], acc[k][6], acc[k][7]);
+                }
+            }
+            if ((db & ((1 << SET_BITS) - 1)) == 0 && own < R) {
+                s_ml[(slot + own) * 2 + 0] = m_run;
+                s_ml[(slot + own) * 2 + 1] = l_run;
+            }
+        }
+        __syncthreads();
+
+        const int total = p.rg_per_block * R * D;
+        const size_t tile_row0 = ((size_t)(tl.b * p.Hkv + tl.kvh) * p.NC + tl.c) * p.RT;
+        for (int idx = tid; idx < total; idx += blockDim.x) {
+            const int rg2 = idx / (R * D);
+            const int rem = idx - rg2 * (R * D);
+            const int jr = rem / D;
+            const int d = rem - jr * D;
+            const int r = (tl.rblk * p.rg_per_block + rg2) * R + jr;
+            if (r >= p.RT) continue;
+            const int base_slot = rg2 * p.nwk * R + jr;     // slot of key wave 0 for this row
+            float M = kNegInf;
+            for (int w = 0; w < p.nwk; ++w) M = fmaxf(M, s_ml[(base_slot + w * R) * 2]);
+            float A = 0.f, L = 0.f;
+            if (M != kNegInf) {
+                for (int w = 0; w < p.nwk; ++w) {
+                    const int sl = base_slot + w * R;
+                    const float wt = fast_exp2(s_ml[sl * 2] - M);
+                    A = __builtin_fmaf(wt, s_acc[(size_t)sl * D + d], A);
+                    L = __builtin_fmaf(wt, s_ml[sl * 2 + 1], L);
+                }
+            }
+            p.ws_acc[(tile_row0 + r) * D + d] = A;
+            if (d == 0) {
+                p.ws_ml[(tile_row0 + r) * 2 + 0] = M;
+                p.ws_ml[(tile_row0 + r) * 2 + 1] = L;
+            }
+        }
+        __syncthreads();                    // LDS is rewritten by the next item's combine
+    };
+
+    // ---- one stream of sub-tiles across this workgroup's work items
+    // Work items of this workgroup: blockIdx.x, +P, +2P, ... Each item gives a
+    // wave SPT slots (sub-tile s at t0 + kw*KPW + s*stride), SPT rounded up to
+    // a multiple of kNumBuf; slots at or past the item's last key read nothing
+    // (outside the buffer resource) and are not computed. A ring of kNumBuf
+    // register slots holds loaded sub-tiles and the load pointer runs
+    // kNumBuf-1 slots ahead of the compute pointer, across item boundaries,
+    // so the memory pipe stays full from one item to the next; since an item
+    // has at least kNumBuf slots, the load pointer is at most one item ahead
+    // (one spare set of query registers), and every item ends at the end of a
+    // ring cycle, where it is combined.
+    int c_item = blockIdx.x;
+    if (c_item >= n_items) return;          // workgroup-uniform
+    const int P = (int)gridDim.x;
+    const int spt_real = (p.chunk + sub_stride - 1) / sub_stride;
+    const int spt = (spt_real + kNumBuf - 1) / kNumBuf * kNumBuf;
+
+    uint4 kb[kNumBuf][NSTEP], vb[kNumBuf][NSTEP];
+    uint4 qc[RP], qn[RP];
+    int limc, limn = 0;
+
+    Tile ct = locate(c_item);
+    load_q(ct, qc, limc);
+    int l_item = c_item;                    // work item of the load pointer
+    int l_s = 0;                            // its next slot
+    Tile lt = ct;
+    Rsrc lrs = make_tile_rsrc(lt);
+
+    auto issue = [&](uint4 (&kd)[NSTEP], uint4 (&vd)[NSTEP]) {
+        if (l_s == spt) {                   // the load pointer enters the next item
+            l_s = 0;
+            l_item += P;
+            if (l_item < n_items) {
+                lt = locate(l_item);
+                lrs = make_tile_rsrc(lt);
+                load_q(lt, qn, limn);
+            }
+        }
+        // past the last item, or past the item's keys: reads nothing
+        const int base = (l_item < n_items && l_s < spt_real) ? lt.t0 + kw * kKeysPerWave + l_s * sub_stride
+                                                              : lt.lim_all;
+        load(lrs, kd, vd, min(base, lt.lim_all));
+        ++l_s;
+    };
+
+    reset_state();
+#pragma unroll
+    for (int u = 0; u < kNumBuf - 1; ++u) issue(kb[u], vb[u]);
+
+    for (;;) {
+        for (int s0 = 0; s0 < spt; s0 += kNumBuf) {
+#pragma unroll
+            for (int u = 0; u < kNumBuf; ++u) {
+                const int nu = (u + kNumBuf - 1) % kNumBuf;     // constant after unrolling
+                issue(kb[nu], vb[nu]);
+                if (DECATTN_PREFETCH_FENCE) __builtin_amdgcn_sched_barrier(0);
+                const int base = ct.t0 + kw * kKeysPerWave + (s0 + u) * sub_stride;
+                if (s0 + u < spt_real && base < ct.lim_all) compute(qc, limc, kb[u], vb[u], base);
+            }
+        }
+        finish(ct);
+        c_item += P;
+        if (c_item >= n_items) break;
+        ct = lt;                            // the load pointer is already in this item
+#pragma unroll
+        for (int j = 0; j < RP; ++j) qc[j] = qn[j];
+        limc = limn;
+        reset_state();
     }
 }
 

@@ -12,22 +12,25 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kProbeThreads = 256;
 constexpr int kProbeUnroll = 4;
 
+// Each workgroup streams its own 64 KB block as 4 KB pages (one 16-byte load
+// per thread per page), four pages in flight: the pattern that sustains the
+// highest read rate measured on MI355X (about 7 TB/s).
+constexpr int kProbeBlockWords = 4096;      // 16-byte words per workgroup (64 KB)
+
 __global__ void __launch_bounds__(kProbeThreads)
 probe_read(const uint4* __restrict__ buf, size_t n16, uint32_t* sink) {
-    const size_t stride = (size_t)gridDim.x * kProbeThreads;
-    size_t i = (size_t)blockIdx.x * kProbeThreads + threadIdx.x;
+    const size_t w0 = (size_t)blockIdx.x * kProbeBlockWords + threadIdx.x;
     uint32_t x = 0;
-    for (; i + (kProbeUnroll - 1) * stride < n16; i += kProbeUnroll * stride) {
+    for (int p0 = 0; p0 < kProbeBlockWords / kProbeThreads; p0 += kProbeUnroll) {
         u32x4 v[kProbeUnroll];
 #pragma unroll
-        for (int u = 0; u < kProbeUnroll; ++u)
-            v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(buf + i + u * stride));
+        for (int u = 0; u < kProbeUnroll; ++u) {
+            const size_t i = w0 + (size_t)(p0 + u) * kProbeThreads;
+            v[u] = i < n16 ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(buf + i))
+                           : u32x4{0, 0, 0, 0};
+        }
 #pragma unroll
         for (int u = 0; u < kProbeUnroll; ++u) x ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
-    }
-    for (; i < n16; i += stride) {
-        const uint4 v = buf[i];
-        x ^= v.x ^ v.y ^ v.z ^ v.w;
     }
     // a data-dependent store that almost never happens keeps the loads alive
     if (x == 0x9E3779B9u) *sink = x;

@@ -92,6 +92,7 @@ def _decode(lib, **kw):
     (dict(B=0), 1), (dict(S=-1), 1), (dict(Hkv=0), 1),
     (dict(D=96), 2), (dict(D=256), 2),      # head dim
     (dict(Hq=18, Hkv=2), 2),                # G = 9 > 8
+    (dict(B=4097), 2),                      # lengths staged in LDS: B <= 4096
     (dict(chunk=48), 2), (dict(chunk=8), 2), (dict(chunk=-32), 2), (dict(chunk=1 << 21), 2),
     (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(lens=None), 1),
     (dict(out=None), 1), (dict(ws=None), 1),
