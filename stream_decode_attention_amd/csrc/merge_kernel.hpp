@@ -51,12 +51,42 @@ lse_merge(const MergeParams p) {
     const int kvh = h / p.G;
     const int r = i * p.G + (h - kvh * p.G);
 
+    const size_t head0 = (size_t)(b * p.Hkv + kvh) * p.NC * p.RT;   // tile 0, row 0
+    const float* ml = p.ws_ml + head0 * 2;
+    const float* accp = p.ws_acc + head0 * D;
+    const int tid = threadIdx.x;
+    const int q4 = tid % QPR;
+    const int cl = tid / QPR;
+
+    // The first batch of tile loads does not wait for the row's length: tiles
+    // c < NC always lie inside the workspace, and those at or past the row's
+    // tile count (stale data from earlier calls) are dropped by a select.
+    float mv[kMergeUnroll], lv[kMergeUnroll];
+    float4 av[kMergeUnroll];
+    auto fetch = [&](int c0, int bound) {
+#pragma unroll
+        for (int u = 0; u < kMergeUnroll; ++u) {
+            const int c = c0 + u * NCL;
+            if (c < bound) {
+                const size_t tr = (size_t)c * p.RT + r;
+                const float2 x = *reinterpret_cast<const float2*>(ml + tr * 2);
+                mv[u] = x.x;
+                lv[u] = x.y;
+                av[u] = *reinterpret_cast<const float4*>(accp + tr * D + q4 * 4);
+            } else {
+                mv[u] = kNegInf;
+                lv[u] = 0.f;
+                av[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        }
+    };
+    fetch(cl, p.NC);
+
     const int len = p.lens[b];
     const int n = clamp_len(p.causal ? len + i + 1 : len, p.S_max);
     int na = (n + p.chunk - 1) / p.chunk;
     na = na < p.NC ? na : p.NC;
 
-    const int tid = threadIdx.x;
     if (na == 0) {
         if (tid < D) {
             if (p.out_bf16) reinterpret_cast<uint16_t*>(p.out)[(size_t)row * D + tid] = 0;
@@ -65,27 +95,13 @@ lse_merge(const MergeParams p) {
         return;
     }
 
-    const size_t head0 = (size_t)(b * p.Hkv + kvh) * p.NC * p.RT;   // tile 0, row 0
-    const float* ml = p.ws_ml + head0 * 2;
-    const float* accp = p.ws_acc + head0 * D;
-    const int q4 = tid % QPR;
-    const int cl = tid / QPR;
-
     float m_t = kNegInf, l_t = 0.f;
     float4 a_t = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int c0 = cl; c0 < na; c0 += NCL * kMergeUnroll) {
-        float mv[kMergeUnroll], lv[kMergeUnroll];
-        float4 av[kMergeUnroll];
+        if (c0 != cl) fetch(c0, na);
 #pragma unroll
         for (int u = 0; u < kMergeUnroll; ++u) {
-            const int c = c0 + u * NCL;
-            if (c < na) {
-                const size_t tr = (size_t)c * p.RT + r;
-                const float2 x = *reinterpret_cast<const float2*>(ml + tr * 2);
-                mv[u] = x.x;
-                lv[u] = x.y;
-                av[u] = *reinterpret_cast<const float4*>(accp + tr * D + q4 * 4);
-            } else {
+            if (c0 + u * NCL >= na) {       // not this row's tile: drop (select, no arithmetic)
                 mv[u] = kNegInf;
                 lv[u] = 0.f;
                 av[u] = make_float4(0.f, 0.f, 0.f, 0.f);
