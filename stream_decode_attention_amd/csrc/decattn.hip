@@ -18,6 +18,7 @@
 #include "merge_kernel.hpp"
 #include "partial_kernel.hpp"
 #include "probe_kernel.hpp"
+#include "verify_kernel.hpp"
 
 namespace decattn {
 namespace {
@@ -40,9 +41,14 @@ struct Plan {
     int B, T, Hq, Hkv, G, D, S_max, chunk, NC, RT;
     int R, NR, nwk, rg_per_block, n_row_blocks;
     size_t ml_bytes, acc_bytes, total_bytes, lds_bytes;
+    bool mfma;              // verify chunk on the matrix cores
+    int mfma_kb;            // 32-key blocks per wave in the matrix-core kernel
+    size_t mfma_lds_main, mfma_lds_bytes;
 };
 
-int pick_default_chunk(int B, int Hkv, int S_max) {
+int pick_default_chunk(int B, int T, int G, int Hkv, int S_max) {
+    // verify chunks that fit the matrix-core kernel: 256-key tiles
+    if (T > 1 && T * G <= kVerifyMaxRows) return 256;
     // Enough tiles to occupy the 256 compute units several times over while
     // S_max is the only length the host knows; larger tiles cut partial-state
     // traffic (about G*(D+2)*4 bytes per tile against 4*D bytes per key).
@@ -58,7 +64,7 @@ int make_plan(int B, int T, int Hq, int Hkv, int D, int S_max, int chunk, Plan* 
     if (D != 64 && D != 128) return DECATTN_ERR_UNSUPPORTED;
     const int G = Hq / Hkv;
     if (G > kMaxG || T > kMaxT) return DECATTN_ERR_UNSUPPORTED;
-    if (chunk == 0) chunk = pick_default_chunk(B, Hkv, S_max);
+    if (chunk == 0) chunk = pick_default_chunk(B, T, G, Hkv, S_max);
     // a chunk >= S_max gives one tile per row
     if (chunk < kMinChunk || chunk > kMaxChunk || !is_pow2(chunk)) return DECATTN_ERR_UNSUPPORTED;
     const long long nc = ((long long)S_max + chunk - 1) / chunk;
@@ -83,6 +89,17 @@ int make_plan(int B, int T, int Hq, int Hkv, int D, int S_max, int chunk, Plan* 
     // work items (b, kvh, row block, tile) must fit the kernel's int counters
     if ((long long)B * Hkv * p.n_row_blocks * nc > 0x7FFFFFFF) return DECATTN_ERR_UNSUPPORTED;
     p.lds_bytes = (size_t)rgb * lds_per_rg + lds_lens;
+
+    // verify chunks of at most 32 rows per kv head on tiles of a multiple of
+    // 128 keys run on the matrix cores (scores and p.V are dense products there)
+    p.mfma = T > 1 && p.RT <= kVerifyMaxRows && chunk % 128 == 0;
+    p.mfma_kb = chunk % 256 == 0 ? 2 : 1;
+    {
+        const size_t vt = (size_t)kVerifyWaves * D * (32 * p.mfma_kb) * 2;
+        const size_t comb = (size_t)kVerifyWaves * p.RT * D * 4 + (size_t)kVerifyWaves * p.RT * 2 * 4;
+        p.mfma_lds_main = (vt > comb ? vt : comb);
+        p.mfma_lds_bytes = p.mfma_lds_main + lds_lens;
+    }
 
     const size_t tiles_rows = (size_t)B * Hkv * p.NC * p.RT;
     p.ml_bytes = round_up(tiles_rows * 2 * sizeof(float), kAlign);
@@ -113,6 +130,9 @@ int resident_blocks(const void* kernel, int threads, size_t lds) {
                 return e.second;
     }
     int cus = 0, per_cu = 0;
+    if (lds > 64 * 1024 &&
+        hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+        return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds) != hipSuccess) return 0;
     const int n = cus * (per_cu > 0 ? per_cu : 1);
@@ -134,8 +154,22 @@ hipError_t launch_partial_dr(const Plan& pl, const PartialParams& pp, hipStream_
     return hipGetLastError();
 }
 
+template <int D, int KB>
+hipError_t launch_verify_dk(const Plan& pl, const PartialParams& pp, hipStream_t s) {
+    const void* fn = reinterpret_cast<const void*>(&verify_partial_mfma<D, KB>);
+    long long grid = resident_blocks(fn, 64 * kVerifyWaves, pl.mfma_lds_bytes);
+    if (grid <= 0) return hipErrorInvalidDeviceFunction;
+    const long long items = (long long)pl.B * pl.Hkv * pl.NC;   // upper bound
+    if (grid > items) grid = items;
+    hipLaunchKernelGGL((verify_partial_mfma<D, KB>), dim3((unsigned)grid), dim3(64 * kVerifyWaves),
+                       pl.mfma_lds_bytes, s, pp);
+    return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_partial_d(const Plan& pl, const PartialParams& pp, hipStream_t s) {
+    if (pl.mfma && pp.causal)
+        return pl.mfma_kb == 2 ? launch_verify_dk<D, 2>(pl, pp, s) : launch_verify_dk<D, 1>(pl, pp, s);
     switch (pl.R) {
         case 1: return launch_partial_dr<D, 1>(pl, pp, s);
         case 2: return launch_partial_dr<D, 2>(pl, pp, s);
@@ -162,6 +196,7 @@ int run_partial(const Plan& pl, const void* q, const void* k, const void* v, con
     pp.chunk = pl.chunk; pp.NC = pl.NC; pp.RT = pl.RT; pp.causal = causal;
     pp.nwk = pl.nwk; pp.rg_per_block = pl.rg_per_block; pp.n_row_blocks = pl.n_row_blocks;
     pp.B = pl.B;
+    pp.lds_main = (int)pl.mfma_lds_main;
     // scores are taken in log2 units (softmax on exp2): the kernel multiplies
     // q.k by |scale|*log2(e) and negates q when scale < 0; a zero scale
     // becomes the smallest normal float, whose scores all round to 2^0

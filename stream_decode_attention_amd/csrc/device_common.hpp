@@ -115,9 +115,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // about 7.1 TB/s (measured).
 constexpr int kLoadStream = 2;
 
-__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kLoadStream);
+template <int POLICY>
+__device__ __forceinline__ uint4 buffer_load16_policy(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, POLICY);
     return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return buffer_load16_policy<kLoadStream>(r, off);
 }
 
 __device__ __forceinline__ int clamp_len(int n, int s_max) {

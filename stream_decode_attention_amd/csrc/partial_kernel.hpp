@@ -36,8 +36,8 @@
 // Every row is computed with the same sequence of floating-point operations
 // whatever R is and whatever other rows share its wave (the butterfly pairs
 // lanes in the same fixed order for every row count, and a rescale by an
-// unchanged maximum multiplies by exactly 1), so a verify-chunk row is
-// bit-identical to the decode call with the same key limit.
+// unchanged maximum multiplies by exactly 1), so a verify-chunk row computed
+// here is bit-identical to the decode call with the same key limit.
 #pragma once
 
 #include "device_common.hpp"
@@ -75,6 +75,7 @@ struct PartialParams {
     float qscale;           // |scale| * log2(e), at least FLT_MIN
     uint32_t qsign;         // 0x80008000 negates both bf16 of a q word (scale < 0), else 0
     int B;                  // batch rows (lengths staged in LDS)
+    int lds_main;           // bytes of dynamic LDS before the staged lengths (verify kernel)
 };
 
 constexpr int pad_rows(int r) { return r <= 1 ? 1 : r <= 2 ? 2 : r <= 4 ? 4 : 8; }

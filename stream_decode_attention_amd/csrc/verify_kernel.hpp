@@ -1,0 +1,311 @@
+// Verify-chunk partial attention on the matrix cores (gfx950 MFMA).
+//
+// The verify pass of speculative decoding (tinydecode README, "speculative
+// decoding") attends T query tokens, each over the cache plus the tokens
+// before it, for all G query heads of a kv head: T*G rows share every key and
+// value row, so scores and p.V are genuine matrix products (18 rows x 128 dims
+// per key at the Llama-3.2-3B shape: about 18 flop per byte read, above what
+// the vector ALUs sustain at HBM speed). This kernel computes the same partial
+// state (m, l, acc) per tile as split_kv_partial, for up to 32 rows per kv
+// head, with v_mfma_f32_32x32x16_bf16:
+//
+//  * scores as S^T = K Q^T: the A operand of a lane is 16 contiguous bytes of
+//    one key row (key = lane % 32, dims 8*(lane/32)..+7 of a 16-dim step), the
+//    B operand the same slice of one query row; no transpose of K. Lane l ends
+//    with 16 keys of row l % 32 per 32-key block (the other 16 sit in l ^ 32).
+//  * softmax on that layout: the mask (key < row limit) and exp2 per element,
+//    row maxima and sums joined across the two lane halves by one shuffle;
+//    online across sub-tiles, rescaling only when a row maximum grew.
+//  * O^T = V^T P^T: V is loaded coalesced and written transposed into LDS in
+//    the key order the S^T registers already have, so the B operand (P) is
+//    packed from registers as is; P is split into bf16 hi + lo parts (two
+//    MFMAs) so the product keeps about 16 bits of P (fp32 output error below
+//    1e-4), V being exact in bf16.
+//  * the four waves of a workgroup split each sub-tile's keys and are combined
+//    through LDS into the tile's partial state, written in the decode layout.
+//
+// Work distribution, lengths and buffer-resource loads as split_kv_partial
+// (persistent grid over attended tiles, keys past a limit read as zeros).
+#pragma once
+
+#include "partial_kernel.hpp"
+
+namespace decattn {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+#ifndef DECATTN_VERIFY_K_POLICY
+#define DECATTN_VERIFY_K_POLICY 2
+#endif
+
+constexpr int kVerifyWaves = 4;
+constexpr int kVerifyMaxRows = 32;
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    const bf16x2v_t v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Position in a wave's transposed V tile of the key at offset a (0 .. 32*KB-1)
+// of the wave's keys. The S^T accumulator gives lane half h, register r the key
+// 8*(r/4) + 4*h + r%4 of a 32-key block; the p.V product takes its B operand
+// from registers 8j..8j+7 as the 16-key step j, so the V^T column order must
+// list, per (block, step, half), keys {4h..4h+3, 8+4h..8+4h+3}.
+__device__ __forceinline__ int vt_position(int a) {
+    const int kb = a >> 5, rr = a & 31, j = rr >> 4, q = rr & 15;
+    const int hh = (q >> 2) & 1, e = (q & 3) + ((q >> 3) << 2);
+    return kb * 32 + j * 16 + hh * 8 + e;
+}
+
+// Byte offset of (dim, position) in a wave's V^T tile: rows of ROW bytes, the
+// 16-byte column chunk XOR-swizzled by (dim ^ dim/8) so that the transposed
+// 2-byte writes (16 lanes, dims 8 apart) and the 16-byte operand reads (8
+// consecutive dims) both spread over the LDS banks.
+template <int ROW>
+__device__ __forceinline__ int vt_offset(int dim, int pos) {
+    constexpr int CHUNKS = ROW / 16;
+    const int chunk = (pos >> 3) ^ ((dim ^ (dim >> 3)) & (CHUNKS - 1));
+    return dim * ROW + chunk * 16 + (pos & 7) * 2;
+}
+
+template <int D, int KB>
+__global__ void __launch_bounds__(256)
+verify_partial_mfma(const PartialParams p) {
+    constexpr int KS = D / 16;              // 16-dim steps of the score product
+    constexpr int DB = D / 32;              // 32-dim blocks of the output
+    constexpr int WK = 32 * KB;             // keys per wave per sub-tile
+    constexpr int SUB = kVerifyWaves * WK;  // keys per workgroup sub-tile
+    constexpr int LPK = D / 8;              // lanes per key row (coalesced V load)
+    constexpr int KPL = 64 / LPK;           // keys per V load
+    constexpr int VSTEP = WK / KPL;         // V loads per wave per sub-tile
+    constexpr int VT_ROW = WK * 2;          // bytes per dim row of a wave's V^T
+    static_assert(D == 64 || D == 128, "head dim 64 or 128");
+    static_assert(KB == 1 || KB == 2, "32 or 64 keys per wave");
+
+    extern __shared__ float smem[];
+    __shared__ int s_count[kVerifyWaves];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int n = lane & 31;                // row (B/D operand) or key (A operand) index
+    const int h = lane >> 5;                // lane half
+    char* vt = reinterpret_cast<char*>(smem) + (size_t)wave * D * VT_ROW;
+    float* c_acc = smem;                                         // [waves][RT][D]  (aliases V^T)
+    float* c_ml = smem + (size_t)kVerifyWaves * p.RT * D;        // [waves][RT][2]
+    int* s_len = reinterpret_cast<int*>(reinterpret_cast<char*>(smem) + p.lds_main);
+
+    // ---- lengths into LDS; count attended tiles (keys j < ctx + T)
+    int my_tiles = 0;
+    for (int i = tid; i < p.B; i += blockDim.x) {
+        const int len = p.lens[i];
+        s_len[i] = len;
+        my_tiles += (clamp_len(len + p.T, p.S_max) + p.chunk - 1) / p.chunk;
+    }
+    for (int o = 32; o > 0; o >>= 1) my_tiles += __shfl_xor(my_tiles, o);
+    if (lane == 0) s_count[wave] = my_tiles;
+    __syncthreads();
+    int n_tiles = 0;
+#pragma unroll
+    for (int w = 0; w < kVerifyWaves; ++w) n_tiles += s_count[w];
+    const int n_items = n_tiles * p.Hkv;
+    auto tiles_of = [&](int b) { return (clamp_len(s_len[b] + p.T, p.S_max) + p.chunk - 1) / p.chunk; };
+    int b_cur = 0, pre_cur = 0;
+
+    const float qs = p.qscale;
+    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+        // locate (b, kvh, tile); items are b-major, the walk only moves forward
+        while (item >= pre_cur + tiles_of(b_cur) * p.Hkv) {
+            pre_cur += tiles_of(b_cur) * p.Hkv;
+            ++b_cur;
+        }
+        const int b = b_cur;
+        const int na = tiles_of(b);
+        const int u = item - pre_cur;
+        const int c = u % na;
+        const int kvh = u / na;
+        const int len = s_len[b];
+        const int t0 = c * p.chunk;
+        const int t1 = min(t0 + p.chunk, p.S_max);
+        const int lim_all = min(clamp_len(len + p.T, p.S_max), t1);
+
+        // this lane's row (n) and its key limit; query slice for the B operand
+        const int i = n / p.G;
+        const bool row_ok = n < p.RT;
+        const int lim_n = row_ok ? min(clamp_len(len + i + 1, p.S_max), t1) : 0;
+        uint4 qv[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (row_ok) {
+                uint4 x = *reinterpret_cast<const uint4*>(
+                    p.q + ((size_t)(b * p.T + i) * p.Hq + kvh * p.G + (n - i * p.G)) * D + ks * 16 + h * 8);
+                x.x ^= p.qsign; x.y ^= p.qsign; x.z ^= p.qsign; x.w ^= p.qsign;
+                qv[ks] = x;
+            } else {
+                qv[ks] = make_uint4(0, 0, 0, 0);
+            }
+        }
+
+        const size_t head_base = (size_t)(b * p.Hkv + kvh) * p.S_max * D;
+        const uint32_t range = (uint32_t)lim_all * D * 2;
+        const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + head_base, range);
+        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + head_base, range);
+
+        float m_run = kNegInf, l_run = 0.f;
+        f32x16_t acc[DB];
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+
+        for (int sub = t0; sub < lim_all; sub += SUB) {
+            const int kbase = sub + wave * WK;
+            // V first (coalesced, 16 bytes per lane), then K in the A-operand layout
+            uint4 vr[VSTEP];
+#pragma unroll
+            for (int st = 0; st < VSTEP; ++st)
+                vr[st] = buffer_load16(vrs, (uint32_t)(kbase + st * KPL + lane / LPK) * (D * 2) + (lane % LPK) * 16);
+            uint4 kr[KB][KS];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    kr[kb][ks] = buffer_load16_policy<DECATTN_VERIFY_K_POLICY>(krs, (uint32_t)(kbase + kb * 32 + n) * (D * 2) + ks * 32 + h * 16);
+
+            // V^T into this wave's LDS tile, columns in S^T register order
+#pragma unroll
+            for (int st = 0; st < VSTEP; ++st) {
+                const int vp = vt_position(st * KPL + lane / LPK);
+                const int d0 = (lane % LPK) * 8;
+                const uint32_t w[4] = {vr[st].x, vr[st].y, vr[st].z, vr[st].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    *reinterpret_cast<uint16_t*>(vt + vt_offset<VT_ROW>(d0 + 2 * e, vp)) = (uint16_t)(w[e] & 0xFFFFu);
+                    *reinterpret_cast<uint16_t*>(vt + vt_offset<VT_ROW>(d0 + 2 * e + 1, vp)) = (uint16_t)(w[e] >> 16);
+                }
+            }
+
+            // scores S^T = K Q^T, scaled to log2 units and masked per row
+            float s[KB][16];
+            float mx = kNegInf;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                f32x16_t st16;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) st16[r] = 0.f;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    st16 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kr[kb][ks]), as_bf16x8(qv[ks]), st16, 0, 0, 0);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kbase + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                    s[kb][r] = key < lim_n ? st16[r] * qs : kNegInf;
+                    mx = fmaxf(mx, s[kb][r]);
+                }
+            }
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float m_new = fmaxf(m_run, mx);
+            const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+            if (__any(m_run != kNegInf && m_new > m_run)) {
+                const float alpha = fast_exp2(m_run - m_use);
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+            }
+            m_run = m_new;
+
+            // P = 2^(s - m), split into bf16 hi + lo, packed as B operands
+            uint4 bhi[KB][2], blo[KB][2];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                float pv[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    pv[r] = fast_exp2(s[kb][r] - m_use);
+                    l_run += pv[r];
+                }
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    uint32_t hw[4], lw[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float a0 = pv[8 * j + 2 * e], a1 = pv[8 * j + 2 * e + 1];
+                        hw[e] = pack_bf16x2(a0, a1);
+                        lw[e] = pack_bf16x2(a0 - __uint_as_float(hw[e] << 16),
+                                            a1 - __uint_as_float(hw[e] & 0xFFFF0000u));
+                    }
+                    bhi[kb][j] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+                    blo[kb][j] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+                }
+            }
+
+            // O^T += V^T P^T (reads of this wave's own LDS tile, after its writes)
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const uint4 a = *reinterpret_cast<const uint4*>(
+                            vt + vt_offset<VT_ROW>(db * 32 + n, kb * 32 + j * 16 + h * 8));
+                        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(bhi[kb][j]), acc[db], 0, 0, 0);
+                        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(blo[kb][j]), acc[db], 0, 0, 0);
+                    }
+                }
+            }
+            __builtin_amdgcn_wave_barrier();     // the next sub-tile rewrites the V^T tile
+        }
+
+        // ---- combine the waves (LDS aliases the V^T tiles: wait for all reads)
+        l_run += __shfl_xor(l_run, 32);
+        __syncthreads();
+        if (row_ok) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int dim = db * 32 + 8 * g4 + 4 * h;
+                    *reinterpret_cast<float4*>(c_acc + ((size_t)wave * p.RT + n) * D + dim) =
+                        make_float4(acc[db][4 * g4], acc[db][4 * g4 + 1], acc[db][4 * g4 + 2], acc[db][4 * g4 + 3]);
+                }
+            if (h == 0) {
+                c_ml[(wave * p.RT + n) * 2 + 0] = m_run;
+                c_ml[(wave * p.RT + n) * 2 + 1] = l_run;
+            }
+        }
+        __syncthreads();
+        const size_t tile_row0 = ((size_t)(b * p.Hkv + kvh) * p.NC + c) * p.RT;
+        for (int idx = tid; idx < p.RT * D; idx += blockDim.x) {
+            const int r = idx / D;
+            const int d = idx - r * D;
+            float M = kNegInf;
+#pragma unroll
+            for (int w = 0; w < kVerifyWaves; ++w) M = fmaxf(M, c_ml[(w * p.RT + r) * 2]);
+            float A = 0.f, L = 0.f;
+            if (M != kNegInf) {
+#pragma unroll
+                for (int w = 0; w < kVerifyWaves; ++w) {
+                    const float wt = fast_exp2(c_ml[(w * p.RT + r) * 2] - M);
+                    A = __builtin_fmaf(wt, c_acc[((size_t)w * p.RT + r) * D + d], A);
+                    L = __builtin_fmaf(wt, c_ml[(w * p.RT + r) * 2 + 1], L);
+                }
+            }
+            p.ws_acc[(tile_row0 + r) * D + d] = A;
+            if (d == 0) {
+                p.ws_ml[(tile_row0 + r) * 2 + 0] = M;
+                p.ws_ml[(tile_row0 + r) * 2 + 1] = L;
+            }
+        }
+        __syncthreads();                    // LDS is rewritten by the next item
+    }
+}
+
+}  // namespace decattn

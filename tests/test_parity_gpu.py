@@ -76,13 +76,43 @@ def test_workload5_verify_chunk_vs_oracle_and_sequential_decodes():
     assert_f32_close(out32, ref)
     out16 = run_chunk(c, tensors=tensors, out_dtype=torch.bfloat16)
     assert_bf16_close(out16, ref)
-    # six sequential decode calls: token i with seq_len = ctx + i + 1, same chunk
-    chunk = sda.default_chunk(1, 6, 24, 8, 128, 16384)
+    # six sequential decode calls: token i with seq_len = ctx + i + 1. The
+    # verify chunk runs on the matrix cores, the decode calls on the vector
+    # path: equal to the fp32 tolerance (each within it of the oracle)
     T = c["q"].shape[1]
     for i in range(T):
         ci = dict(c, q=np.ascontiguousarray(c["q"][:, i]), lens=c["lens"] + i + 1)
-        dec = run_decode(ci, chunk=chunk, tensors=(dev_bits(ci["q"]), tensors[1], tensors[2]))
-        assert torch.equal(dec, out32[:, i]), f"token {i}: chunk row differs from its decode call"
+        dec = run_decode(ci, tensors=(dev_bits(ci["q"]), tensors[1], tensors[2]))
+        d = (dec - out32[:, i]).abs().max().item()
+        assert d <= 1e-4, f"token {i}: chunk row and its decode call differ by {d}"
+
+
+@pytest.mark.parametrize("T,G,chunk", [(6, 3, 64), (16, 3, 256), (4, 8, 32)])
+def test_vector_chunk_path_bit_identical_to_sequential_decodes(T, G, chunk):
+    # chunks below 128 keys, or more than 32 rows per kv head, take the vector
+    # path, whose rows run exactly the decode operation sequence
+    Hkv = 2
+    c = workloads.make_case(1, G * Hkv, Hkv, 128, 1024, [700], T=T, seed=T * 10 + G)
+    out = run_chunk(c, chunk=chunk)
+    ref = oracle.chunk_attention(c["q"], c["k"], c["v"], c["lens"], c["scale"])
+    assert_f32_close(out, ref)
+    kt, vt = dev_bits(c["k"]), dev_bits(c["v"])
+    for i in range(T):
+        ci = dict(c, q=np.ascontiguousarray(c["q"][:, i]), lens=c["lens"] + i + 1)
+        dec = run_decode(ci, chunk=chunk, tensors=(dev_bits(ci["q"]), kt, vt))
+        assert torch.equal(dec, out[:, i]), f"token {i}: chunk row differs from its decode call"
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("T,G,chunk", [(6, 3, 256), (2, 8, 128), (5, 6, 512), (1, 4, 256), (16, 2, 1024)])
+def test_matrix_core_chunk_path_vs_oracle(D, T, G, chunk):
+    Hkv = 3
+    c = workloads.make_case(2, G * Hkv, Hkv, D, 1500, [1200, 90], T=T, seed=D + T * 7 + G + chunk)
+    if T == 1:
+        c["q"] = c["q"].reshape(2, 1, G * Hkv, D)
+    ref = oracle.chunk_attention(c["q"], c["k"], c["v"], c["lens"], c["scale"])
+    assert_f32_close(run_chunk(c, chunk=chunk), ref)
+    assert_bf16_close(run_chunk(c, chunk=chunk, out_dtype=torch.bfloat16), ref)
 
 
 # ----------------------------------------------------------- shapes and chunking
@@ -162,6 +192,18 @@ def test_chunk_nan_poison_past_context_plus_t():
         poisoned["v"][b, :, ctx + 5:] = BF16_NAN
     a = run_chunk(c, chunk=64)
     p = run_chunk(poisoned, chunk=64)
+    assert torch.equal(a, p) and not torch.isnan(p).any()
+
+
+@pytest.mark.parametrize("chunk", [128, 256])
+def test_matrix_core_chunk_nan_poison_past_context_plus_t(chunk):
+    c = workloads.make_case(2, 24, 8, 128, 700, [300, 517], T=6, seed=18 + chunk)
+    poisoned = dict(c, k=c["k"].copy(), v=c["v"].copy())
+    for b, ctx in enumerate(c["lens"]):
+        poisoned["k"][b, :, ctx + 6:] = BF16_NAN
+        poisoned["v"][b, :, ctx + 6:] = BF16_NAN
+    a = run_chunk(c, chunk=chunk)
+    p = run_chunk(poisoned, chunk=chunk)
     assert torch.equal(a, p) and not torch.isnan(p).any()
 
 
