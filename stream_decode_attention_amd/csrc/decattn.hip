@@ -197,12 +197,12 @@ int run_partial(const Plan& pl, const void* q, const void* k, const void* v, con
     pp.nwk = pl.nwk; pp.rg_per_block = pl.rg_per_block; pp.n_row_blocks = pl.n_row_blocks;
     pp.B = pl.B;
     pp.lds_main = (int)pl.mfma_lds_main;
-    // scores are taken in log2 units (softmax on exp2): the kernel multiplies
-    // q.k by |scale|*log2(e) and negates q when scale < 0; a zero scale
-    // becomes the smallest normal float, whose scores all round to 2^0
+    // scores are taken in log2 units (softmax on exp2): the kernels multiply
+    // q.k by scale*log2(e), rounded once to fp32; a zero scale becomes the
+    // smallest normal float, whose scores all round to 2^0
     const double qs = std::fabs((double)scale) * 1.4426950408889634;
-    pp.qscale = qs < (double)FLT_MIN ? FLT_MIN : (float)qs;
-    pp.qsign = scale < 0.f ? 0x80008000u : 0u;
+    const float qmag = qs < (double)FLT_MIN ? FLT_MIN : (float)qs;
+    pp.qscale = scale < 0.f ? -qmag : qmag;
     const hipError_t e = pl.D == 64 ? launch_partial_d<64>(pl, pp, s) : launch_partial_d<128>(pl, pp, s);
     return e == hipSuccess ? DECATTN_OK : DECATTN_ERR_HIP;
 }

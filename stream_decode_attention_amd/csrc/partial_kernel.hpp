@@ -72,8 +72,7 @@ struct PartialParams {
     int nwk;                // key waves per workgroup
     int rg_per_block;       // row groups per workgroup
     int n_row_blocks;       // workgroups per tile along the row axis
-    float qscale;           // |scale| * log2(e), at least FLT_MIN
-    uint32_t qsign;         // 0x80008000 negates both bf16 of a q word (scale < 0), else 0
+    float qscale;           // scale * log2(e); magnitude at least FLT_MIN, sign of scale
     int B;                  // batch rows (lengths staged in LDS)
     int lds_main;           // bytes of dynamic LDS before the staged lengths (verify kernel)
 };
@@ -228,25 +227,24 @@ split_kv_partial(const PartialParams p) {
         return tl;
     };
 
-    // this wave's query rows of a tile (raw bf16 pairs) and its own row's key limit
+    // this wave's query rows of a tile (raw bf16 pairs) and its own row's key
+    // limit. Every slot loads a valid row, with no branch: slots past the
+    // wave's rows take row 0 of the item; their scores land only in lanes whose
+    // own row is one of them, which have a key limit of 0. Nothing here waits
+    // for the loads, so entering the next item does not drain the K/V loads in
+    // flight (vector memory completes in order).
     auto load_q = [&](const Tile& tl, uint4 (&qraw)[RP], int& my_lim) {
         const int rg = tl.rblk * p.rg_per_block + rgl;
         my_lim = 0;
 #pragma unroll
         for (int j = 0; j < RP; ++j) {
-            const int r = rg * R + j;
-            if (j < R && r < p.RT) {
-                const int i = r / p.G;
-                const int h = tl.kvh * p.G + (r - i * p.G);
-                const int n = min(clamp_len(p.causal ? tl.len + i + 1 : tl.len, p.S_max), tl.t1);
-                if (j == own) my_lim = n;
-                uint4 qv = *reinterpret_cast<const uint4*>(
-                    p.q + ((size_t)(tl.b * p.T + i) * p.Hq + h) * D + db * 8);
-                qv.x ^= p.qsign; qv.y ^= p.qsign; qv.z ^= p.qsign; qv.w ^= p.qsign;
-                qraw[j] = qv;
-            } else {
-                qraw[j] = make_uint4(0, 0, 0, 0);
-            }
+            const int r0 = rg * R + j;
+            const bool ok = j < R && r0 < p.RT;
+            const int r = ok ? r0 : 0;
+            const int i = r / p.G;
+            const int h = tl.kvh * p.G + (r - i * p.G);
+            if (j == own && ok) my_lim = min(clamp_len(p.causal ? tl.len + i + 1 : tl.len, p.S_max), tl.t1);
+            qraw[j] = *reinterpret_cast<const uint4*>(p.q + ((size_t)(tl.b * p.T + i) * p.Hq + h) * D + db * 8);
         }
     };
 

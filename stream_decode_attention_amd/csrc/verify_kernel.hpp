@@ -134,22 +134,17 @@ verify_partial_mfma(const PartialParams p) {
         const int t1 = min(t0 + p.chunk, p.S_max);
         const int lim_all = min(clamp_len(len + p.T, p.S_max), t1);
 
-        // this lane's row (n) and its key limit; query slice for the B operand
-        const int i = n / p.G;
+        // this lane's row (n) and its key limit; query slice for the B operand.
+        // Lanes past the last row load row 0 (all loads issue back to back with
+        // no branch) and are masked by a key limit of 0.
         const bool row_ok = n < p.RT;
+        const int nr = row_ok ? n : 0;
+        const int i = nr / p.G;
         const int lim_n = row_ok ? min(clamp_len(len + i + 1, p.S_max), t1) : 0;
+        const uint16_t* qrow = p.q + ((size_t)(b * p.T + i) * p.Hq + kvh * p.G + (nr - i * p.G)) * D + h * 8;
         uint4 qv[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            if (row_ok) {
-                uint4 x = *reinterpret_cast<const uint4*>(
-                    p.q + ((size_t)(b * p.T + i) * p.Hq + kvh * p.G + (n - i * p.G)) * D + ks * 16 + h * 8);
-                x.x ^= p.qsign; x.y ^= p.qsign; x.z ^= p.qsign; x.w ^= p.qsign;
-                qv[ks] = x;
-            } else {
-                qv[ks] = make_uint4(0, 0, 0, 0);
-            }
-        }
+        for (int ks = 0; ks < KS; ++ks) qv[ks] = *reinterpret_cast<const uint4*>(qrow + ks * 16);
 
         const size_t head_base = (size_t)(b * p.Hkv + kvh) * p.S_max * D;
         const uint32_t range = (uint32_t)lim_all * D * 2;

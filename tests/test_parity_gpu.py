@@ -261,6 +261,27 @@ def test_chunk_shapes_vs_oracle(T, ctx):
     assert_f32_close(run_chunk(c), ref)
 
 
+@pytest.mark.parametrize("path", ["decode", "chunk_vector", "chunk_matrix_core"])
+@pytest.mark.parametrize("scale_kind", ["negative", "zero", "large"])
+def test_scale_sign_and_magnitude(path, scale_kind):
+    D = 128 if path == "chunk_matrix_core" else 64
+    if path == "decode":
+        c = workloads.make_case(2, 12, 4, D, 700, [700, 65], seed=91)
+        chunk = 64
+    else:
+        T, G = (6, 3) if path == "chunk_matrix_core" else (16, 3)     # 18 or 48 rows per kv head
+        c = workloads.make_case(2, 3 * G, 3, D, 900, [600, 5], T=T, seed=92 + T)
+        chunk = 256 if path == "chunk_matrix_core" else 64
+    c["scale"] = {"negative": -1.0 / np.sqrt(D), "zero": 0.0, "large": 0.9}[scale_kind]
+    if path == "decode":
+        ref = oracle.decode_attention(c["q"], c["k"], c["v"], c["lens"], c["scale"])
+        out = run_decode(c, chunk=chunk)
+    else:
+        ref = oracle.chunk_attention(c["q"], c["k"], c["v"], c["lens"], c["scale"])
+        out = run_chunk(c, chunk=chunk)
+    assert_f32_close(out, ref)
+
+
 def test_chunk_context_reaching_s_max_clamps():
     c = workloads.make_case(2, 8, 4, 64, 128, [125, 128], T=6, seed=14)
     ref = oracle.chunk_attention(c["q"], c["k"], c["v"], c["lens"], c["scale"])
