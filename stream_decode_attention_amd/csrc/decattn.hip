@@ -28,6 +28,10 @@ constexpr int kMaxT = 16;
 constexpr int kMaxB = 4096;                // lengths are staged in LDS
 constexpr int kMaxRowsPerWave = 8;
 constexpr int kMaxWavesPerBlock = 8;       // matches __launch_bounds__(512)
+#ifndef DECATTN_MAX_KEY_WAVES
+#define DECATTN_MAX_KEY_WAVES 4
+#endif
+constexpr int kMaxKeyWaves = DECATTN_MAX_KEY_WAVES;   // waves splitting one tile's keys
 constexpr size_t kMaxLdsBytes = 64 * 1024;
 constexpr int kMinChunk = 16;
 constexpr int kMaxChunk = 1 << 20;
@@ -47,8 +51,10 @@ struct Plan {
 };
 
 int pick_default_chunk(int B, int T, int G, int Hkv, int S_max) {
-    // verify chunks that fit the matrix-core kernel: 256-key tiles
-    if (T > 1 && T * G <= kVerifyMaxRows) return 256;
+    // verify chunks that fit the matrix-core kernel: 256-key tiles, or 128 when
+    // that still leaves fewer than 1024 tiles (more workgroups in flight)
+    if (T > 1 && T * G <= kVerifyMaxRows)
+        return (long long)B * Hkv * ((S_max + 255) / 256) < 1024 ? 128 : 256;
     // Enough tiles to occupy the 256 compute units several times over while
     // S_max is the only length the host knows; larger tiles cut partial-state
     // traffic (about G*(D+2)*4 bytes per tile against 4*D bytes per key).
@@ -77,7 +83,7 @@ int make_plan(int B, int T, int Hq, int Hkv, int D, int S_max, int chunk, Plan* 
     p.NR = (p.RT + kMaxRowsPerWave - 1) / kMaxRowsPerWave;
     p.R = (p.RT + p.NR - 1) / p.NR;
     int nwk = chunk / kKeysPerWave;
-    p.nwk = nwk < 1 ? 1 : (nwk > 4 ? 4 : nwk);
+    p.nwk = nwk < 1 ? 1 : (nwk > kMaxKeyWaves ? kMaxKeyWaves : nwk);
     const size_t lds_per_rg = (size_t)p.nwk * p.R * (D + 2) * sizeof(float);
     const size_t lds_lens = (size_t)B * sizeof(int);
     int rgb = kMaxWavesPerBlock / p.nwk;
@@ -96,7 +102,7 @@ int make_plan(int B, int T, int Hq, int Hkv, int D, int S_max, int chunk, Plan* 
     p.mfma_kb = chunk % 256 == 0 ? 2 : 1;
     {
         const size_t vt = (size_t)kVerifyWaves * D * (32 * p.mfma_kb) * 2;
-        const size_t comb = (size_t)kVerifyWaves * p.RT * D * 4 + (size_t)kVerifyWaves * p.RT * 2 * 4;
+        const size_t comb = (size_t)verify_comb_floats(p.RT, D) * sizeof(float);
         p.mfma_lds_main = (vt > comb ? vt : comb);
         p.mfma_lds_bytes = p.mfma_lds_main + lds_lens;
     }

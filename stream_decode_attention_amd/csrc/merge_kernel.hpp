@@ -110,13 +110,17 @@ lse_merge(const MergeParams p) {
         float mb = mv[0];
 #pragma unroll
         for (int u = 1; u < kMergeUnroll; ++u) mb = fmaxf(mb, mv[u]);
-        const float m_new = fmaxf(m_t, mb);           // finite: tile c0 < na is valid
-        const float sc = fast_exp2(m_t - m_new);
+        // An empty tile state (m = -inf, l = 0, acc = 0) adds nothing: while this
+        // lane has seen only such tiles its maximum stays -inf and the weights
+        // are taken against 0, which makes them all 0 (never 2^(-inf + inf)).
+        const float m_new = fmaxf(m_t, mb);
+        const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+        const float sc = fast_exp2(m_t - m_use);
         l_t *= sc;
         a_t.x *= sc; a_t.y *= sc; a_t.z *= sc; a_t.w *= sc;
 #pragma unroll
         for (int u = 0; u < kMergeUnroll; ++u) {
-            const float wt = fast_exp2(mv[u] - m_new);
+            const float wt = fast_exp2(mv[u] - m_use);
             l_t = __builtin_fmaf(wt, lv[u], l_t);
             a_t.x = __builtin_fmaf(wt, av[u].x, a_t.x);
             a_t.y = __builtin_fmaf(wt, av[u].y, a_t.y);

@@ -36,12 +36,23 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
+// K is read in the MFMA operand layout: each load instruction touches 32 bytes
+// of 32 key rows, and four instructions share every cache line, so K keeps
+// the default cache policy (the line stays in L1 for the other three); V is
+// read in whole rows, streamed (non-temporal).
 #ifndef DECATTN_VERIFY_K_POLICY
-#define DECATTN_VERIFY_K_POLICY 2
+#define DECATTN_VERIFY_K_POLICY 0
 #endif
 
 constexpr int kVerifyWaves = 4;
 constexpr int kVerifyMaxRows = 32;
+
+// LDS of the cross-wave combine, in floats: per wave RT rows of D + 4 floats
+// (the pad staggers the rows over the banks), then (m, l) per wave and row,
+// then one weight per wave and row.
+__host__ __device__ constexpr int verify_comb_floats(int RT, int D) {
+    return kVerifyWaves * RT * (D + 4) + kVerifyWaves * RT * 2 + RT * kVerifyWaves;
+}
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
@@ -96,16 +107,21 @@ verify_partial_mfma(const PartialParams p) {
     const int n = lane & 31;                // row (B/D operand) or key (A operand) index
     const int h = lane >> 5;                // lane half
     char* vt = reinterpret_cast<char*>(smem) + (size_t)wave * D * VT_ROW;
-    float* c_acc = smem;                                         // [waves][RT][D]  (aliases V^T)
-    float* c_ml = smem + (size_t)kVerifyWaves * p.RT * D;        // [waves][RT][2]
+    constexpr int CST = D + 4;                                   // combine row stride (floats)
+    float* c_acc = smem;                                         // [waves][RT][CST]  (aliases V^T)
+    float* c_ml = smem + (size_t)kVerifyWaves * p.RT * CST;      // [waves][RT][2]
+    float* c_wt = c_ml + kVerifyWaves * p.RT * 2;                // [RT][waves]
     int* s_len = reinterpret_cast<int*>(reinterpret_cast<char*>(smem) + p.lds_main);
 
-    // ---- lengths into LDS; count attended tiles (keys j < ctx + T)
+    // one work item per attended tile (keys j < ctx + T) of every (b, kvh)
+    auto items_for = [&](int len) { return (clamp_len(len + p.T, p.S_max) + p.chunk - 1) / p.chunk; };
+
+    // ---- lengths into LDS; count attended tiles
     int my_tiles = 0;
     for (int i = tid; i < p.B; i += blockDim.x) {
         const int len = p.lens[i];
         s_len[i] = len;
-        my_tiles += (clamp_len(len + p.T, p.S_max) + p.chunk - 1) / p.chunk;
+        my_tiles += items_for(len);
     }
     for (int o = 32; o > 0; o >>= 1) my_tiles += __shfl_xor(my_tiles, o);
     if (lane == 0) s_count[wave] = my_tiles;
@@ -114,7 +130,7 @@ verify_partial_mfma(const PartialParams p) {
 #pragma unroll
     for (int w = 0; w < kVerifyWaves; ++w) n_tiles += s_count[w];
     const int n_items = n_tiles * p.Hkv;
-    auto tiles_of = [&](int b) { return (clamp_len(s_len[b] + p.T, p.S_max) + p.chunk - 1) / p.chunk; };
+    auto tiles_of = [&](int b) { return items_for(s_len[b]); };
     int b_cur = 0, pre_cur = 0;
 
     const float qs = p.qscale;
@@ -141,6 +157,7 @@ verify_partial_mfma(const PartialParams p) {
         const int nr = row_ok ? n : 0;
         const int i = nr / p.G;
         const int lim_n = row_ok ? min(clamp_len(len + i + 1, p.S_max), t1) : 0;
+        const int lim_min = min(clamp_len(len + 1, p.S_max), t1);   // row i = 0 attends the fewest keys
         const uint16_t* qrow = p.q + ((size_t)(b * p.T + i) * p.Hq + kvh * p.G + (nr - i * p.G)) * D + h * 8;
         uint4 qv[KS];
 #pragma unroll
@@ -196,11 +213,19 @@ verify_partial_mfma(const PartialParams p) {
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
                     st16 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kr[kb][ks]), as_bf16x8(qv[ks]), st16, 0, 0, 0);
+                if (kbase + WK <= lim_min) {        // wave-uniform: every row attends every key here
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = kbase + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                    s[kb][r] = key < lim_n ? st16[r] * qs : kNegInf;
-                    mx = fmaxf(mx, s[kb][r]);
+                    for (int r = 0; r < 16; ++r) {
+                        s[kb][r] = st16[r] * qs;
+                        mx = fmaxf(mx, s[kb][r]);
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = kbase + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                        s[kb][r] = key < lim_n ? st16[r] * qs : kNegInf;
+                        mx = fmaxf(mx, s[kb][r]);
+                    }
                 }
             }
             mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -268,7 +293,7 @@ verify_partial_mfma(const PartialParams p) {
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
                     const int dim = db * 32 + 8 * g4 + 4 * h;
-                    *reinterpret_cast<float4*>(c_acc + ((size_t)wave * p.RT + n) * D + dim) =
+                    *reinterpret_cast<float4*>(c_acc + ((size_t)wave * p.RT + n) * CST + dim) =
                         make_float4(acc[db][4 * g4], acc[db][4 * g4 + 1], acc[db][4 * g4 + 2], acc[db][4 * g4 + 3]);
                 }
             if (h == 0) {
@@ -278,26 +303,36 @@ verify_partial_mfma(const PartialParams p) {
         }
         __syncthreads();
         const size_t tile_row0 = ((size_t)(b * p.Hkv + kvh) * p.NC + c) * p.RT;
-        for (int idx = tid; idx < p.RT * D; idx += blockDim.x) {
-            const int r = idx / D;
-            const int d = idx - r * D;
+        // per row: the waves' common maximum, their weights and the summed l
+        if (tid < p.RT) {
             float M = kNegInf;
 #pragma unroll
-            for (int w = 0; w < kVerifyWaves; ++w) M = fmaxf(M, c_ml[(w * p.RT + r) * 2]);
-            float A = 0.f, L = 0.f;
-            if (M != kNegInf) {
+            for (int w = 0; w < kVerifyWaves; ++w) M = fmaxf(M, c_ml[(w * p.RT + tid) * 2]);
+            float L = 0.f;
 #pragma unroll
-                for (int w = 0; w < kVerifyWaves; ++w) {
-                    const float wt = fast_exp2(c_ml[(w * p.RT + r) * 2] - M);
-                    A = __builtin_fmaf(wt, c_acc[((size_t)w * p.RT + r) * D + d], A);
-                    L = __builtin_fmaf(wt, c_ml[(w * p.RT + r) * 2 + 1], L);
-                }
+            for (int w = 0; w < kVerifyWaves; ++w) {
+                const float wt = M == kNegInf ? 0.f : fast_exp2(c_ml[(w * p.RT + tid) * 2] - M);
+                c_wt[tid * kVerifyWaves + w] = wt;
+                L = __builtin_fmaf(wt, c_ml[(w * p.RT + tid) * 2 + 1], L);
             }
-            p.ws_acc[(tile_row0 + r) * D + d] = A;
-            if (d == 0) {
-                p.ws_ml[(tile_row0 + r) * 2 + 0] = M;
-                p.ws_ml[(tile_row0 + r) * 2 + 1] = L;
+            p.ws_ml[(tile_row0 + tid) * 2 + 0] = M;
+            p.ws_ml[(tile_row0 + tid) * 2 + 1] = L;
+        }
+        __syncthreads();
+        for (int idx = tid; idx < p.RT * (D / 4); idx += blockDim.x) {
+            const int r = idx / (D / 4);
+            const int d = (idx - r * (D / 4)) * 4;
+            float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int w = 0; w < kVerifyWaves; ++w) {
+                const float wt = c_wt[r * kVerifyWaves + w];
+                const float4 a = *reinterpret_cast<const float4*>(c_acc + ((size_t)w * p.RT + r) * CST + d);
+                A.x = __builtin_fmaf(wt, a.x, A.x);
+                A.y = __builtin_fmaf(wt, a.y, A.y);
+                A.z = __builtin_fmaf(wt, a.z, A.z);
+                A.w = __builtin_fmaf(wt, a.w, A.w);
             }
+            *reinterpret_cast<float4*>(p.ws_acc + (tile_row0 + r) * D + d) = A;
         }
         __syncthreads();                    // LDS is rewritten by the next item
     }

@@ -115,6 +115,18 @@ def test_matrix_core_chunk_path_vs_oracle(D, T, G, chunk):
     assert_bf16_close(run_chunk(c, chunk=chunk, out_dtype=torch.bfloat16), ref)
 
 
+@pytest.mark.parametrize("chunk", [128, 256])
+def test_matrix_core_context_just_past_a_tile_boundary(chunk):
+    """Sequence 0's keys end 4 into a new tile, so its first two query rows read
+    one tile fewer than the other four; sequence 1 ends 46 keys into its last
+    tile. The workspace starts as NaN everywhere."""
+    c = workloads.make_case(2, 9, 3, 128, 4 * chunk + 64, [3 * chunk - 2, 2 * chunk + 40], T=6,
+                            seed=77 + chunk)
+    ref = oracle.chunk_attention(c["q"], c["k"], c["v"], c["lens"], c["scale"])
+    assert_f32_close(run_chunk(c, chunk=chunk), ref)
+    assert_bf16_close(run_chunk(c, chunk=chunk, out_dtype=torch.bfloat16), ref)
+
+
 # ----------------------------------------------------------- shapes and chunking
 
 @pytest.mark.parametrize("D", [64, 128])
