@@ -57,9 +57,11 @@ int pick_default_chunk(int B, int T, int G, int Hkv, int S_max) {
         return (long long)B * Hkv * ((S_max + 255) / 256) < 1024 ? 128 : 256;
     // Enough tiles to occupy the 256 compute units several times over while
     // S_max is the only length the host knows; larger tiles cut partial-state
-    // traffic (about G*(D+2)*4 bytes per tile against 4*D bytes per key).
+    // traffic (about G*(D+2)*4 bytes per tile against 4*D bytes per key) and
+    // per-tile work. Below 128 keys the per-tile cost outweighs the extra
+    // parallelism even for single-sequence calls of a few MB (measured).
     int c = 512;
-    while (c > 32 && (long long)B * Hkv * ((S_max + c - 1) / c) < 2048) c >>= 1;
+    while (c > 128 && (long long)B * Hkv * ((S_max + c - 1) / c) < 2048) c >>= 1;
     return c;
 }
 
