@@ -51,10 +51,10 @@ struct Plan {
 };
 
 int pick_default_chunk(int B, int T, int G, int Hkv, int S_max) {
-    // verify chunks that fit the matrix-core kernel: 256-key tiles, or 128 when
-    // that still leaves fewer than 1024 tiles (more workgroups in flight)
-    if (T > 1 && T * G <= kVerifyMaxRows)
-        return (long long)B * Hkv * ((S_max + 255) / 256) < 1024 ? 128 : 256;
+    // verify chunks that fit the matrix-core kernel: 512-key tiles (measured
+    // fastest per call at the Llama-3.2-3B verify shape: one round of
+    // workgroups, and the fewest tiles for the merge)
+    if (T > 1 && T * G <= kVerifyMaxRows) return 512;
     // Enough tiles to occupy the 256 compute units several times over while
     // S_max is the only length the host knows; larger tiles cut partial-state
     // traffic (about G*(D+2)*4 bytes per tile against 4*D bytes per key) and
@@ -103,7 +103,7 @@ int make_plan(int B, int T, int Hq, int Hkv, int D, int S_max, int chunk, Plan* 
     p.mfma = T > 1 && p.RT <= kVerifyMaxRows && chunk % 128 == 0;
     p.mfma_kb = chunk % 256 == 0 ? 2 : 1;
     {
-        const size_t vt = (size_t)kVerifyWaves * D * (32 * p.mfma_kb) * 2;
+        const size_t vt = (size_t)kVerifyWaves * (32 * p.mfma_kb) * verify_vrow(D);
         const size_t comb = (size_t)verify_comb_floats(p.RT, D) * sizeof(float);
         p.mfma_lds_main = (vt > comb ? vt : comb);
         p.mfma_lds_bytes = p.mfma_lds_main + lds_lens;

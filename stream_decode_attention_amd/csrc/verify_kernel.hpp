@@ -16,11 +16,13 @@
 //  * softmax on that layout: the mask (key < row limit) and exp2 per element,
 //    row maxima and sums joined across the two lane halves by one shuffle;
 //    online across sub-tiles, rescaling only when a row maximum grew.
-//  * O^T = V^T P^T: V is loaded coalesced and written transposed into LDS in
-//    the key order the S^T registers already have, so the B operand (P) is
-//    packed from registers as is; P is split into bf16 hi + lo parts (two
-//    MFMAs) so the product keeps about 16 bits of P (fp32 output error below
-//    1e-4), V being exact in bf16.
+//  * O^T = V^T P^T: V is loaded coalesced and stored row-major in LDS with
+//    16-byte writes; the A operand (V^T) is read back with the gfx950
+//    transposing LDS load (ds_read_b64_tr_b16), which hands each lane four
+//    consecutive keys at one dim, in the key order the S^T registers give P,
+//    so the B operand (P) is packed from registers as is. P is split into
+//    bf16 hi + lo parts (two MFMAs) so the product keeps about 16 bits of P
+//    (fp32 output error below 1e-4), V being exact in bf16.
 //  * the four waves of a workgroup split each sub-tile's keys and are combined
 //    through LDS into the tile's partial state, written in the decode layout.
 //
@@ -62,26 +64,21 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
-// Position in a wave's transposed V tile of the key at offset a (0 .. 32*KB-1)
-// of the wave's keys. The S^T accumulator gives lane half h, register r the key
-// 8*(r/4) + 4*h + r%4 of a 32-key block; the p.V product takes its B operand
-// from registers 8j..8j+7 as the 16-key step j, so the V^T column order must
-// list, per (block, step, half), keys {4h..4h+3, 8+4h..8+4h+3}.
-__device__ __forceinline__ int vt_position(int a) {
-    const int kb = a >> 5, rr = a & 31, j = rr >> 4, q = rr & 15;
-    const int hh = (q >> 2) & 1, e = (q & 3) + ((q >> 3) << 2);
-    return kb * 32 + j * 16 + hh * 8 + e;
-}
+// Bytes per key row of a wave's V tile in LDS: D bf16 plus 64 bytes, so that
+// the eight rows one transposing load touches fall on distinct bank groups.
+__host__ __device__ constexpr int verify_vrow(int D) { return D * 2 + 64; }
 
-// Byte offset of (dim, position) in a wave's V^T tile: rows of ROW bytes, the
-// 16-byte column chunk XOR-swizzled by (dim ^ dim/8) so that the transposed
-// 2-byte writes (16 lanes, dims 8 apart) and the 16-byte operand reads (8
-// consecutive dims) both spread over the LDS banks.
-template <int ROW>
-__device__ __forceinline__ int vt_offset(int dim, int pos) {
-    constexpr int CHUNKS = ROW / 16;
-    const int chunk = (pos >> 3) ^ ((dim ^ (dim >> 3)) & (CHUNKS - 1));
-    return dim * ROW + chunk * 16 + (pos & 7) * 2;
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16 at LDS address p (8-byte aligned). Within each group of 16
+// lanes, lane i receives element i%4 of the 8 bytes addressed by lanes
+// 4r + i/4, r = 0..3 (checked on gfx950 against four address patterns).
+// With lanes 4r..4r+3 pointing at key K+r, dims d0+4q..+3 (q = lane%4), lane i
+// gets keys K..K+3 at dim d0+i.
+__device__ __forceinline__ uint2 lds_read_tr16_b64(const char* p) {
+    const v4i16_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16_t*)(__attribute__((address_space(3))) char*)p);
+    return __builtin_bit_cast(uint2, r);
 }
 
 template <int D, int KB>
@@ -94,7 +91,7 @@ verify_partial_mfma(const PartialParams p) {
     constexpr int LPK = D / 8;              // lanes per key row (coalesced V load)
     constexpr int KPL = 64 / LPK;           // keys per V load
     constexpr int VSTEP = WK / KPL;         // V loads per wave per sub-tile
-    constexpr int VT_ROW = WK * 2;          // bytes per dim row of a wave's V^T
+    constexpr int VROW = verify_vrow(D);    // bytes per key row of a wave's V tile
     static_assert(D == 64 || D == 128, "head dim 64 or 128");
     static_assert(KB == 1 || KB == 2, "32 or 64 keys per wave");
 
@@ -106,9 +103,15 @@ verify_partial_mfma(const PartialParams p) {
     const int wave = tid >> 6;
     const int n = lane & 31;                // row (B/D operand) or key (A operand) index
     const int h = lane >> 5;                // lane half
-    char* vt = reinterpret_cast<char*>(smem) + (size_t)wave * D * VT_ROW;
+    char* vt = reinterpret_cast<char*>(smem) + (size_t)wave * WK * VROW;
+    // this lane's byte offsets in the V tile: its 16-byte store (key lane/LPK
+    // of a load, dims 8*(lane%LPK)..+7) and its transposing-read address
+    // (group g = lane/16, i = lane%16: key 4*(lane/32) + i/4, dims
+    // 16*(g%2) + 4*(i%4)..+3; the step, block and 8-key half add constants)
+    const int v_st_off = (lane / LPK) * VROW + (lane % LPK) * 16;
+    const int v_tr_off = (4 * h + ((lane & 15) >> 2)) * VROW + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
     constexpr int CST = D + 4;                                   // combine row stride (floats)
-    float* c_acc = smem;                                         // [waves][RT][CST]  (aliases V^T)
+    float* c_acc = smem;                                         // [waves][RT][CST]  (aliases the V tiles)
     float* c_ml = smem + (size_t)kVerifyWaves * p.RT * CST;      // [waves][RT][2]
     float* c_wt = c_ml + kVerifyWaves * p.RT * 2;                // [RT][waves]
     int* s_len = reinterpret_cast<int*>(reinterpret_cast<char*>(smem) + p.lds_main);
@@ -189,18 +192,10 @@ verify_partial_mfma(const PartialParams p) {
                 for (int ks = 0; ks < KS; ++ks)
                     kr[kb][ks] = buffer_load16_policy<DECATTN_VERIFY_K_POLICY>(krs, (uint32_t)(kbase + kb * 32 + n) * (D * 2) + ks * 32 + h * 16);
 
-            // V^T into this wave's LDS tile, columns in S^T register order
+            // V into this wave's LDS tile, row-major
 #pragma unroll
-            for (int st = 0; st < VSTEP; ++st) {
-                const int vp = vt_position(st * KPL + lane / LPK);
-                const int d0 = (lane % LPK) * 8;
-                const uint32_t w[4] = {vr[st].x, vr[st].y, vr[st].z, vr[st].w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    *reinterpret_cast<uint16_t*>(vt + vt_offset<VT_ROW>(d0 + 2 * e, vp)) = (uint16_t)(w[e] & 0xFFFFu);
-                    *reinterpret_cast<uint16_t*>(vt + vt_offset<VT_ROW>(d0 + 2 * e + 1, vp)) = (uint16_t)(w[e] >> 16);
-                }
-            }
+            for (int st = 0; st < VSTEP; ++st)
+                *reinterpret_cast<uint4*>(vt + v_st_off + st * KPL * VROW) = vr[st];
 
             // scores S^T = K Q^T, scaled to log2 units and masked per row
             float s[KB][16];
@@ -266,7 +261,7 @@ verify_partial_mfma(const PartialParams p) {
                 }
             }
 
-            // O^T += V^T P^T (reads of this wave's own LDS tile, after its writes)
+            // O^T += V^T P^T (transposing reads of this wave's own LDS tile, after its writes)
             __builtin_amdgcn_wave_barrier();
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
@@ -274,17 +269,21 @@ verify_partial_mfma(const PartialParams p) {
                 for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
                     for (int j = 0; j < 2; ++j) {
-                        const uint4 a = *reinterpret_cast<const uint4*>(
-                            vt + vt_offset<VT_ROW>(db * 32 + n, kb * 32 + j * 16 + h * 8));
+                        // keys 16j + 4h + 0..3 and 16j + 8 + 4h + 0..3 of block kb at
+                        // dim 32db + lane%32: the order P has in registers
+                        const char* ap = vt + v_tr_off + (kb * 32 + j * 16) * VROW + db * 64;
+                        const uint2 a0 = lds_read_tr16_b64(ap);
+                        const uint2 a1 = lds_read_tr16_b64(ap + 8 * VROW);
+                        const uint4 a = make_uint4(a0.x, a0.y, a1.x, a1.y);
                         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(bhi[kb][j]), acc[db], 0, 0, 0);
                         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(blo[kb][j]), acc[db], 0, 0, 0);
                     }
                 }
             }
-            __builtin_amdgcn_wave_barrier();     // the next sub-tile rewrites the V^T tile
+            __builtin_amdgcn_wave_barrier();     // the next sub-tile rewrites the V tile
         }
 
-        // ---- combine the waves (LDS aliases the V^T tiles: wait for all reads)
+        // ---- combine the waves (LDS aliases the V tiles: wait for all reads)
         l_run += __shfl_xor(l_run, 32);
         __syncthreads();
         if (row_ok) {
