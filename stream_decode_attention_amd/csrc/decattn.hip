@@ -51,10 +51,10 @@ struct Plan {
 };
 
 int pick_default_chunk(int B, int T, int G, int Hkv, int S_max) {
-    // verify chunks that fit the matrix-core kernel: 512-key tiles (measured
-    // fastest per call at the Llama-3.2-3B verify shape: one round of
-    // workgroups, and the fewest tiles for the merge)
-    if (T > 1 && T * G <= kVerifyMaxRows) return 512;
+    // verify chunks that fit the matrix-core kernel: 256-key tiles (two
+    // pipelined sub-tiles per workgroup; measured fastest per call at the
+    // Llama-3.2-3B verify shape)
+    if (T > 1 && T * G <= kVerifyMaxRows) return 256;
     // Enough tiles to occupy the 256 compute units several times over while
     // S_max is the only length the host knows; larger tiles cut partial-state
     // traffic (about G*(D+2)*4 bytes per tile against 4*D bytes per key) and
@@ -101,7 +101,9 @@ int make_plan(int B, int T, int Hq, int Hkv, int D, int S_max, int chunk, Plan* 
     // verify chunks of at most 32 rows per kv head on tiles of a multiple of
     // 128 keys run on the matrix cores (scores and p.V are dense products there)
     p.mfma = T > 1 && p.RT <= kVerifyMaxRows && chunk % 128 == 0;
-    p.mfma_kb = chunk % 256 == 0 ? 2 : 1;
+    // one 32-key block per wave: a 128-key sub-tile per workgroup, and room
+    // in registers for the next sub-tile's loads while one is computed
+    p.mfma_kb = 1;
     {
         const size_t vt = (size_t)kVerifyWaves * (32 * p.mfma_kb) * verify_vrow(D);
         const size_t comb = (size_t)verify_comb_floats(p.RT, D) * sizeof(float);
@@ -177,7 +179,7 @@ hipError_t launch_verify_dk(const Plan& pl, const PartialParams& pp, hipStream_t
 template <int D>
 hipError_t launch_partial_d(const Plan& pl, const PartialParams& pp, hipStream_t s) {
     if (pl.mfma && pp.causal)
-        return pl.mfma_kb == 2 ? launch_verify_dk<D, 2>(pl, pp, s) : launch_verify_dk<D, 1>(pl, pp, s);
+        return launch_verify_dk<D, 1>(pl, pp, s);
     switch (pl.R) {
         case 1: return launch_partial_dr<D, 1>(pl, pp, s);
         case 2: return launch_partial_dr<D, 2>(pl, pp, s);

@@ -23,8 +23,10 @@
 //    so the B operand (P) is packed from registers as is. P is split into
 //    bf16 hi + lo parts (two MFMAs) so the product keeps about 16 bits of P
 //    (fp32 output error below 1e-4), V being exact in bf16.
-//  * the four waves of a workgroup split each sub-tile's keys and are combined
-//    through LDS into the tile's partial state, written in the decode layout.
+//  * the four waves of a workgroup split each sub-tile's keys (32 each);
+//    sub-tiles stream through a ring of two register buffers, and the waves
+//    are combined through LDS into the tile's partial state, written in the
+//    decode layout.
 //
 // Work distribution, lengths and buffer-resource loads as split_kv_partial
 // (persistent grid over attended tiles, keys past a limit read as zeros).
@@ -96,7 +98,7 @@ verify_partial_mfma(const PartialParams p) {
     static_assert(KB == 1 || KB == 2, "32 or 64 keys per wave");
 
     extern __shared__ float smem[];
-    __shared__ int s_count[kVerifyWaves];
+    __shared__ int s_count[2 * kVerifyWaves];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -116,28 +118,52 @@ verify_partial_mfma(const PartialParams p) {
     float* c_wt = c_ml + kVerifyWaves * p.RT * 2;                // [RT][waves]
     int* s_len = reinterpret_cast<int*>(reinterpret_cast<char*>(smem) + p.lds_main);
 
-    // one work item per attended tile (keys j < ctx + T) of every (b, kvh)
-    auto items_for = [&](int len) { return (clamp_len(len + p.T, p.S_max) + p.chunk - 1) / p.chunk; };
+    // One work item per attended tile (keys j < ctx + T) of every (b, kvh);
+    // when that leaves a few items for a second round of workgroups and
+    // taking every short last tile (at most a quarter chunk) with the tile
+    // before it does not, those tiles are folded: the item before computes
+    // them too (one more sub-tile, already in flight by then) and writes an
+    // empty state (m = -inf, l = 0, acc = 0) into the folded tile's slot, so
+    // the merge still reads, for every row, slots that partition exactly the
+    // keys that row attends.
+    auto tiles_raw = [&](int len) { return (clamp_len(len + p.T, p.S_max) + p.chunk - 1) / p.chunk; };
+    auto short_tail = [&](int len) {
+        const int lim = clamp_len(len + p.T, p.S_max);
+        const int na = (lim + p.chunk - 1) / p.chunk;
+        return na >= 2 && 4 * (lim - (na - 1) * p.chunk) <= p.chunk;
+    };
 
-    // ---- lengths into LDS; count attended tiles
-    int my_tiles = 0;
+    // ---- lengths into LDS; count attended tiles, with and without folding
+    int my_raw = 0, my_short = 0;
     for (int i = tid; i < p.B; i += blockDim.x) {
         const int len = p.lens[i];
         s_len[i] = len;
-        my_tiles += items_for(len);
+        my_raw += tiles_raw(len);
+        my_short += short_tail(len) ? 1 : 0;
     }
-    for (int o = 32; o > 0; o >>= 1) my_tiles += __shfl_xor(my_tiles, o);
-    if (lane == 0) s_count[wave] = my_tiles;
+    for (int o = 32; o > 0; o >>= 1) {
+        my_raw += __shfl_xor(my_raw, o);
+        my_short += __shfl_xor(my_short, o);
+    }
+    if (lane == 0) {
+        s_count[wave] = my_raw;
+        s_count[kVerifyWaves + wave] = my_short;
+    }
     __syncthreads();
-    int n_tiles = 0;
+    int n_raw = 0, n_short = 0;
 #pragma unroll
-    for (int w = 0; w < kVerifyWaves; ++w) n_tiles += s_count[w];
-    const int n_items = n_tiles * p.Hkv;
-    auto tiles_of = [&](int b) { return items_for(s_len[b]); };
+    for (int w = 0; w < kVerifyWaves; ++w) {
+        n_raw += s_count[w];
+        n_short += s_count[kVerifyWaves + w];
+    }
+    const int P = (int)gridDim.x;
+    const bool fold = (n_raw * p.Hkv + P - 1) / P > ((n_raw - n_short) * p.Hkv + P - 1) / P;
+    const int n_items = (fold ? n_raw - n_short : n_raw) * p.Hkv;
+    auto tiles_of = [&](int b) { return tiles_raw(s_len[b]) - (fold && short_tail(s_len[b]) ? 1 : 0); };
     int b_cur = 0, pre_cur = 0;
 
     const float qs = p.qscale;
-    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    for (int item = blockIdx.x; item < n_items; item += P) {
         // locate (b, kvh, tile); items are b-major, the walk only moves forward
         while (item >= pre_cur + tiles_of(b_cur) * p.Hkv) {
             pre_cur += tiles_of(b_cur) * p.Hkv;
@@ -149,9 +175,11 @@ verify_partial_mfma(const PartialParams p) {
         const int c = u % na;
         const int kvh = u / na;
         const int len = s_len[b];
+        const int lim_head = clamp_len(len + p.T, p.S_max);
+        const bool folded = c == na - 1 && fold && short_tail(len);   // also takes the tile after it
         const int t0 = c * p.chunk;
-        const int t1 = min(t0 + p.chunk, p.S_max);
-        const int lim_all = min(clamp_len(len + p.T, p.S_max), t1);
+        const int t1 = folded ? lim_head : min(t0 + p.chunk, p.S_max);
+        const int lim_all = min(lim_head, t1);
 
         // this lane's row (n) and its key limit; query slice for the B operand.
         // Lanes past the last row load row 0 (all loads issue back to back with
@@ -178,20 +206,26 @@ verify_partial_mfma(const PartialParams p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
-        for (int sub = t0; sub < lim_all; sub += SUB) {
+        // Sub-tiles of SUB keys (WK per wave) stream through a ring of two
+        // register buffers: the next sub-tile's loads are in flight while the
+        // current one is computed.
+        uint4 vr[2][VSTEP];
+        uint4 kr[2][KB][KS];
+        auto load = [&](uint4 (&vd)[VSTEP], uint4 (&kd)[KB][KS], int sub) {
             const int kbase = sub + wave * WK;
             // V first (coalesced, 16 bytes per lane), then K in the A-operand layout
-            uint4 vr[VSTEP];
 #pragma unroll
             for (int st = 0; st < VSTEP; ++st)
-                vr[st] = buffer_load16(vrs, (uint32_t)(kbase + st * KPL + lane / LPK) * (D * 2) + (lane % LPK) * 16);
-            uint4 kr[KB][KS];
+                vd[st] = buffer_load16(vrs, (uint32_t)(kbase + st * KPL + lane / LPK) * (D * 2) + (lane % LPK) * 16);
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
-                    kr[kb][ks] = buffer_load16_policy<DECATTN_VERIFY_K_POLICY>(krs, (uint32_t)(kbase + kb * 32 + n) * (D * 2) + ks * 32 + h * 16);
-
+                    kd[kb][ks] = buffer_load16_policy<DECATTN_VERIFY_K_POLICY>(krs, (uint32_t)(kbase + kb * 32 + n) * (D * 2) + ks * 32 + h * 16);
+            __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the compute that follows
+        };
+        auto compute = [&](const uint4 (&vr)[VSTEP], const uint4 (&kr)[KB][KS], int sub) {
+            const int kbase = sub + wave * WK;
             // V into this wave's LDS tile, row-major
 #pragma unroll
             for (int st = 0; st < VSTEP; ++st)
@@ -281,6 +315,19 @@ verify_partial_mfma(const PartialParams p) {
                 }
             }
             __builtin_amdgcn_wave_barrier();     // the next sub-tile rewrites the V tile
+        };
+
+        // The loads are issued without a condition (keys at or past lim_all
+        // are outside the buffer resource and read nothing): a load skipped on
+        // one path would leave the compiler unable to count the loads still
+        // in flight, and it would then wait for the next sub-tile's as well.
+        load(vr[0], kr[0], t0);                 // t0 < lim_all: the item holds an attended key
+        for (int sub = t0; sub < lim_all; sub += 2 * SUB) {
+            load(vr[1], kr[1], sub + SUB);
+            compute(vr[0], kr[0], sub);
+            if (sub + SUB >= lim_all) break;
+            load(vr[0], kr[0], sub + 2 * SUB);
+            compute(vr[1], kr[1], sub + SUB);
         }
 
         // ---- combine the waves (LDS aliases the V tiles: wait for all reads)
@@ -316,7 +363,14 @@ verify_partial_mfma(const PartialParams p) {
             }
             p.ws_ml[(tile_row0 + tid) * 2 + 0] = M;
             p.ws_ml[(tile_row0 + tid) * 2 + 1] = L;
+            if (folded) {                   // the folded tile's slot: an empty state
+                p.ws_ml[(tile_row0 + p.RT + tid) * 2 + 0] = kNegInf;
+                p.ws_ml[(tile_row0 + p.RT + tid) * 2 + 1] = 0.f;
+            }
         }
+        if (folded)
+            for (int idx = tid; idx < p.RT * (D / 4); idx += blockDim.x)
+                *reinterpret_cast<float4*>(p.ws_acc + (tile_row0 + p.RT) * D + idx * 4) = make_float4(0.f, 0.f, 0.f, 0.f);
         __syncthreads();
         for (int idx = tid; idx < p.RT * (D / 4); idx += blockDim.x) {
             const int r = idx / (D / 4);
