@@ -76,22 +76,67 @@ __device__ __forceinline__ int swizzle_xor_i(int x) {
     return __builtin_amdgcn_ds_swizzle(x, 0x1F | (XOR << 10));
 }
 
+// gfx950 VALU lane swaps (no LDS traffic), as measured on the GPU:
+// swap16(a, b) returns {[a.r0, b.r0, a.r2, b.r2], [a.r1, b.r1, a.r3, b.r3]}
+// and swap32(a, b) returns {[a.lo, b.lo], [a.hi, b.hi]}, where r0..r3 are the
+// 16-lane rows of a register and lo/hi its 32-lane halves. Adding the two
+// results of swap16(a, b) gives rows 0/2 the pair sums of a's rows (0+1, 2+3)
+// and rows 1/3 those of b; adding those of swap32(a, b) gives the lower half
+// a.lo + a.hi and the upper half b.lo + b.hi.
+struct f32x2 {
+    float x, y;
+};
+__device__ __forceinline__ f32x2 swap16(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ f32x2 swap32(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+
 // Reduce across the 64/N lane groups of a wave (lanes with equal index inside
-// their group). N = 8 or 16.
+// their group), result in every lane. N = 8 or 16. The order of the additions
+// is ((g0 + g1) + (g2 + g3)) over the 16-lane rows for every lane.
 template <int N>
 __device__ __forceinline__ float across_groups_sum(float x) {
     if constexpr (N == 8) x += dpp_move<kDppRor8>(x);
-    x += __shfl_xor(x, 16);
-    x += __shfl_xor(x, 32);
-    return x;
+    const f32x2 a = swap16(x, x);
+    x = a.x + a.y;
+    const f32x2 b = swap32(x, x);
+    return b.x + b.y;
 }
 
 template <int N>
 __device__ __forceinline__ float across_groups_max(float x) {
     if constexpr (N == 8) x = fmaxf(x, dpp_move<kDppRor8>(x));
-    x = fmaxf(x, __shfl_xor(x, 16));
-    x = fmaxf(x, __shfl_xor(x, 32));
-    return x;
+    const f32x2 a = swap16(x, x);
+    x = fmaxf(a.x, a.y);
+    const f32x2 b = swap32(x, x);
+    return fmaxf(b.x, b.y);
+}
+
+// Reduce-scatter of M values (M a multiple of 4) across the 64/N lane groups:
+// on return, every lane of 16-lane row q holds in out[m] the sum over all
+// groups of v[4m + q], added in the same order as across_groups_sum.
+template <int N, int M>
+__device__ __forceinline__ void across_groups_sum_scatter(float (&v)[M], float (&out)[M / 4]) {
+    static_assert(M % 4 == 0, "values come in fours");
+    if constexpr (N == 8) {
+#pragma unroll
+        for (int j = 0; j < M; ++j) v[j] += dpp_move<kDppRor8>(v[j]);
+    }
+    float w[M / 2];
+#pragma unroll
+    for (int j = 0; j < M / 2; ++j) {       // rows 0,2: v[2j] pair sums; rows 1,3: v[2j+1]
+        const f32x2 a = swap16(v[2 * j], v[2 * j + 1]);
+        w[j] = a.x + a.y;
+    }
+#pragma unroll
+    for (int m = 0; m < M / 4; ++m) {       // lower half: w[2m] halves summed, upper: w[2m+1]
+        const f32x2 b = swap32(w[2 * m], w[2 * m + 1]);
+        out[m] = b.x + b.y;
+    }
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

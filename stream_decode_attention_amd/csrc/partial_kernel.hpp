@@ -343,26 +343,33 @@ split_kv_partial(const PartialParams p) {
     // work item, in the same order (two workgroup barriers).
     auto finish = [&](const Tile& tl) {
         l_run = across_groups_sum<LPK>(l_run);
+        // acc summed over the key groups and scattered over the four 16-lane
+        // rows: row q ends with dims db*8 + q and db*8 + 4 + q of every slot
+        // (for D = 64 both 8-lane halves of a row hold the same sums)
+        float flat[RP * 8];
 #pragma unroll
         for (int k = 0; k < RP; ++k)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[k][e] = across_groups_sum<LPK>(acc[k][e]);
+            for (int e = 0; e < 8; ++e) flat[k * 8 + e] = acc[k][e];
+        float red[RP * 2];
+        across_groups_sum_scatter<LPK>(flat, red);
 
         const int slot = (rgl * p.nwk + kw) * R;
-        if (kk == 0) {
+        const int q = lane >> 4;
+        if (LPK == 16 || (kk & 1) == 0) {
 #pragma unroll
             for (int k = 0; k < RP; ++k) {
                 const int row = slot_row[k];
                 if (row < R) {
-                    float4* dst = reinterpret_cast<float4*>(s_acc + (size_t)(slot + row) * D + db * 8);
-                    dst[0] = make_float4(acc[k][0], acc[k][1], acc[k][2], acc[k][3]);
-                    dst[1] = make_float4(acc[k][4], acc[k][5], acc[k][6], acc[k][7]);
+                    float* dst = s_acc + (size_t)(slot + row) * D + db * 8 + q;
+                    dst[0] = red[2 * k];
+                    dst[4] = red[2 * k + 1];
                 }
             }
-            if ((db & ((1 << SET_BITS) - 1)) == 0 && own < R) {
-                s_ml[(slot + own) * 2 + 0] = m_run;
-                s_ml[(slot + own) * 2 + 1] = l_run;
-            }
+        }
+        if (kk == 0 && (db & ((1 << SET_BITS) - 1)) == 0 && own < R) {
+            s_ml[(slot + own) * 2 + 0] = m_run;
+            s_ml[(slot + own) * 2 + 1] = l_run;
         }
         __syncthreads();
 
