@@ -373,28 +373,35 @@ split_kv_partial(const PartialParams p) {
         }
         __syncthreads();
 
-        const int total = p.rg_per_block * R * D;
+        // four dims per thread, the key waves folded in a fixed order
+        constexpr int Q4 = D / 4;
+        const int total = p.rg_per_block * R * Q4;
         const size_t tile_row0 = ((size_t)(tl.b * p.Hkv + tl.kvh) * p.NC + tl.c) * p.RT;
         for (int idx = tid; idx < total; idx += blockDim.x) {
-            const int rg2 = idx / (R * D);
-            const int rem = idx - rg2 * (R * D);
-            const int jr = rem / D;
-            const int d = rem - jr * D;
+            const int rg2 = idx / (R * Q4);
+            const int rem = idx - rg2 * (R * Q4);
+            const int jr = rem / Q4;
+            const int d = (rem - jr * Q4) * 4;
             const int r = (tl.rblk * p.rg_per_block + rg2) * R + jr;
             if (r >= p.RT) continue;
             const int base_slot = rg2 * p.nwk * R + jr;     // slot of key wave 0 for this row
             float M = kNegInf;
             for (int w = 0; w < p.nwk; ++w) M = fmaxf(M, s_ml[(base_slot + w * R) * 2]);
-            float A = 0.f, L = 0.f;
+            float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
+            float L = 0.f;
             if (M != kNegInf) {
                 for (int w = 0; w < p.nwk; ++w) {
                     const int sl = base_slot + w * R;
                     const float wt = fast_exp2(s_ml[sl * 2] - M);
-                    A = __builtin_fmaf(wt, s_acc[(size_t)sl * D + d], A);
+                    const float4 a = *reinterpret_cast<const float4*>(s_acc + (size_t)sl * D + d);
+                    A.x = __builtin_fmaf(wt, a.x, A.x);
+                    A.y = __builtin_fmaf(wt, a.y, A.y);
+                    A.z = __builtin_fmaf(wt, a.z, A.z);
+                    A.w = __builtin_fmaf(wt, a.w, A.w);
                     L = __builtin_fmaf(wt, s_ml[sl * 2 + 1], L);
                 }
             }
-            p.ws_acc[(tile_row0 + r) * D + d] = A;
+            *reinterpret_cast<float4*>(p.ws_acc + (tile_row0 + r) * D + d) = A;
             if (d == 0) {
                 p.ws_ml[(tile_row0 + r) * 2 + 0] = M;
                 p.ws_ml[(tile_row0 + r) * 2 + 1] = L;
