@@ -257,7 +257,10 @@ verify_partial_mfma(const PartialParams p) {
                     }
                 }
             }
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            {
+                const f32x2 sw = swap32(mx, mx);    // the other lane half's maximum, in VALU
+                mx = fmaxf(sw.x, sw.y);
+            }
             const float m_new = fmaxf(m_run, mx);
             const float m_use = (m_new == kNegInf) ? 0.f : m_new;
             if (__any(m_run != kNegInf && m_new > m_run)) {
@@ -331,7 +334,10 @@ verify_partial_mfma(const PartialParams p) {
         }
 
         // ---- combine the waves (LDS aliases the V tiles: wait for all reads)
-        l_run += __shfl_xor(l_run, 32);
+        {
+            const f32x2 sw = swap32(l_run, l_run);
+            l_run = sw.x + sw.y;
+        }
         __syncthreads();
         if (row_ok) {
 #pragma unroll
