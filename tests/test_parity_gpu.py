@@ -127,6 +127,36 @@ def test_matrix_core_context_just_past_a_tile_boundary(chunk):
     assert_bf16_close(run_chunk(c, chunk=chunk, out_dtype=torch.bfloat16), ref)
 
 
+# ------------------------------------------------------------- size extremes
+
+def test_row_with_more_tiles_than_one_merge_batch():
+    """1250 tiles in one row: the merge folds them in five batches of 256."""
+    c = workloads.make_case(2, 4, 1, 128, 40000, [40000, 17000], seed=41)
+    ref = oracle.decode_attention(c["q"], c["k"], c["v"], c["lens"], c["scale"])
+    assert_f32_close(run_decode(c, chunk=32), ref)
+    assert_bf16_close(run_decode(c, chunk=32, out_dtype=torch.bfloat16), ref)
+
+
+def test_largest_batch():
+    """B = 4096 (the most lengths the kernels stage in LDS), lengths 0..16."""
+    B = 4096
+    rng = np.random.default_rng(42)
+    lens = rng.integers(0, 17, size=B).astype(np.int32)
+    c = workloads.make_case(B, 2, 1, 64, 16, lens, seed=42)
+    ref = oracle.decode_attention(c["q"], c["k"], c["v"], c["lens"], c["scale"])
+    out = run_decode(c, chunk=16)
+    assert_f32_close(out, ref)
+    assert torch.all(out[torch.from_numpy(lens == 0).to(out.device)] == 0), "rows with no key must be zero"
+
+
+def test_vector_chunk_path_at_most_tokens_and_group():
+    """T = 16 tokens, G = 8: 128 query rows per kv head in 16 row groups."""
+    c = workloads.make_case(2, 16, 2, 64, 700, [500, 33], T=16, seed=43)
+    ref = oracle.chunk_attention(c["q"], c["k"], c["v"], c["lens"], c["scale"])
+    assert_f32_close(run_chunk(c, chunk=64), ref)
+    assert_f32_close(run_chunk(c), ref)
+
+
 # ----------------------------------------------------------- shapes and chunking
 
 @pytest.mark.parametrize("D", [64, 128])
