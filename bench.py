@@ -231,12 +231,32 @@ def main():
     us_one = back_to_back_us(torch, stream, g_one, K, W, busy=flush)
     us_one_floor = back_to_back_us(torch, stream, g_one_floor, K, W, busy=flush)
     cold_med, cold_p10, cold_p90 = cold_us(torch, stream, g_one, max(20, args.steps // 2), flush)
+    # cold inside a step's graph: each call follows a 512 MiB read (twice the
+    # Infinity Cache), as a layer's attention call follows other reads in a
+    # decode step; per call = graph(flush, call, flush, call, ...) minus
+    # graph(flush, flush, ...), both replayed on a busy GPU, median of rounds
+    cold_buf = probe_buf[: 1 << 29]
+
+    def flush_small():
+        sda.probe_read(cold_buf, sink, stream=stream)
+
+    KC = 20
+    g_fc = graph_of(torch, stream, [f for i in range(KC) for f in (flush_small, call(i % 2))])
+    g_f = graph_of(torch, stream, [flush_small] * KC)
+    cold_rounds = []
+    for _ in range(ROUNDS):
+        a = back_to_back_us(torch, stream, [g_fc], 1, 1, busy=flush)
+        b = back_to_back_us(torch, stream, [g_f], 1, 1, busy=flush)
+        cold_rounds.append((a - b) / KC)
+    cold_graph = float(np.median(cold_rounds))
+    del g_fc, g_f
     ms_per_step = us_call / 1e3
     value = kv_bytes / (us_call / 1e6) / 1e9
     achieved = kv_bytes / (us_part / 1e6) / 1e9
     log(f"workload 4: {us_call:.1f} us/call ({value:.0f} GB/s), {K} calls in one graph; partial kernel "
         f"{us_part:.1f} us = {achieved:.0f} GB/s; launch floor {us_floor:.1f} us/call; one call per "
-        f"graph {us_one:.1f} us (floor {us_one_floor:.1f}), cold {cold_med:.1f} us")
+        f"graph {us_one:.1f} us (floor {us_one_floor:.1f}), cold {cold_med:.1f} us; cold inside a graph "
+        f"{cold_graph:.1f} us ({kv_bytes / cold_graph / 1e3:.0f} GB/s)")
 
     traffic = load_traffic(w4.name, chunk)
     result = {
@@ -268,7 +288,13 @@ def main():
             "cold_us": {"median": round(cold_med, 2), "p10": round(cold_p10, 2), "p90": round(cold_p90, 2)},
             "cold_GBps": round(kv_bytes / (cold_med / 1e6) / 1e9, 1),
             "cold_frac_of_hbm_peak": round(kv_bytes / (cold_med / 1e6) / 1e9 / rf.HBM_PEAK_GBPS, 4)},
+        "cold_in_graph": {
+            "us_per_call": round(cold_graph, 2), "calls_per_graph": KC, "flush_bytes": 1 << 29,
+            "us_per_call_rounds": [round(x, 2) for x in cold_rounds],
+            "GBps": round(kv_bytes / (cold_graph / 1e6) / 1e9, 1),
+            "frac_of_hbm_peak": round(kv_bytes / (cold_graph / 1e6) / 1e9 / rf.HBM_PEAK_GBPS, 4)},
         "probe_read_GBps": round(probe_gbps, 1),
+        "frac_of_probe_read": round(value / probe_gbps, 4),
         "roofline": {
             "kernel": "split_kv_partial",
             "bound": "hbm",
