@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for split-KV single-query decode attention.
+"""fp64 CPU oracle for split-KV single-query decode attention, and for the step
+before it (rotary embedding of the new tokens and their K/V-cache write).
 
 TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or link
 this package: only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline
@@ -20,3 +21,12 @@ from .attention import (  # noqa: F401
     kv_head_of,
 )
 from .bf16 import bf16_bracket, f64_to_bf16_bits_rne  # noqa: F401
+from .rope import (  # noqa: F401
+    llama3_scale_frequencies,
+    model_frequencies,
+    rope_frequencies,
+    rope_kv_write,
+    rope_kv_write_f64,
+    rotate_f64,
+    token_positions,
+)
