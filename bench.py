@@ -309,15 +309,88 @@ def main():
     }
     del g_one, g_one_floor
 
+    # ------------------------------------------- the step before attention
+    if not args.headline_only:
+        result["rope_kv_write"] = [rope_step_headline(args, up, sda, workloads, rf, np, torch, stream, flush,
+                                                      c4, q, ks, vs, lens)]
+
     # ------------------------------------------------------- other workloads
     if not args.headline_only:
         result["workloads"] = other_workloads(args, dev, up, sda, workloads, rf, np, torch, stream, flush)
+        result["rope_kv_write"].append(result["workloads"][-1].pop("rope_kv_write"))
 
     # ------------------------------------------------------ CPU oracle baseline
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(c4, rf, np)
 
     print(json.dumps(result), flush=True)
+
+
+ROPE_THETA = 500000.0
+ROPE_LLAMA3 = {"factor": 32.0, "low_freq_factor": 1.0, "high_freq_factor": 4.0, "original_max_position": 8192.0}
+
+
+def rope_bytes(B, T, Hq, Hkv, D):
+    """Bytes a rope_kv_write call must move: q read and written, k and v read
+    and written once (bf16)."""
+    return B * T * D * 2 * (2 * Hq + 4 * Hkv)
+
+
+def rope_timings(args, sda, torch, np, stream, flush, rope_call, attn_call, floor_call):
+    """µs per call of rope alone, of its smallest launch (the floor) and of the
+    rope + attention step, each in graphs of back-to-back calls, median of 5
+    interleaved rounds."""
+    K = 50
+    graphs = {"rope": graph_of(torch, stream, [rope_call] * K),
+              "floor": graph_of(torch, stream, [floor_call] * K),
+              "step": graph_of(torch, stream, [f for _ in range(K // 2) for f in (rope_call, attn_call)]),
+              "attn": graph_of(torch, stream, [attn_call] * (K // 2))}
+    per = {n: [] for n in graphs}
+    for _ in range(5):
+        for n, g in graphs.items():
+            calls = K if n in ("rope", "floor") else K // 2
+            per[n].append(back_to_back_us(torch, stream, [g], 1, 1, busy=flush) / calls)
+    return {n: float(np.median(v)) for n, v in per.items()}
+
+
+def rope_step_headline(args, up, sda, workloads, rf, np, torch, stream, flush, c4, q, ks, vs, lens):
+    """Decode step of the Llama-3-8B-shaped batch: rotate the new q/k, write
+    k/v at each row's length, then attend over j < length + 1 (a T = 1 chunk
+    call on the rotated q)."""
+    w = c4["workload"]
+    B, Hq, Hkv, D, S = w.B, w.Hq, w.Hkv, w.D, w.S_max
+    pos0 = torch.clamp(lens, max=S - 1)
+    qn = up(workloads.bf16_randn((B, 1, Hq, D), 411))
+    kn = up(workloads.bf16_randn((B, 1, Hkv, D), 412))
+    vn = up(workloads.bf16_randn((B, 1, Hkv, D), 413))
+    q_rot = torch.empty_like(qn)
+    chunk = sda.default_chunk(B, 1, Hq, Hkv, D, S)
+    ws = torch.empty(sda.workspace_bytes(B, 1, Hq, Hkv, D, S, chunk), dtype=torch.uint8, device=qn.device)
+    out = torch.empty((B, 1, Hq, D), dtype=torch.bfloat16, device=qn.device)
+    one = [up(workloads.bf16_randn((1, 1, 1, D), 414 + i)) for i in range(3)]
+    kc1 = torch.zeros((1, 1, 16, D), dtype=torch.int16, device=qn.device)
+    vc1 = torch.zeros_like(kc1)
+    q1 = torch.empty_like(one[0])
+    p1 = torch.zeros(1, dtype=torch.int32, device=qn.device)
+
+    def rope_call():
+        sda.rope_kv_write(qn, kn, vn, pos0, q_rot, ks[0], vs[0], ROPE_THETA, stream=stream)
+
+    def attn_call():
+        sda.chunk_attn(q_rot, ks[0], vs[0], pos0, c4["scale"], out, ws, chunk, stream=stream)
+
+    def floor_call():
+        sda.rope_kv_write(one[0], one[1], one[2], p1, q1, kc1, vc1, ROPE_THETA, stream=stream)
+
+    t = rope_timings(args, sda, torch, np, stream, flush, rope_call, attn_call, floor_call)
+    nb = rope_bytes(B, 1, Hq, Hkv, D)
+    log(f"rope_kv_write, batched decode step: {t['rope']:.2f} us/call (floor {t['floor']:.2f}); rope + attention "
+        f"{t['step']:.1f} us vs attention alone {t['attn']:.1f} us")
+    return {"workload": "llama3-8b-batched-decode-step", "B": B, "T": 1, "Hq": Hq, "Hkv": Hkv, "D": D, "S_max": S,
+            "theta": ROPE_THETA, "pairing": "half", "llama3_scaling": False, "calls_per_graph": 50,
+            "us_per_call": round(t["rope"], 2), "launch_floor_us": round(t["floor"], 2),
+            "bytes_per_call": nb, "GBps": round(nb / (t["rope"] / 1e6) / 1e9, 1),
+            "step_us": round(t["step"], 2), "attention_alone_us": round(t["attn"], 2)}
 
 
 def other_workloads(args, dev, up, sda, workloads, rf, np, torch, stream, flush):
@@ -414,6 +487,38 @@ def other_workloads(args, dev, up, sda, workloads, rf, np, torch, stream, flush)
                 "frac_of_hbm_peak": round(kvb / (us / 1e6) / 1e9 / rf.HBM_PEAK_GBPS, 4)})
     log(f"workload 5: {us:.1f} us/call, {res[-1]['GBps']:.0f} GB/s")
     del g5
+
+    # the verify step before attention: rotate and write the T draft tokens
+    # (llama3 frequency scaling), then the chunk call on the rotated q
+    qn = up(workloads.bf16_randn((w.B, w.T, w.Hq, w.D), 511))
+    kn = up(workloads.bf16_randn((w.B, w.T, w.Hkv, w.D), 512))
+    vn = up(workloads.bf16_randn((w.B, w.T, w.Hkv, w.D), 513))
+    q_rot = torch.empty_like(qn)
+    one = [up(workloads.bf16_randn((1, 1, 1, w.D), 514 + i)) for i in range(3)]
+    kc1 = torch.zeros((1, 1, 16, w.D), dtype=torch.int16, device=dev)
+    vc1 = torch.zeros_like(kc1)
+    q1 = torch.empty_like(one[0])
+    p1 = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def rope_call():
+        sda.rope_kv_write(qn, kn, vn, lens, q_rot, k0, v0, ROPE_THETA, llama3=ROPE_LLAMA3, stream=stream)
+
+    def attn_call():
+        sda.chunk_attn(q_rot, k0, v0, lens, c["scale"], out, ws, chunk, stream=stream)
+
+    def floor_call():
+        sda.rope_kv_write(one[0], one[1], one[2], p1, q1, kc1, vc1, ROPE_THETA, llama3=ROPE_LLAMA3, stream=stream)
+
+    t = rope_timings(args, sda, torch, np, stream, flush, rope_call, attn_call, floor_call)
+    nb = rope_bytes(w.B, w.T, w.Hq, w.Hkv, w.D)
+    log(f"rope_kv_write, verify step: {t['rope']:.2f} us/call (floor {t['floor']:.2f}); rope + chunk attention "
+        f"{t['step']:.1f} us vs chunk attention alone {t['attn']:.1f} us")
+    res[-1]["rope_kv_write"] = {
+        "workload": "llama3.2-3b-verify-step", "B": w.B, "T": w.T, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
+        "S_max": w.S_max, "theta": ROPE_THETA, "pairing": "half", "llama3_scaling": ROPE_LLAMA3,
+        "calls_per_graph": 50, "us_per_call": round(t["rope"], 2), "launch_floor_us": round(t["floor"], 2),
+        "bytes_per_call": nb, "GBps": round(nb / (t["rope"] / 1e6) / 1e9, 1),
+        "step_us": round(t["step"], 2), "attention_alone_us": round(t["attn"], 2)}
     return res
 
 

@@ -134,6 +134,53 @@ int attn_merge(const int32_t* lens,
                void* workspace, size_t workspace_bytes, int chunk,
                void* stream);
 
+/* The step before attention: rotary position embedding of a step's new
+ * tokens and the write of their K/V into the static cache (tinydecode README,
+ * "What's in here": in-place rope; "how the decode step is put together":
+ * positions come from the device-resident lengths and the K/V write is an
+ * indexed store at those positions; llm-decode-cuda's per-layer step list,
+ * which puts the rotation and the cache write in one step; the llama3 flavour
+ * of rope scaling as the only one, tinydecode README, "not done / known gaps").
+ *
+ * Token i of row b sits at position p = clamp(pos0[b], 0, S_max) + i. Pair j
+ * of every head (j < D/2) turns by the angle p * f_j, f_j = theta^(-2j/D)
+ * (llama3-scaled when asked): a pair (a, b) becomes (a cos - b sin,
+ * a sin + b cos), computed in fp64 and rounded once to nearest-even bf16.
+ *   q_in       bf16 [B][T][Hq][D]; q_out bf16 [B][T][Hq][D] receives the
+ *              rotated q; q_out == q_in rotates in place (any other overlap
+ *              with q_in is rejected)
+ *   k_in, v_in bf16 [B][T][Hkv][D]: the new tokens' keys (unrotated) and values
+ *   pos0       int32 [B], device: each row's length before the step (seq_lens
+ *              for decode, ctx_lens for a verify chunk)
+ *   k_cache, v_cache  bf16 [B][Hkv][S_max][D]: slot p of row b, head h gets
+ *              the rotated k and the unchanged v of token i; a token with
+ *              p >= S_max has no slot and writes no K/V (its q is still
+ *              rotated at p); every other slot is left as it was
+ *   rope       HOST pointer to the frequency description
+ * The caller keeps pos0 + T <= S_max in normal use and advances its lengths
+ * afterwards (for decode: attention over j < pos0 + 1, e.g. chunk_attn with
+ * T = 1 and ctx_lens = pos0). k_in, v_in, the caches, pos0 and q_out must
+ * not overlap (checked on the host). One launch of B*T workgroups; D in
+ * {64, 128}; Hq % Hkv == 0. */
+typedef enum {
+    DECATTN_ROPE_HALF = 0,         /* pairs (x_j, x_{j+D/2}): the Hugging Face Llama layout */
+    DECATTN_ROPE_ADJACENT = 1      /* pairs (x_{2j}, x_{2j+1}): the RoFormer paper's layout */
+} decattn_rope_pairing;
+
+typedef struct {
+    double theta;                  /* frequency base, > 0 */
+    int pairing;                   /* decattn_rope_pairing */
+    int llama3_scaling;            /* 0: none; 1: llama3 frequency scaling with the fields below */
+    double factor;                 /* low frequencies are divided by this */
+    double low_freq_factor;        /* wavelengths above original_max_position / low_freq_factor: divided */
+    double high_freq_factor;       /* wavelengths below original_max_position / high_freq_factor: kept */
+    double original_max_position;  /* in between: linear blend in original_max_position / wavelength */
+} decattn_rope;
+
+int rope_kv_write(const void* q_in, const void* k_in, const void* v_in, const int32_t* pos0,
+                  int B, int T, int Hq, int Hkv, int D, int S_max, const decattn_rope* rope,
+                  void* q_out, void* k_cache, void* v_cache, void* stream);
+
 /* Measurement helpers (the streaming-read probe of llm-decode-cuda's roofline
  * section). decattn_probe_read reads `bytes` (a multiple of 16) from `buf`
  * with 16-byte loads and writes at most 4 bytes to `sink`; decattn_probe_copy

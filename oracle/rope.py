@@ -10,7 +10,8 @@ What the pages fix:
     sequence is (tinydecode README, "how the decode step is put together");
   * q and k are rotated in place by a dedicated kernel (tinydecode README,
     "What's in here": in-place rope), fused with the K/V-cache write in
-    llm-decode-cuda's engine (its layer list: "RoPE + KV-cache write");
+    llm-decode-cuda's engine (its per-layer step list puts the rotation and the
+    cache write in one step);
   * the only rope scaling supported is the llama3 flavour (tinydecode README,
     "not done / known gaps").
 

@@ -16,7 +16,7 @@ import torch
 __all__ = [
     "DecattnError", "load_library", "abi_version", "status_str", "default_chunk",
     "workspace_bytes", "decode_attn", "chunk_attn", "attn_partial", "attn_merge",
-    "probe_read", "probe_copy", "OUT_BF16", "OUT_F32", "LIB_PATH",
+    "probe_read", "probe_copy", "rope_kv_write", "RopeParams", "OUT_BF16", "OUT_F32", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdecattn.so")
@@ -27,6 +27,14 @@ _lib: Optional[ctypes.CDLL] = None
 
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 
+
+class RopeParams(ctypes.Structure):
+    """decattn_rope: the rotary frequencies of a model (include/decattn.h)."""
+    _fields_ = [("theta", ctypes.c_double), ("pairing", ctypes.c_int), ("llama3_scaling", ctypes.c_int),
+                ("factor", ctypes.c_double), ("low_freq_factor", ctypes.c_double),
+                ("high_freq_factor", ctypes.c_double), ("original_max_position", ctypes.c_double)]
+
+
 _SIGNATURES = {
     "decattn_abi_version": ([], _i),
     "decattn_status_str": ([_i], ctypes.c_char_p),
@@ -36,6 +44,8 @@ _SIGNATURES = {
     "chunk_attn": ([_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp, _i, _vp, _sz, _i, _vp], _i),
     "attn_partial": ([_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _i, _vp], _i),
     "attn_merge": ([_vp, _i, _i, _i, _i, _i, _i, _i, _vp, _i, _vp, _sz, _i, _vp], _i),
+    "rope_kv_write": ([_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, ctypes.POINTER(RopeParams), _vp, _vp, _vp,
+                       _vp], _i),
     "decattn_probe_read": ([_vp, _sz, _vp, _vp], _i),
     "decattn_probe_copy": ([_vp, _vp, _sz, _vp], _i),
 }
@@ -188,6 +198,48 @@ def attn_merge(lens, out, workspace, *, T: int, Hq: int, Hkv: int, S_max: int, c
         _ptr(workspace, "workspace", (torch.uint8,)), workspace.numel(), int(chunk),
         _stream(stream, out.device))
     _check("attn_merge", st)
+
+
+_PAIRING = {"half": 0, "adjacent": 1}
+
+
+def rope_params(theta: float, pairing: str = "half", llama3: Optional[dict] = None) -> RopeParams:
+    """Pack the frequency description; ``llama3`` holds factor, low_freq_factor,
+    high_freq_factor and original_max_position when that scaling applies."""
+    if pairing not in _PAIRING:
+        raise ValueError(f"pairing must be one of {sorted(_PAIRING)}")
+    r = RopeParams(float(theta), _PAIRING[pairing], 0, 0.0, 0.0, 0.0, 0.0)
+    if llama3:
+        r.llama3_scaling = 1
+        r.factor = float(llama3["factor"])
+        r.low_freq_factor = float(llama3["low_freq_factor"])
+        r.high_freq_factor = float(llama3["high_freq_factor"])
+        r.original_max_position = float(llama3["original_max_position"])
+    return r
+
+
+def rope_kv_write(q_in, k_in, v_in, pos0, q_out, k_cache, v_cache, theta: float, pairing: str = "half",
+                  llama3: Optional[dict] = None, stream=None):
+    """Rotate the step's new q (into ``q_out``, which may be ``q_in``) and k by
+    their positions pos0[b] + i and store k, v into the caches there.
+
+    q_in / q_out bf16 [B,T,Hq,D]; k_in / v_in bf16 [B,T,Hkv,D]; pos0 int32 [B]
+    (device); caches bf16 [B,Hkv,S_max,D]. See include/decattn.h.
+    """
+    B, T, Hq, D = q_in.shape
+    _, Hkv, S_max, Dk = k_cache.shape
+    if tuple(q_out.shape) != (B, T, Hq, D) or tuple(k_in.shape) != (B, T, Hkv, D) \
+            or tuple(v_in.shape) != (B, T, Hkv, D) or Dk != D or k_cache.shape[0] != B \
+            or tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(pos0.shape) != (B,):
+        raise ValueError("shape mismatch between q, k, v, pos0 and the caches")
+    params = rope_params(theta, pairing, llama3)
+    st = load_library().rope_kv_write(
+        _ptr(q_in, "q_in", _BF16), _ptr(k_in, "k_in", _BF16), _ptr(v_in, "v_in", _BF16),
+        _ptr(pos0, "pos0", (torch.int32,)), B, T, Hq, Hkv, D, S_max, ctypes.byref(params),
+        _ptr(q_out, "q_out", _BF16), _ptr(k_cache, "k_cache", _BF16), _ptr(v_cache, "v_cache", _BF16),
+        _stream(stream, q_in.device))
+    _check("rope_kv_write", st)
+    return q_out
 
 
 def probe_read(buf: torch.Tensor, sink: torch.Tensor, stream=None):

@@ -18,6 +18,7 @@
 #include "merge_kernel.hpp"
 #include "partial_kernel.hpp"
 #include "probe_kernel.hpp"
+#include "rope_kernel.hpp"
 #include "verify_kernel.hpp"
 
 namespace decattn {
@@ -266,6 +267,28 @@ int attention(const void* q, const void* k, const void* v, const int32_t* lens, 
     return run_merge(pl, lens, causal, out, out_dtype, ws, s);
 }
 
+// True when [a, a + na) and [b, b + nb) share a byte.
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+bool positive_finite(double x) { return std::isfinite(x) && x > 0.0; }
+
+int check_rope(const decattn_rope* r) {
+    if (!r) return DECATTN_ERR_INVALID_ARG;
+    if (r->pairing != DECATTN_ROPE_HALF && r->pairing != DECATTN_ROPE_ADJACENT) return DECATTN_ERR_INVALID_ARG;
+    if (!positive_finite(r->theta)) return DECATTN_ERR_INVALID_ARG;
+    if (r->llama3_scaling != 0 && r->llama3_scaling != 1) return DECATTN_ERR_INVALID_ARG;
+    if (r->llama3_scaling) {
+        if (!positive_finite(r->factor) || !positive_finite(r->low_freq_factor) ||
+            !positive_finite(r->high_freq_factor) || !positive_finite(r->original_max_position))
+            return DECATTN_ERR_INVALID_ARG;
+        if (!(r->high_freq_factor > r->low_freq_factor)) return DECATTN_ERR_INVALID_ARG;
+    }
+    return DECATTN_OK;
+}
+
 }  // namespace
 }  // namespace decattn
 
@@ -336,6 +359,59 @@ int attn_merge(const int32_t* lens, int B, int T, int Hq, int Hkv, int D, int S_
     if (workspace_bytes < pl.total_bytes) return DECATTN_ERR_WORKSPACE;
     if ((st = check_out(out, out_dtype)) != DECATTN_OK) return st;
     return run_merge(pl, lens, causal, out, out_dtype, workspace, static_cast<hipStream_t>(stream));
+}
+
+int rope_kv_write(const void* q_in, const void* k_in, const void* v_in, const int32_t* pos0, int B, int T,
+                  int Hq, int Hkv, int D, int S_max, const decattn_rope* rope, void* q_out, void* k_cache,
+                  void* v_cache, void* stream) {
+    if (!q_in || !k_in || !v_in || !pos0 || !q_out || !k_cache || !v_cache) return DECATTN_ERR_INVALID_ARG;
+    if (B <= 0 || T <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || S_max <= 0) return DECATTN_ERR_INVALID_ARG;
+    if (Hq % Hkv != 0) return DECATTN_ERR_INVALID_ARG;
+    if (D != 64 && D != 128) return DECATTN_ERR_UNSUPPORTED;
+    if ((long long)B * T > 0x7FFFFFFF || (long long)S_max + T > 0x7FFFFFFF) return DECATTN_ERR_UNSUPPORTED;
+    int st = check_rope(rope);
+    if (st != DECATTN_OK) return st;
+    if (!aligned16(q_in) || !aligned16(k_in) || !aligned16(v_in) || !aligned16(q_out) || !aligned16(k_cache) ||
+        !aligned16(v_cache) || (reinterpret_cast<uintptr_t>(pos0) & 3u))
+        return DECATTN_ERR_INVALID_ARG;
+    // q_out is q_in itself or apart from every other buffer; the new k/v rows
+    // and the two caches do not overlap each other
+    const size_t qb = (size_t)B * T * Hq * D * 2, kb = (size_t)B * T * Hkv * D * 2;
+    const size_t cb = (size_t)B * Hkv * S_max * D * 2;
+    if (q_out != q_in && overlaps(q_out, qb, q_in, qb)) return DECATTN_ERR_INVALID_ARG;
+    const void* bufs[5] = {k_in, v_in, k_cache, v_cache, pos0};
+    const size_t sizes[5] = {kb, kb, cb, cb, (size_t)B * 4};
+    for (int a = 0; a < 5; ++a) {
+        if (overlaps(q_out, qb, bufs[a], sizes[a])) return DECATTN_ERR_INVALID_ARG;
+        for (int c = a + 1; c < 5; ++c)
+            if (overlaps(bufs[a], sizes[a], bufs[c], sizes[c])) return DECATTN_ERR_INVALID_ARG;
+    }
+    RopeParams rp{};
+    rp.q_in = static_cast<const uint16_t*>(q_in);
+    rp.k_in = static_cast<const uint16_t*>(k_in);
+    rp.v_in = static_cast<const uint16_t*>(v_in);
+    rp.pos0 = pos0;
+    rp.q_out = static_cast<uint16_t*>(q_out);
+    rp.k_cache = static_cast<uint16_t*>(k_cache);
+    rp.v_cache = static_cast<uint16_t*>(v_cache);
+    rp.T = T; rp.Hq = Hq; rp.Hkv = Hkv; rp.S_max = S_max;
+    rp.llama3 = rope->llama3_scaling;
+    rp.theta = rope->theta;
+    rp.factor = rope->factor;
+    rp.low_freq_factor = rope->low_freq_factor;
+    rp.high_freq_factor = rope->high_freq_factor;
+    rp.original_max_position = rope->original_max_position;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const dim3 grid((unsigned)(B * T)), block(kRopeThreads);
+    const bool adj = rope->pairing == DECATTN_ROPE_ADJACENT;
+    if (D == 64) {
+        if (adj) hipLaunchKernelGGL((rope_kv_write_kernel<64, true>), grid, block, 0, s, rp);
+        else hipLaunchKernelGGL((rope_kv_write_kernel<64, false>), grid, block, 0, s, rp);
+    } else {
+        if (adj) hipLaunchKernelGGL((rope_kv_write_kernel<128, true>), grid, block, 0, s, rp);
+        else hipLaunchKernelGGL((rope_kv_write_kernel<128, false>), grid, block, 0, s, rp);
+    }
+    return hipGetLastError() == hipSuccess ? DECATTN_OK : DECATTN_ERR_HIP;
 }
 
 int decattn_probe_read(const void* buf, size_t bytes, void* sink, void* stream) {

@@ -34,7 +34,7 @@ def test_header_declares_the_boundary():
     names = set(declared_functions())
     assert {"decode_attn", "chunk_attn", "attn_partial", "attn_merge", "decattn_workspace_bytes",
             "decattn_default_chunk", "decattn_status_str", "decattn_abi_version",
-            "decattn_probe_read", "decattn_probe_copy"} <= names
+            "decattn_probe_read", "decattn_probe_copy", "rope_kv_write"} <= names
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -125,3 +125,47 @@ def test_probes_reject_bad_arguments(lib):
     assert lib.decattn_probe_read(FAKE, 100, FAKE, None) == 1      # not a multiple of 16
     assert lib.decattn_probe_read(None, 1024, FAKE, None) == 1
     assert lib.decattn_probe_copy(FAKE, FAKE + 8, 1024, None) == 1
+
+
+# rope_kv_write: every case below fails a host check, so nothing is launched.
+# Disjoint fake addresses for a B=2, T=3, Hq=8, Hkv=2, D=64, S_max=64 step.
+_ROPE_PTRS = dict(q=0x1000000, k=0x2000000, v=0x3000000, pos=0x4000000, qo=0x1000000,
+                  kc=0x5000000, vc=0x6000000)
+
+
+def _rope(lib, rope=None, **kw):
+    a = dict(_ROPE_PTRS, B=2, T=3, Hq=8, Hkv=2, D=64, S=64)
+    a.update(kw)
+    r = rope if rope is not None else sda.rope_params(10000.0)
+    rp = ctypes.byref(r) if r is not False else None
+    return lib.rope_kv_write(a["q"], a["k"], a["v"], a["pos"], a["B"], a["T"], a["Hq"], a["Hkv"], a["D"],
+                             a["S"], rp, a["qo"], a["kc"], a["vc"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(pos=None), 1), (dict(qo=None), 1),
+    (dict(kc=None), 1), (dict(vc=None), 1),
+    (dict(B=0), 1), (dict(T=0), 1), (dict(Hq=0), 1), (dict(S=0), 1), (dict(Hq=9), 1),
+    (dict(D=96), 2), (dict(D=256), 2), (dict(S=0x7FFFFFFF), 2),
+    (dict(q=0x1000008, qo=0x1000008), 1), (dict(pos=0x4000002), 1), (dict(kc=0x5000004), 1),
+    (dict(qo=0x1000010), 1),                    # q_out overlaps q_in without being it
+    (dict(vc=0x5000000), 1),                    # the two caches overlap
+    (dict(k=0x5000100), 1),                     # new keys inside the key cache
+    (dict(qo=0x6000000), 1),                    # q_out inside the value cache
+])
+def test_rope_kv_write_rejects_bad_arguments(lib, kw, status):
+    assert _rope(lib, **kw) == status
+
+
+def test_rope_kv_write_rejects_bad_frequencies(lib):
+    bad = [sda.RopeParams(0.0, 0, 0, 0, 0, 0, 0), sda.RopeParams(float("nan"), 0, 0, 0, 0, 0, 0),
+           sda.RopeParams(-1.0, 0, 0, 0, 0, 0, 0), sda.RopeParams(1e4, 2, 0, 0, 0, 0, 0),
+           sda.RopeParams(1e4, 0, 2, 0, 0, 0, 0),
+           sda.RopeParams(1e4, 0, 1, 0.0, 1.0, 4.0, 8192.0),      # factor 0
+           sda.RopeParams(1e4, 0, 1, 8.0, 4.0, 4.0, 8192.0),      # high == low
+           sda.RopeParams(1e4, 0, 1, 8.0, 1.0, 4.0, float("inf"))]
+    for r in bad:
+        assert _rope(lib, rope=r) == 1
+    assert _rope(lib, rope=False) == 1          # no description at all
+    with pytest.raises(ValueError):
+        sda.rope_params(1e4, pairing="interleaved")
