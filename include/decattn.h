@@ -117,6 +117,23 @@ int chunk_attn(const void* q, const void* k_cache, const void* v_cache,
                void* workspace, size_t workspace_bytes, int chunk,
                void* stream);
 
+/* Causal attention of many query tokens (prefill, or a long chunk of it) on
+ * the matrix cores: the chunk_attn operation for any T (query token i of row
+ * b attends keys j < ctx_lens[b] + i + 1, clamped to S_max; the T tokens' K/V
+ * already sit at positions ctx .. ctx+T-1), read with the tiled online
+ * softmax that tinydecode's verify pass and llm-decode-cuda's next step call
+ * for, with no split over keys and so no workspace.
+ *   q          bf16 [B][T][Hq][D];  out [B][T][Hq][D], bf16 or fp32
+ *   k_cache, v_cache, ctx_lens, scale as chunk_attn
+ * bf16 output uses bf16 softmax weights in p.V; fp32 output carries them as
+ * bf16 hi + lo parts (about 16 bits), which keeps |out - exact| within 1e-4.
+ * One launch, no host sync, capturable. D in {64, 128}; G = Hq/Hkv in 1..8;
+ * (S_max + 64) * D * 2 < 2^32. Rows with no key (ctx + i + 1 <= 0) output 0. */
+int prefill_attn(const void* q, const void* k_cache, const void* v_cache,
+                 const int32_t* ctx_lens,
+                 int B, int T, int Hq, int Hkv, int D, int S_max, float scale,
+                 void* out, int out_dtype, void* stream);
+
 /* The two phases of decode_attn / chunk_attn as separate launches, for callers
  * that time them apart or merge partial state produced elsewhere.
  * `causal` = 0 gives decode (T must be 1, lens = seq_lens); 1 gives chunk

@@ -16,7 +16,7 @@ import torch
 __all__ = [
     "DecattnError", "load_library", "abi_version", "status_str", "default_chunk",
     "workspace_bytes", "decode_attn", "chunk_attn", "attn_partial", "attn_merge",
-    "probe_read", "probe_copy", "rope_kv_write", "RopeParams", "OUT_BF16", "OUT_F32", "LIB_PATH",
+    "probe_read", "probe_copy", "rope_kv_write", "RopeParams", "prefill_attn", "OUT_BF16", "OUT_F32", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdecattn.so")
@@ -43,6 +43,7 @@ _SIGNATURES = {
     "decode_attn": ([_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _i, _vp, _sz, _i, _vp], _i),
     "chunk_attn": ([_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp, _i, _vp, _sz, _i, _vp], _i),
     "attn_partial": ([_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _i, _vp], _i),
+    "prefill_attn": ([_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp, _i, _vp], _i),
     "attn_merge": ([_vp, _i, _i, _i, _i, _i, _i, _i, _vp, _i, _vp, _sz, _i, _vp], _i),
     "rope_kv_write": ([_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, ctypes.POINTER(RopeParams), _vp, _vp, _vp,
                        _vp], _i),
@@ -167,6 +168,23 @@ def chunk_attn(q, k_cache, v_cache, ctx_lens, scale: float, out, workspace, chun
         _ptr(workspace, "workspace", (torch.uint8,)), workspace.numel(), int(chunk),
         _stream(stream, q.device))
     _check("chunk_attn", st)
+    return out
+
+
+def prefill_attn(q, k_cache, v_cache, ctx_lens, scale: float, out, stream=None):
+    """Causal attention of T query tokens on the matrix cores (any T): token i
+    attends keys j < ctx_lens[b]+i+1. q bf16 [B,T,Hq,D]; out fp32 or bf16
+    [B,T,Hq,D]; no workspace. See include/decattn.h."""
+    B, T, Hq, D = q.shape
+    _, Hkv, S_max, Dk = k_cache.shape
+    if Dk != D or tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(out.shape) != (B, T, Hq, D) \
+            or k_cache.shape[0] != B or tuple(ctx_lens.shape) != (B,):
+        raise ValueError("shape mismatch between q, caches, ctx_lens and out")
+    st = load_library().prefill_attn(
+        _ptr(q, "q", _BF16), _ptr(k_cache, "k_cache", _BF16), _ptr(v_cache, "v_cache", _BF16),
+        _ptr(ctx_lens, "ctx_lens", (torch.int32,)), B, T, Hq, Hkv, D, S_max, float(scale),
+        _ptr(out, "out", (torch.float32,) + _BF16), _out_dtype(out), _stream(stream, q.device))
+    _check("prefill_attn", st)
     return out
 
 

@@ -17,6 +17,7 @@
 #include "../../include/decattn.h"
 #include "merge_kernel.hpp"
 #include "partial_kernel.hpp"
+#include "prefill_kernel.hpp"
 #include "probe_kernel.hpp"
 #include "rope_kernel.hpp"
 #include "verify_kernel.hpp"
@@ -197,6 +198,15 @@ hipError_t launch_partial_d(const Plan& pl, const PartialParams& pp, hipStream_t
     }
 }
 
+// Scores are taken in log2 units (softmax on exp2): the kernels multiply q.k
+// by scale*log2(e), rounded once to fp32; a zero scale becomes the smallest
+// normal float, whose scores all round to 2^0.
+float log2_scale(float scale) {
+    const double qs = std::fabs((double)scale) * 1.4426950408889634;
+    const float qmag = qs < (double)FLT_MIN ? FLT_MIN : (float)qs;
+    return scale < 0.f ? -qmag : qmag;
+}
+
 int run_partial(const Plan& pl, const void* q, const void* k, const void* v, const int32_t* lens,
                 float scale, int causal, void* ws, hipStream_t s) {
     PartialParams pp{};
@@ -211,12 +221,7 @@ int run_partial(const Plan& pl, const void* q, const void* k, const void* v, con
     pp.nwk = pl.nwk; pp.rg_per_block = pl.rg_per_block; pp.n_row_blocks = pl.n_row_blocks;
     pp.B = pl.B;
     pp.lds_main = (int)pl.mfma_lds_main;
-    // scores are taken in log2 units (softmax on exp2): the kernels multiply
-    // q.k by scale*log2(e), rounded once to fp32; a zero scale becomes the
-    // smallest normal float, whose scores all round to 2^0
-    const double qs = std::fabs((double)scale) * 1.4426950408889634;
-    const float qmag = qs < (double)FLT_MIN ? FLT_MIN : (float)qs;
-    pp.qscale = scale < 0.f ? -qmag : qmag;
+    pp.qscale = log2_scale(scale);
     const hipError_t e = pl.D == 64 ? launch_partial_d<64>(pl, pp, s) : launch_partial_d<128>(pl, pp, s);
     return e == hipSuccess ? DECATTN_OK : DECATTN_ERR_HIP;
 }
@@ -359,6 +364,55 @@ int attn_merge(const int32_t* lens, int B, int T, int Hq, int Hkv, int D, int S_
     if (workspace_bytes < pl.total_bytes) return DECATTN_ERR_WORKSPACE;
     if ((st = check_out(out, out_dtype)) != DECATTN_OK) return st;
     return run_merge(pl, lens, causal, out, out_dtype, workspace, static_cast<hipStream_t>(stream));
+}
+
+int prefill_attn(const void* q, const void* k_cache, const void* v_cache, const int32_t* ctx_lens, int B,
+                 int T, int Hq, int Hkv, int D, int S_max, float scale, void* out, int out_dtype, void* stream) {
+    if (!q || !k_cache || !v_cache || !ctx_lens || !out) return DECATTN_ERR_INVALID_ARG;
+    if (B <= 0 || T <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || S_max <= 0) return DECATTN_ERR_INVALID_ARG;
+    if (Hq % Hkv != 0) return DECATTN_ERR_INVALID_ARG;
+    if (D != 64 && D != 128) return DECATTN_ERR_UNSUPPORTED;
+    const int G = Hq / Hkv;
+    if (G > kMaxG) return DECATTN_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || (reinterpret_cast<uintptr_t>(ctx_lens) & 3u))
+        return DECATTN_ERR_INVALID_ARG;
+    if (!std::isfinite(scale)) return DECATTN_ERR_INVALID_ARG;
+    int st = check_out(out, out_dtype);
+    if (st != DECATTN_OK) return st;
+    // one kv head's cache must be addressable by a 32-bit buffer offset
+    if ((long long)(S_max + kPrefillKeys) * D * 2 > 0xFFFFFFFFLL) return DECATTN_ERR_UNSUPPORTED;
+    if ((long long)B * T * Hq > 0x7FFFFFFF) return DECATTN_ERR_UNSUPPORTED;
+    PrefillParams pp{};
+    pp.q = static_cast<const uint16_t*>(q);
+    pp.k = static_cast<const uint16_t*>(k_cache);
+    pp.v = static_cast<const uint16_t*>(v_cache);
+    pp.ctx = ctx_lens;
+    pp.out = out;
+    pp.out_bf16 = out_dtype == DECATTN_OUT_BF16;
+    pp.B = B; pp.T = T; pp.Hq = Hq; pp.Hkv = Hkv; pp.G = G; pp.S_max = S_max;
+    pp.PW = 32 / G;
+    pp.NQB = (T + kPrefillWaves * pp.PW - 1) / (kPrefillWaves * pp.PW);
+    pp.qscale = log2_scale(scale);
+    const long long grid = (long long)B * Hkv * pp.NQB;
+    if (grid > 0x7FFFFFFF) return DECATTN_ERR_UNSUPPORTED;
+    const size_t lds = (size_t)prefill_lds_bytes(D);
+    const void* fn;
+    if (D == 64) fn = pp.out_bf16 ? reinterpret_cast<const void*>(&prefill_attn_mfma<64, false>)
+                                  : reinterpret_cast<const void*>(&prefill_attn_mfma<64, true>);
+    else fn = pp.out_bf16 ? reinterpret_cast<const void*>(&prefill_attn_mfma<128, false>)
+                          : reinterpret_cast<const void*>(&prefill_attn_mfma<128, true>);
+    // sets the dynamic-LDS limit of this kernel on the current device (cached)
+    if (resident_blocks(fn, 256, lds) <= 0) return DECATTN_ERR_HIP;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const dim3 g((unsigned)grid), blk(256);
+    if (D == 64) {
+        if (pp.out_bf16) hipLaunchKernelGGL((prefill_attn_mfma<64, false>), g, blk, lds, s, pp);
+        else hipLaunchKernelGGL((prefill_attn_mfma<64, true>), g, blk, lds, s, pp);
+    } else {
+        if (pp.out_bf16) hipLaunchKernelGGL((prefill_attn_mfma<128, false>), g, blk, lds, s, pp);
+        else hipLaunchKernelGGL((prefill_attn_mfma<128, true>), g, blk, lds, s, pp);
+    }
+    return hipGetLastError() == hipSuccess ? DECATTN_OK : DECATTN_ERR_HIP;
 }
 
 int rope_kv_write(const void* q_in, const void* k_in, const void* v_in, const int32_t* pos0, int B, int T,

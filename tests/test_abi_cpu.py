@@ -34,7 +34,7 @@ def test_header_declares_the_boundary():
     names = set(declared_functions())
     assert {"decode_attn", "chunk_attn", "attn_partial", "attn_merge", "decattn_workspace_bytes",
             "decattn_default_chunk", "decattn_status_str", "decattn_abi_version",
-            "decattn_probe_read", "decattn_probe_copy", "rope_kv_write"} <= names
+            "decattn_probe_read", "decattn_probe_copy", "rope_kv_write", "prefill_attn"} <= names
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -169,3 +169,22 @@ def test_rope_kv_write_rejects_bad_frequencies(lib):
     assert _rope(lib, rope=False) == 1          # no description at all
     with pytest.raises(ValueError):
         sda.rope_params(1e4, pairing="interleaved")
+
+
+def _prefill(lib, **kw):
+    a = dict(q=0x1000000, k=0x2000000, v=0x3000000, lens=0x4000000, B=1, T=300, Hq=8, Hkv=2, D=64, S=512,
+             scale=0.125, out=0x5000000, od=1)
+    a.update(kw)
+    return lib.prefill_attn(a["q"], a["k"], a["v"], a["lens"], a["B"], a["T"], a["Hq"], a["Hkv"], a["D"], a["S"],
+                            a["scale"], a["out"], a["od"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(lens=None), 1), (dict(out=None), 1),
+    (dict(B=0), 1), (dict(T=0), 1), (dict(S=0), 1), (dict(Hq=9), 1),
+    (dict(D=96), 2), (dict(Hq=18, Hkv=2), 2), (dict(S=1 << 24, D=128), 2),
+    (dict(q=0x1000008), 1), (dict(lens=0x4000002), 1), (dict(out=0x5000004), 1), (dict(od=3), 1),
+    (dict(scale=float("nan")), 1),
+])
+def test_prefill_rejects_bad_arguments(lib, kw, status):
+    assert _prefill(lib, **kw) == status

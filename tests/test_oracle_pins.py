@@ -262,6 +262,30 @@ def test_chunk_matches_sdpa_causal_mask():
     assert np.max(np.abs(out - ref)) <= 1e-12
 
 
+@pytest.mark.parametrize("ctx", [[0, 0], [0, 37], [-5, 150]])
+def test_prefill_length_chunk_matches_sdpa_and_torch_causal(ctx):
+    """T in the hundreds (prefill): the explicit-mask SDPA reference, and at
+    ctx = 0 torch's own is_causal path, which knows nothing of the offsets."""
+    rng = np.random.default_rng(32)
+    B, T, Hq, Hkv, D, S = 2, 160, 8, 2, 16, 200
+    q = rng.standard_normal((B, T, Hq, D))
+    k = rng.standard_normal((B, Hkv, S, D))
+    v = rng.standard_normal((B, Hkv, S, D))
+    ctx = np.array(ctx)
+    out = oracle.chunk_attention_f64(q, k, v, ctx, 0.25)
+    # rows with no key (ctx + i + 1 <= 0) are zeros; compare the others
+    live = (ctx[:, None] + np.arange(T)[None, :] + 1) > 0
+    ref = sdpa_chunk(q, k, v, ctx, 0.25)
+    assert np.max(np.abs((out - ref)[live])) <= 1e-12
+    assert np.all(out[~live] == 0)
+    if not ctx.any():
+        qt = torch.as_tensor(q).permute(0, 2, 1, 3)
+        kt = torch.as_tensor(k[:, :, :T]).repeat_interleave(Hq // Hkv, dim=1)
+        vt = torch.as_tensor(v[:, :, :T]).repeat_interleave(Hq // Hkv, dim=1)
+        tc = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True, scale=0.25)
+        assert np.max(np.abs(out - tc.permute(0, 2, 1, 3).numpy())) <= 1e-12
+
+
 def test_chunk_row_unchanged_by_later_key():
     rng = np.random.default_rng(32)
     q = rng.standard_normal((1, 5, 4, 16))
