@@ -314,6 +314,10 @@ def main():
         result["rope_kv_write"] = [rope_step_headline(args, up, sda, workloads, rf, np, torch, stream, flush,
                                                       c4, q, ks, vs, lens)]
 
+    # -------------------------------------------- many-token causal attention
+    if not args.headline_only:
+        result["prefill_attn"] = prefill_runs(up, sda, workloads, np, torch, stream, flush)
+
     # ------------------------------------------------------- other workloads
     if not args.headline_only:
         result["workloads"] = other_workloads(args, dev, up, sda, workloads, rf, np, torch, stream, flush)
@@ -391,6 +395,54 @@ def rope_step_headline(args, up, sda, workloads, rf, np, torch, stream, flush, c
             "us_per_call": round(t["rope"], 2), "launch_floor_us": round(t["floor"], 2),
             "bytes_per_call": nb, "GBps": round(nb / (t["rope"] / 1e6) / 1e9, 1),
             "step_us": round(t["step"], 2), "attention_alone_us": round(t["attn"], 2)}
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
+
+PREFILL_CASES = [
+    # name, B, T, Hq, Hkv, D, S_max, ctx
+    ("llama3-8b-prefill-4096", 1, 4096, 32, 8, 128, 8192, 0),
+    ("llama3-8b-chunked-prefill-2048-after-8192", 1, 2048, 32, 8, 128, 16384, 8192),
+    ("smollm2-360m-prefill-4096", 1, 4096, 15, 5, 64, 8192, 0),
+    ("tinyllama-1.1b-prefill-4096", 1, 4096, 32, 4, 64, 8192, 0),
+]
+
+
+def prefill_flops(B, T, Hq, D, ctx):
+    """Algorithmic flops of causal attention: 4*D per (query row, attended key)."""
+    keys = T * ctx + T * (T + 1) // 2
+    return 4 * B * Hq * D * keys
+
+
+def prefill_runs(up, sda, workloads, np, torch, stream, flush):
+    """prefill_attn per call (graphs of 5 back-to-back calls, median of 5
+    rounds) in both output modes, as TFLOP/s of algorithmic flops against the
+    dense bf16 matrix peak."""
+    res = []
+    for ci, (name, B, T, Hq, Hkv, D, S, ctx) in enumerate(PREFILL_CASES):
+        q = up(workloads.bf16_randn((B, T, Hq, D), 600 + 10 * ci + 1))
+        k = up(workloads.bf16_randn((B, Hkv, S, D), 600 + 10 * ci + 2))
+        v = up(workloads.bf16_randn((B, Hkv, S, D), 600 + 10 * ci + 3))
+        lens = torch.full((B,), ctx, dtype=torch.int32, device=q.device)
+        scale = float(np.float32(1 / np.sqrt(D)))
+        entry = {"workload": name, "B": B, "T": T, "Hq": Hq, "Hkv": Hkv, "D": D, "S_max": S, "ctx": ctx,
+                 "flops_per_call": prefill_flops(B, T, Hq, D, ctx), "calls_per_graph": 5}
+        for dt, tag in ((torch.bfloat16, "bf16_out"), (torch.float32, "f32_out")):
+            out = torch.empty((B, T, Hq, D), dtype=dt, device=q.device)
+            with torch.cuda.stream(stream):
+                sda.prefill_attn(q, k, v, lens, scale, out, stream=stream)
+                stream.synchronize()
+            g = graph_of(torch, stream, [lambda: sda.prefill_attn(q, k, v, lens, scale, out, stream=stream)] * 5)
+            us = float(np.median([back_to_back_us(torch, stream, [g], 1, 1, busy=flush) / 5 for _ in range(5)]))
+            tf = entry["flops_per_call"] / us / 1e6
+            entry[tag] = {"us_per_call": round(us, 2), "TFLOPs": round(tf, 1),
+                          "frac_of_bf16_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+            del g
+        log(f"prefill_attn {name}: bf16 out {entry['bf16_out']['us_per_call']:.1f} us "
+            f"({entry['bf16_out']['TFLOPs']:.0f} TFLOP/s), fp32 out {entry['f32_out']['us_per_call']:.1f} us "
+            f"({entry['f32_out']['TFLOPs']:.0f} TFLOP/s)")
+        res.append(entry)
+    return res
 
 
 def other_workloads(args, dev, up, sda, workloads, rf, np, torch, stream, flush):

@@ -380,7 +380,7 @@ int prefill_attn(const void* q, const void* k_cache, const void* v_cache, const 
     int st = check_out(out, out_dtype);
     if (st != DECATTN_OK) return st;
     // one kv head's cache must be addressable by a 32-bit buffer offset
-    if ((long long)(S_max + kPrefillKeys) * D * 2 > 0xFFFFFFFFLL) return DECATTN_ERR_UNSUPPORTED;
+    if ((long long)(S_max + 4 * kPrefillKeys) * D * 2 > 0xFFFFFFFFLL) return DECATTN_ERR_UNSUPPORTED;
     if ((long long)B * T * Hq > 0x7FFFFFFF) return DECATTN_ERR_UNSUPPORTED;
     PrefillParams pp{};
     pp.q = static_cast<const uint16_t*>(q);

@@ -47,7 +47,10 @@ struct PrefillParams {
 };
 
 constexpr int kPrefillWaves = 4;
-constexpr int kPrefillKeys = 64;         // keys per tile
+#ifndef DECATTN_PREFILL_KEYS
+#define DECATTN_PREFILL_KEYS 64
+#endif
+constexpr int kPrefillKeys = DECATTN_PREFILL_KEYS;   // keys per tile
 
 // LDS row strides in bytes: K rows padded by 16 bytes (the A-operand reads of
 // 32 lanes hit 32 rows at one column), V rows by 64 (as the verify kernel's,
@@ -59,8 +62,23 @@ __host__ __device__ constexpr int prefill_tile_bytes(int D) {
 }
 __host__ __device__ constexpr int prefill_lds_bytes(int D) { return 2 * prefill_tile_bytes(D); }
 
+// A pointer every lane holds the same value of, moved to scalar registers.
+__device__ __forceinline__ const uint16_t* uniform_ptr(const uint16_t* ptr) {
+    const uint64_t u = reinterpret_cast<uint64_t>(ptr);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+    return reinterpret_cast<const uint16_t*>(((uint64_t)hi << 32) | lo);
+}
+
+#ifndef DECATTN_PREFILL_PIPE
+#define DECATTN_PREFILL_PIPE 0
+#endif
+#ifndef DECATTN_PREFILL_WPE
+#define DECATTN_PREFILL_WPE 2
+#endif
+
 template <int D, bool SPLIT>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DECATTN_PREFILL_WPE)))
 prefill_attn_mfma(const PrefillParams p) {
     constexpr int KS = D / 16;              // 16-dim steps of the score product
     constexpr int DB = D / 32;              // 32-dim blocks of the output
@@ -103,7 +121,10 @@ prefill_attn_mfma(const PrefillParams p) {
     const bool wave_has = wpos0 < p.T;
     const int lim_wmin = wave_has ? lim_of(wpos0) : 0;                       // fewest keys of the wave's rows
     const int lim_wmax = wave_has ? lim_of(min(wpos0 + p.PW, p.T) - 1) : 0;  // most keys
-    const int lim_all = lim_of(min(pos0 + kPrefillWaves * p.PW, p.T) - 1);   // most keys of the workgroup
+    // most keys of the workgroup; uniform, and said so: the buffer resources
+    // below must sit in scalar registers (a value the compiler takes for
+    // divergent would put every K/V load in a waterfall loop)
+    const int lim_all = __builtin_amdgcn_readfirstlane(lim_of(min(pos0 + kPrefillWaves * p.PW, p.T) - 1));
 
     // query slice of this lane's row (idle lanes read the workgroup's first row)
     const int qpos = row_ok ? ipos : pos0;
@@ -113,29 +134,43 @@ prefill_attn_mfma(const PrefillParams p) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qv[ks] = *reinterpret_cast<const uint4*>(qrow + ks * 16);
 
-    const size_t head_base = (size_t)(b * p.Hkv + kvh) * p.S_max * D;
+    const size_t head_base = (size_t)bh * p.S_max * D;
     const uint32_t range = (uint32_t)lim_all * D * 2;
-    const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + head_base, range);
-    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + head_base, range);
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(uniform_ptr(p.k + head_base), range);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(uniform_ptr(p.v + head_base), range);
 
-    // this thread's pieces of a tile: key pc / LPR, 16-byte column pc % LPR
+    // this thread's pieces of a tile: key pc / LPR, 16-byte column pc % LPR.
+    // LDS holds two K buffers, then two V buffers.
+    char* const kbase_lds = lds;
+    char* const vbase_lds = lds + 2 * KT * KROW;
     uint4 kst[PPT], vst[PPT];
-    auto gload = [&](int t) {
+    auto gload_k = [&](int t) {
 #pragma unroll
         for (int r = 0; r < PPT; ++r) {
             const int pc = tid + 256 * r;
-            const uint32_t off = (uint32_t)(t * KT + pc / LPR) * (D * 2) + (pc % LPR) * 16;
-            kst[r] = buffer_load16_policy<0>(krs, off);
-            vst[r] = buffer_load16_policy<0>(vrs, off);
+            kst[r] = buffer_load16_policy<0>(krs, (uint32_t)(t * KT + pc / LPR) * (D * 2) + (pc % LPR) * 16);
         }
     };
-    auto lstore = [&](int buf) {
-        char* kt = lds + buf * TILE;
-        char* vt = kt + KT * KROW;
+    auto gload_v = [&](int t) {
+#pragma unroll
+        for (int r = 0; r < PPT; ++r) {
+            const int pc = tid + 256 * r;
+            vst[r] = buffer_load16_policy<0>(vrs, (uint32_t)(t * KT + pc / LPR) * (D * 2) + (pc % LPR) * 16);
+        }
+    };
+    auto lstore_k = [&](int buf) {
+        char* kt = kbase_lds + buf * (KT * KROW);
 #pragma unroll
         for (int r = 0; r < PPT; ++r) {
             const int pc = tid + 256 * r;
             *reinterpret_cast<uint4*>(kt + (pc / LPR) * KROW + (pc % LPR) * 16) = kst[r];
+        }
+    };
+    auto lstore_v = [&](int buf) {
+        char* vt = vbase_lds + buf * (KT * VROW);
+#pragma unroll
+        for (int r = 0; r < PPT; ++r) {
+            const int pc = tid + 256 * r;
             *reinterpret_cast<uint4*>(vt + (pc / LPR) * VROW + (pc % LPR) * 16) = vst[r];
         }
     };
@@ -143,8 +178,23 @@ prefill_attn_mfma(const PrefillParams p) {
     // transposing-read address of this lane in a V tile (see the verify kernel:
     // lanes 4r..4r+3 of a 16-lane group point at key 4h + r, dims 16*(group%2) + 4*(lane%4))
     const int v_tr_off = (4 * h + ((lane & 15) >> 2)) * VROW + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
-    const float qs = p.qscale;
+    // A negative scale is moved into q: flipping the sign bits of q negates
+    // every product and sum exactly, and the exponent argument then takes
+    // |scale*log2(e)|. This also makes the q loads complete before the tile
+    // loop, so no wait inside it is charged to them.
+    const float qs = fabsf(p.qscale);
+    const uint32_t qflip = p.qscale < 0.f ? 0x80008000u : 0u;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        qv[ks].x ^= qflip; qv[ks].y ^= qflip; qv[ks].z ^= qflip; qv[ks].w ^= qflip;
+    }
 
+    // m_run is the row maximum (log2 units) the weights are taken against; it
+    // is moved only when a tile's maximum exceeds it by more than kSlack, so
+    // weights reach 2^kSlack at most and rescaling is rare. acc and l share
+    // the same m_run, so the quotient is unchanged (the online-softmax
+    // identity holds for any reference value, not only the running maximum).
+    constexpr float kSlack = 8.f;
     float m_run = kNegInf, l_run = 0.f;
     f32x16_t acc[DB];
 #pragma unroll
@@ -152,54 +202,65 @@ prefill_attn_mfma(const PrefillParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
-    auto compute = [&](int buf, int k0) {
-        const char* kt = lds + buf * TILE;
-        const char* vt = kt + KT * KROW;
-        float s[KBLK][16];
-        float mx = kNegInf;
+    // raw scores S^T = K Q^T of the K tile in buffer kbuf: the KBLK
+    // accumulation chains interleaved
+    auto qk = [&](f32x16_t (&st)[KBLK], int kbuf) {
+        const char* kt = kbase_lds + kbuf * (KT * KROW);
 #pragma unroll
-        for (int kb = 0; kb < KBLK; ++kb) {
-            f32x16_t st;
+        for (int kb = 0; kb < KBLK; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) st[r] = 0.f;
+            for (int r = 0; r < 16; ++r) st[kb][r] = 0.f;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const uint4 a = *reinterpret_cast<const uint4*>(kt + (kb * 32 + n) * KROW + (ks * 16 + h * 8) * 2);
-                st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qv[ks]), st, 0, 0, 0);
-            }
-            const int kbase = k0 + kb * 32;
-            if (kbase + 32 <= lim_wmin) {           // wave-uniform: every row of the wave attends every key
+        for (int ks = 0; ks < KS; ++ks) {
+            uint4 a[KBLK];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    s[kb][r] = st[r] * qs;
-                    mx = fmaxf(mx, s[kb][r]);
-                }
-            } else {
+            for (int kb = 0; kb < KBLK; ++kb)
+                a[kb] = *reinterpret_cast<const uint4*>(kt + (kb * 32 + n) * KROW + (ks * 16 + h * 8) * 2);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = kbase + 8 * (r >> 2) + 4 * h + (r & 3);
-                    s[kb][r] = key < lim_n ? st[r] * qs : kNegInf;
-                    mx = fmaxf(mx, s[kb][r]);
-                }
-            }
+            for (int kb = 0; kb < KBLK; ++kb)
+                st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[kb]), as_bf16x8(qv[ks]), st[kb], 0, 0, 0);
         }
+    };
+
+    // softmax of the raw scores of the tile at key k0, then O^T += V^T P^T
+    // with the V tile in buffer vbuf
+    auto softmax_pv = [&](f32x16_t (&st)[KBLK], int k0, int vbuf) {
+        const char* vt = vbase_lds + vbuf * (KT * VROW);
+        // keys at or past a row's limit: -inf (only on tiles that cross the
+        // smallest limit of the wave's rows; wave-uniform test)
+        if (k0 + KT > lim_wmin) {
+#pragma unroll
+            for (int kb = 0; kb < KBLK; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                    st[kb][r] = key < lim_n ? st[kb][r] : kNegInf;
+                }
+        }
+        float mx = st[0][0];
+#pragma unroll
+        for (int kb = 0; kb < KBLK; ++kb)
+#pragma unroll
+            for (int r = (kb == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, st[kb][r]);
         {
             const f32x2 sw = swap32(mx, mx);
             mx = fmaxf(sw.x, sw.y);
         }
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-        if (__any(m_run != kNegInf && m_new > m_run)) {
-            const float alpha = fast_exp2(m_run - m_use);
+        const float m_tile = mx * qs;                      // -inf stays -inf (qs > 0)
+        if (__any(m_tile > m_run + kSlack)) {
+            const float m_new = fmaxf(m_run, m_tile);
+            const float m_to = (m_new == kNegInf) ? 0.f : m_new;
+            const float alpha = fast_exp2(m_run - m_to);   // 0 while the row had no key
             l_run *= alpha;
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+            m_run = m_new;
         }
-        m_run = m_new;
+        const float neg_m = (m_run == kNegInf) ? 0.f : -m_run;
 
-        // P = 2^(s - m) as B operands: uint4 j of block kb holds keys
+        // P = 2^(s*qs - m) as B operands: uint4 j of block kb holds keys
         // 16j + 4h + 0..3 and 16j + 8 + 4h + 0..3 of that block
         uint4 bhi[KBLK][2], blo[KBLK][2];
 #pragma unroll
@@ -207,7 +268,7 @@ prefill_attn_mfma(const PrefillParams p) {
             float pv[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                pv[r] = fast_exp2(s[kb][r] - m_use);
+                pv[r] = fast_exp2(__builtin_fmaf(st[kb][r], qs, neg_m));
                 l_run += pv[r];
             }
 #pragma unroll
@@ -226,39 +287,87 @@ prefill_attn_mfma(const PrefillParams p) {
             }
         }
 
-        // O^T += V^T P^T
+        // O^T += V^T P^T: the DB accumulation chains interleaved
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
+        for (int kb = 0; kb < KBLK; ++kb) {
 #pragma unroll
-            for (int kb = 0; kb < KBLK; ++kb) {
+            for (int j = 0; j < 2; ++j) {
+                uint4 a[DB];
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
+                for (int db = 0; db < DB; ++db) {
                     const char* ap = vt + v_tr_off + (kb * 32 + j * 16) * VROW + db * 64;
                     const uint2 a0 = lds_read_tr16_b64(ap);
                     const uint2 a1 = lds_read_tr16_b64(ap + 8 * VROW);
-                    const uint4 a = make_uint4(a0.x, a0.y, a1.x, a1.y);
-                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(bhi[kb][j]), acc[db], 0, 0, 0);
-                    if constexpr (SPLIT)
-                        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(blo[kb][j]), acc[db], 0, 0, 0);
+                    a[db] = make_uint4(a0.x, a0.y, a1.x, a1.y);
+                }
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[db]), as_bf16x8(bhi[kb][j]), acc[db], 0, 0, 0);
+                if constexpr (SPLIT) {
+#pragma unroll
+                    for (int db = 0; db < DB; ++db)
+                        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[db]), as_bf16x8(blo[kb][j]), acc[db], 0, 0, 0);
                 }
             }
         }
     };
 
-    // two LDS buffers: tile t+1 is loaded into registers while tile t is
-    // computed, then stored into the other buffer; one barrier per tile
     const int ntiles = (lim_all + KT - 1) / KT;
-    if (ntiles > 0) {
-        gload(0);
-        lstore(0);
+#if DECATTN_PREFILL_PIPE
+    // Software pipeline: the score products of tile t+1 are issued before the
+    // softmax and p.V of tile t, so the matrix cores work while the vector
+    // ALUs take the exponentials. K runs one tile ahead of V: iteration t
+    // reads K(t+1) and V(t), then stores K(t+2) and V(t+1) into the buffers
+    // K(t) and V(t-1) left (both last read before the previous barrier).
+    // Loads past the last tile read zeros; every wave runs every tile of the
+    // workgroup (a tile past a wave's rows is all masked and adds nothing).
+    gload_k(0);
+    gload_v(0);
+    lstore_k(0);
+    lstore_v(0);
+    gload_k(1);
+    lstore_k(1);
+    __syncthreads();
+    f32x16_t s_cur[KBLK];
+    qk(s_cur, 0);
+    __syncthreads();                       // K(0) is overwritten by K(2) below
+    for (int t = 0; t < ntiles; ++t) {
+        gload_k(t + 2);
+        gload_v(t + 1);
+        f32x16_t s_nxt[KBLK];
+        qk(s_nxt, (t + 1) & 1);
+        softmax_pv(s_cur, t * KT, t & 1);
+        lstore_k(t & 1);
+        lstore_v((t + 1) & 1);
+        __syncthreads();
+#pragma unroll
+        for (int kb = 0; kb < KBLK; ++kb) s_cur[kb] = s_nxt[kb];
     }
+#else
+    // Two buffers each of K and V: tile t+1 is loaded into registers while
+    // tile t is computed, then stored into the other buffers; one barrier per
+    // tile. The load and store of tile t+1 are issued on every iteration (past
+    // the last tile they read zeros and fill buffers nobody reads): a
+    // conditional load would leave the compiler unsure how many loads are in
+    // flight, and it would then wait for them before the score products.
+    gload_k(0);
+    gload_v(0);
+    lstore_k(0);
+    lstore_v(0);
     __syncthreads();
     for (int t = 0; t < ntiles; ++t) {
-        if (t + 1 < ntiles) gload(t + 1);
-        if (t * KT < lim_wmax) compute(t & 1, t * KT);      // wave-uniform
-        if (t + 1 < ntiles) lstore((t + 1) & 1);
+        gload_k(t + 1);
+        gload_v(t + 1);
+        if (t * KT < lim_wmax) {                             // wave-uniform
+            f32x16_t st[KBLK];
+            qk(st, t & 1);
+            softmax_pv(st, t * KT, t & 1);
+        }
+        lstore_k((t + 1) & 1);
+        lstore_v((t + 1) & 1);
         __syncthreads();
     }
+#endif
 
     // rows: join the two halves' sums, normalise, store 4 dims per group
     {
