@@ -1,5 +1,6 @@
-"""fp64 CPU oracle for split-KV single-query decode attention, and for the step
-before it (rotary embedding of the new tokens and their K/V-cache write).
+"""fp64 CPU oracle for split-KV single-query decode attention, for the step
+before it (rotary embedding of the new tokens and their K/V-cache write), and
+for the weight products of a decode step (bf16 and INT8 weight-only GEMV).
 
 TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or link
 this package: only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline
@@ -29,4 +30,11 @@ from .rope import (  # noqa: F401
     rope_kv_write_f64,
     rotate_f64,
     token_positions,
+)
+from .gemv import (  # noqa: F401
+    gemv,
+    gemv_f64,
+    gemv_int8,
+    gemv_int8_f64,
+    quantize_rows_int8,
 )
