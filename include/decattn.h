@@ -134,6 +134,30 @@ int prefill_attn(const void* q, const void* k_cache, const void* v_cache,
                  int B, int T, int Hq, int Hkv, int D, int S_max, float scale,
                  void* out, int out_dtype, void* stream);
 
+/* The weight products of a decode step (llm-decode-cuda: roofline paragraph,
+ * GEMV table, INT8 section): y[b][n] = sum_k W[n][k] x[b][k] for B <= 8
+ * activation vectors. Each weight is read once per call (bytes-bound).
+ *   W        bf16 [N][K] row-major (gemv_bf16), or
+ *   Wq,scale int8 [N][K] row-major with one fp32 scale per row (gemv_int8):
+ *            the weight is q * scale[n]
+ *   x        bf16 [B][K];  y [B][N], fp32 or bf16 per out_dtype
+ * Products accumulate in fp32. K must be a multiple of 8 (bf16) or 16 (int8);
+ * B in 1..8 (vectors beyond what 144 KB of LDS holds at this K go to further
+ * launches, each reading the weights again). One launch per group, no host
+ * sync, capturable. W, Wq, x, y 16-byte aligned; scale 4-byte aligned. */
+int gemv_bf16(const void* W, const void* x, int B, int N, int K,
+              void* y, int out_dtype, void* stream);
+int gemv_int8(const void* Wq, const float* scale, const void* x, int B, int N, int K,
+              void* y, int out_dtype, void* stream);
+
+/* Per-output-row symmetric INT8 quantization, done once when weights are
+ * loaded (llm-decode-cuda, INT8 section), in fp32: a = max_k |W[n][k]|,
+ * scale[n] = a / 127, Wq[n][k] = round-half-even(W[n][k] / scale[n]) in
+ * [-127, 127]; a row of zeros gets scale 0 and codes 0.
+ *   W bf16 [N][K] (K a multiple of 16) -> Wq int8 [N][K], scale fp32 [N];
+ * the three buffers must not overlap. */
+int quantize_rows_int8(const void* W, int N, int K, void* Wq, float* scale, void* stream);
+
 /* The two phases of decode_attn / chunk_attn as separate launches, for callers
  * that time them apart or merge partial state produced elsewhere.
  * `causal` = 0 gives decode (T must be 1, lens = seq_lens); 1 gives chunk

@@ -16,7 +16,8 @@ import torch
 __all__ = [
     "DecattnError", "load_library", "abi_version", "status_str", "default_chunk",
     "workspace_bytes", "decode_attn", "chunk_attn", "attn_partial", "attn_merge",
-    "probe_read", "probe_copy", "rope_kv_write", "RopeParams", "prefill_attn", "OUT_BF16", "OUT_F32", "LIB_PATH",
+    "probe_read", "probe_copy", "rope_kv_write", "RopeParams", "prefill_attn",
+    "gemv_bf16", "gemv_int8", "quantize_rows_int8", "OUT_BF16", "OUT_F32", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdecattn.so")
@@ -44,6 +45,9 @@ _SIGNATURES = {
     "chunk_attn": ([_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp, _i, _vp, _sz, _i, _vp], _i),
     "attn_partial": ([_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _i, _vp], _i),
     "prefill_attn": ([_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp, _i, _vp], _i),
+    "gemv_bf16": ([_vp, _vp, _i, _i, _i, _vp, _i, _vp], _i),
+    "gemv_int8": ([_vp, _vp, _vp, _i, _i, _i, _vp, _i, _vp], _i),
+    "quantize_rows_int8": ([_vp, _i, _i, _vp, _vp, _vp], _i),
     "attn_merge": ([_vp, _i, _i, _i, _i, _i, _i, _i, _vp, _i, _vp, _sz, _i, _vp], _i),
     "rope_kv_write": ([_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, ctypes.POINTER(RopeParams), _vp, _vp, _vp,
                        _vp], _i),
@@ -186,6 +190,42 @@ def prefill_attn(q, k_cache, v_cache, ctx_lens, scale: float, out, stream=None):
         _ptr(out, "out", (torch.float32,) + _BF16), _out_dtype(out), _stream(stream, q.device))
     _check("prefill_attn", st)
     return out
+
+
+def gemv_bf16(W, x, y, stream=None):
+    """y[b, n] = sum_k W[n, k] x[b, k]: W bf16 [N, K], x bf16 [B, K] (B <= 8),
+    y fp32 or bf16 [B, N]. See include/decattn.h."""
+    N, K = W.shape
+    B = x.shape[0]
+    if tuple(x.shape) != (B, K) or tuple(y.shape) != (B, N):
+        raise ValueError("shape mismatch between W, x and y")
+    st = load_library().gemv_bf16(_ptr(W, "W", _BF16), _ptr(x, "x", _BF16), B, N, K,
+                                  _ptr(y, "y", (torch.float32,) + _BF16), _out_dtype(y), _stream(stream, W.device))
+    _check("gemv_bf16", st)
+    return y
+
+
+def gemv_int8(Wq, scale, x, y, stream=None):
+    """y[b, n] = scale[n] * sum_k Wq[n, k] x[b, k]: Wq int8 [N, K], scale fp32 [N]."""
+    N, K = Wq.shape
+    B = x.shape[0]
+    if tuple(x.shape) != (B, K) or tuple(y.shape) != (B, N) or tuple(scale.shape) != (N,):
+        raise ValueError("shape mismatch between Wq, scale, x and y")
+    st = load_library().gemv_int8(_ptr(Wq, "Wq", (torch.int8,)), _ptr(scale, "scale", (torch.float32,)),
+                                  _ptr(x, "x", _BF16), B, N, K, _ptr(y, "y", (torch.float32,) + _BF16),
+                                  _out_dtype(y), _stream(stream, Wq.device))
+    _check("gemv_int8", st)
+    return y
+
+
+def quantize_rows_int8(W, Wq, scale, stream=None):
+    """Per-row symmetric INT8 codes and fp32 scales of bf16 W [N, K]."""
+    N, K = W.shape
+    if tuple(Wq.shape) != (N, K) or tuple(scale.shape) != (N,):
+        raise ValueError("shape mismatch between W, Wq and scale")
+    st = load_library().quantize_rows_int8(_ptr(W, "W", _BF16), N, K, _ptr(Wq, "Wq", (torch.int8,)),
+                                           _ptr(scale, "scale", (torch.float32,)), _stream(stream, W.device))
+    _check("quantize_rows_int8", st)
 
 
 def attn_partial(q, k_cache, v_cache, lens, scale: float, workspace, causal: bool = False,

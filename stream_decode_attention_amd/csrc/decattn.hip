@@ -15,6 +15,7 @@
 #include <vector>
 
 #include "../../include/decattn.h"
+#include "gemv_kernel.hpp"
 #include "merge_kernel.hpp"
 #include "partial_kernel.hpp"
 #include "prefill_kernel.hpp"
@@ -294,6 +295,80 @@ int check_rope(const decattn_rope* r) {
     return DECATTN_OK;
 }
 
+// ---- weight products (GEMV) ------------------------------------------------
+
+constexpr size_t kGemvLdsBudget = 144 * 1024;   // staged activations per workgroup
+constexpr int kGemvMaxB = 8;
+
+template <int LPR, int B, bool INT8>
+int launch_gemv_b(const GemvParams& gp, size_t lds, hipStream_t s) {
+    const void* fn = reinterpret_cast<const void*>(&gemv_kernel<LPR, B, INT8>);
+    long long grid = resident_blocks(fn, kGemvThreads, lds);
+    if (grid <= 0) return DECATTN_ERR_HIP;
+    const long long groups = ((long long)gp.N + 64 / LPR - 1) / (64 / LPR);
+    const long long need = (groups + kGemvThreads / 64 - 1) / (kGemvThreads / 64);
+    if (grid > need) grid = need;
+    hipLaunchKernelGGL((gemv_kernel<LPR, B, INT8>), dim3((unsigned)grid), dim3(kGemvThreads), lds, s, gp);
+    return hipGetLastError() == hipSuccess ? DECATTN_OK : DECATTN_ERR_HIP;
+}
+
+template <int LPR, bool INT8>
+int launch_gemv_lpr(const GemvParams& gp, int B, size_t lds, hipStream_t s) {
+    switch (B) {
+        case 1: return launch_gemv_b<LPR, 1, INT8>(gp, lds, s);
+        case 2: return launch_gemv_b<LPR, 2, INT8>(gp, lds, s);
+        case 3: return launch_gemv_b<LPR, 3, INT8>(gp, lds, s);
+        case 4: return launch_gemv_b<LPR, 4, INT8>(gp, lds, s);
+        case 5: return launch_gemv_b<LPR, 5, INT8>(gp, lds, s);
+        case 6: return launch_gemv_b<LPR, 6, INT8>(gp, lds, s);
+        case 7: return launch_gemv_b<LPR, 7, INT8>(gp, lds, s);
+        case 8: return launch_gemv_b<LPR, 8, INT8>(gp, lds, s);
+        default: return DECATTN_ERR_UNSUPPORTED;
+    }
+}
+
+// y = x W^T for B vectors, in launches of as many vectors as the LDS budget
+// holds (each launch reads the weights once).
+int gemv_common(const void* W, const float* scale, const void* x, int B, int N, int K, void* y, int out_dtype,
+                bool int8, void* stream) {
+    if (!W || !x || !y || (int8 && !scale)) return DECATTN_ERR_INVALID_ARG;
+    if (B <= 0 || N <= 0 || K <= 0) return DECATTN_ERR_INVALID_ARG;
+    if (B > kGemvMaxB) return DECATTN_ERR_UNSUPPORTED;
+    const int epc = int8 ? 16 : 8;
+    if (K % epc != 0) return DECATTN_ERR_UNSUPPORTED;
+    if (!aligned16(W) || !aligned16(x) || (int8 && (reinterpret_cast<uintptr_t>(scale) & 3u)))
+        return DECATTN_ERR_INVALID_ARG;
+    int st = check_out(y, out_dtype);
+    if (st != DECATTN_OK) return st;
+    if ((long long)N * K > (1LL << 40)) return DECATTN_ERR_UNSUPPORTED;
+    GemvParams gp{};
+    gp.W = W;
+    gp.scale = scale;
+    gp.N = N;
+    gp.K = K;
+    gp.KC = K / epc;
+    const int lpr = gp.KC >= 256 ? 64 : (gp.KC >= 128 ? 32 : 16);
+    gp.KCP = (gp.KC + lpr - 1) / lpr * lpr;
+    gp.xrow = gp.KCP * epc;
+    const size_t per_vec = (size_t)gp.xrow * 2;
+    const int bmax = (int)(kGemvLdsBudget / per_vec);
+    if (bmax < 1) return DECATTN_ERR_UNSUPPORTED;          // one activation row does not fit in LDS
+    gp.out_bf16 = out_dtype == DECATTN_OUT_BF16;
+    const size_t osz = gp.out_bf16 ? 2 : 4;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int b0 = 0; b0 < B; b0 += bmax) {
+        const int nb = B - b0 < bmax ? B - b0 : bmax;
+        gp.x = static_cast<const uint16_t*>(x) + (size_t)b0 * K;
+        gp.y = static_cast<char*>(y) + (size_t)b0 * N * osz;
+        const size_t lds = (size_t)nb * per_vec;
+        if (lpr == 64) st = int8 ? launch_gemv_lpr<64, true>(gp, nb, lds, s) : launch_gemv_lpr<64, false>(gp, nb, lds, s);
+        else if (lpr == 32) st = int8 ? launch_gemv_lpr<32, true>(gp, nb, lds, s) : launch_gemv_lpr<32, false>(gp, nb, lds, s);
+        else st = int8 ? launch_gemv_lpr<16, true>(gp, nb, lds, s) : launch_gemv_lpr<16, false>(gp, nb, lds, s);
+        if (st != DECATTN_OK) return st;
+    }
+    return DECATTN_OK;
+}
+
 }  // namespace
 }  // namespace decattn
 
@@ -465,6 +540,31 @@ int rope_kv_write(const void* q_in, const void* k_in, const void* v_in, const in
         if (adj) hipLaunchKernelGGL((rope_kv_write_kernel<128, true>), grid, block, 0, s, rp);
         else hipLaunchKernelGGL((rope_kv_write_kernel<128, false>), grid, block, 0, s, rp);
     }
+    return hipGetLastError() == hipSuccess ? DECATTN_OK : DECATTN_ERR_HIP;
+}
+
+int gemv_bf16(const void* W, const void* x, int B, int N, int K, void* y, int out_dtype, void* stream) {
+    return gemv_common(W, nullptr, x, B, N, K, y, out_dtype, false, stream);
+}
+
+int gemv_int8(const void* Wq, const float* scale, const void* x, int B, int N, int K, void* y, int out_dtype,
+              void* stream) {
+    return gemv_common(Wq, scale, x, B, N, K, y, out_dtype, true, stream);
+}
+
+int quantize_rows_int8(const void* W, int N, int K, void* Wq, float* scale, void* stream) {
+    if (!W || !Wq || !scale) return DECATTN_ERR_INVALID_ARG;
+    if (N <= 0 || K <= 0) return DECATTN_ERR_INVALID_ARG;
+    if (K % 16 != 0) return DECATTN_ERR_UNSUPPORTED;
+    if (!aligned16(W) || !aligned16(Wq) || (reinterpret_cast<uintptr_t>(scale) & 3u)) return DECATTN_ERR_INVALID_ARG;
+    const size_t wb = (size_t)N * K * 2, qb = (size_t)N * K, sb = (size_t)N * 4;
+    if (overlaps(W, wb, Wq, qb) || overlaps(W, wb, scale, sb) || overlaps(Wq, qb, scale, sb))
+        return DECATTN_ERR_INVALID_ARG;
+    const long long blocks = ((long long)N + kQuantThreads / 64 - 1) / (kQuantThreads / 64);
+    if (blocks > 0x7FFFFFFF) return DECATTN_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(quantize_rows_int8_kernel, dim3((unsigned)blocks), dim3(kQuantThreads), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(W), N, K,
+                       static_cast<int8_t*>(Wq), scale);
     return hipGetLastError() == hipSuccess ? DECATTN_OK : DECATTN_ERR_HIP;
 }
 

@@ -1,0 +1,207 @@
+// The weight products of a decode step: y[b, n] = sum_k W[n, k] x[b, k] for
+// a few activation vectors (B <= 8), W row-major [N][K] in bf16 or as INT8
+// with one fp32 scale per output row (llm-decode-cuda: roofline paragraph,
+// GEMV table and INT8 section). Every weight is read once per call and used
+// for 2*B flops, so the kernel is bound by HBM bytes.
+//
+// A group of LPR lanes (16, 32 or 64, chosen from K) owns one output row at a
+// time; each lane reads 16-byte chunks c = lane_in_group + LPR*i of the row
+// (8 bf16 or 16 INT8 weights), eight chunks in flight before any is used. The
+// activations are staged once per workgroup in LDS (zero-padded to whole
+// chunk rounds, so the tail needs no branch) and read back as 16-byte pieces
+// that line up with the lane's chunks. Products accumulate in fp32 with
+// v_dot2c_f32_bf16; INT8 weights are widened once per chunk to bf16 pairs
+// (exact for |q| <= 127) and reused for all B vectors, so a larger batch adds
+// only the dot products (the fix the INT8 section names for its batch-4
+// slowdown). Row sums are joined across the group with DPP and lane swaps;
+// the group's first lane applies the row scale and stores y. The grid is
+// persistent: every wave walks row groups wave, wave + all waves, ...
+#pragma once
+
+#include "device_common.hpp"
+
+namespace decattn {
+
+struct GemvParams {
+    const void* W;            // bf16 [N][K] or int8 [N][K]
+    const float* scale;       // [N], INT8 weights only
+    const uint16_t* x;        // bf16 [B][K]
+    void* y;                  // [B][N], fp32 or bf16
+    int out_bf16;
+    int N, K;
+    int KC;                   // 16-byte chunks per weight row
+    int KCP;                  // chunks per row padded to a multiple of LPR
+    int xrow;                 // bf16 elements per staged activation row in LDS
+};
+
+constexpr int kGemvThreads = 512;
+constexpr int kGemvUnroll = 8;        // chunks per lane in flight
+
+template <int LPR>
+__device__ __forceinline__ float gemv_group_sum(float v) {
+    static_assert(LPR == 16 || LPR == 32 || LPR == 64, "16, 32 or 64 lanes per row");
+    v = group_sum<16>(v);
+    if constexpr (LPR >= 32) {
+        const f32x2 a = swap16(v, v);           // [r0, r0, r2, r2] and [r1, r1, r3, r3]
+        v = a.x + a.y;
+    }
+    if constexpr (LPR == 64) {
+        const f32x2 a = swap32(v, v);
+        v = a.x + a.y;
+    }
+    return v;
+}
+
+// INT8 weights: 16 codes in a uint4 -> eight packed bf16 pairs (exact)
+__device__ __forceinline__ uint32_t int8x2_to_bf16x2(uint32_t w, int shift) {
+    const float lo = (float)(int)(int8_t)(w >> shift);
+    const float hi = (float)(int)(int8_t)(w >> (shift + 8));
+    return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);   // exact: |q| <= 127
+}
+
+template <int LPR, int B, bool INT8>
+__global__ void __launch_bounds__(kGemvThreads)
+gemv_kernel(const GemvParams p) {
+    constexpr int RPW = 64 / LPR;                   // rows per wave at a time
+    constexpr int EPC = INT8 ? 16 : 8;              // weights per chunk
+    extern __shared__ __align__(16) uint16_t xs[];  // [B][xrow]
+
+    // stage x (zero-padded to KCP chunks)
+    const int xelems = p.KCP * EPC;
+    for (int b = 0; b < B; ++b) {
+        for (int e = threadIdx.x * 8; e < xelems; e += kGemvThreads * 8) {
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (e < p.K) v = *reinterpret_cast<const uint4*>(p.x + (size_t)b * p.K + e);
+            *reinterpret_cast<uint4*>(xs + b * p.xrow + e) = v;
+        }
+    }
+    __syncthreads();
+
+    const int lane = threadIdx.x & 63;
+    const int sub = lane % LPR;
+    const int grp = lane / LPR;
+    const int waves_total = (int)gridDim.x * (kGemvThreads / 64);
+    const int wave_id = (int)blockIdx.x * (kGemvThreads / 64) + (int)(threadIdx.x >> 6);
+    const int groups = (p.N + RPW - 1) / RPW;
+    const size_t row_bytes = (size_t)p.KC * 16;
+    const char* wbase = static_cast<const char*>(p.W);
+
+    for (int g = wave_id; g < groups; g += waves_total) {
+        const int row = g * RPW + grp;
+        const bool row_ok = row < p.N;
+        const char* wrow = wbase + (size_t)(row_ok ? row : 0) * row_bytes;
+        float acc[B];
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[b] = 0.f;
+
+        for (int c0 = 0; c0 < p.KCP; c0 += LPR * kGemvUnroll) {
+            uint4 w[kGemvUnroll];
+#pragma unroll
+            for (int u = 0; u < kGemvUnroll; ++u) {
+                const int c = c0 + u * LPR + sub;
+                // chunks past the row (the padded tail) are zeros: no read
+                w[u] = (c < p.KC) ? *reinterpret_cast<const uint4*>(wrow + (size_t)c * 16) : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int u = 0; u < kGemvUnroll; ++u) {
+                if (c0 + u * LPR >= p.KCP) break;           // uniform: past the padded row
+                const int c = c0 + u * LPR + sub;
+                if constexpr (!INT8) {
+#pragma unroll
+                    for (int b = 0; b < B; ++b) {
+                        const uint4 xv = *reinterpret_cast<const uint4*>(xs + b * p.xrow + c * 8);
+                        float a = acc[b];
+                        a = dot2_bf16(w[u].x, xv.x, a);
+                        a = dot2_bf16(w[u].y, xv.y, a);
+                        a = dot2_bf16(w[u].z, xv.z, a);
+                        a = dot2_bf16(w[u].w, xv.w, a);
+                        acc[b] = a;
+                    }
+                } else {
+                    const uint32_t wd[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+                    uint32_t wb[8];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        wb[2 * i] = int8x2_to_bf16x2(wd[i], 0);
+                        wb[2 * i + 1] = int8x2_to_bf16x2(wd[i], 16);
+                    }
+#pragma unroll
+                    for (int b = 0; b < B; ++b) {
+                        const uint4 x0 = *reinterpret_cast<const uint4*>(xs + b * p.xrow + c * 16);
+                        const uint4 x1 = *reinterpret_cast<const uint4*>(xs + b * p.xrow + c * 16 + 8);
+                        float a = acc[b];
+                        a = dot2_bf16(wb[0], x0.x, a);
+                        a = dot2_bf16(wb[1], x0.y, a);
+                        a = dot2_bf16(wb[2], x0.z, a);
+                        a = dot2_bf16(wb[3], x0.w, a);
+                        a = dot2_bf16(wb[4], x1.x, a);
+                        a = dot2_bf16(wb[5], x1.y, a);
+                        a = dot2_bf16(wb[6], x1.z, a);
+                        a = dot2_bf16(wb[7], x1.w, a);
+                        acc[b] = a;
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[b] = gemv_group_sum<LPR>(acc[b]);
+        if (sub == 0 && row_ok) {
+            const float sc = INT8 ? p.scale[row] : 1.f;
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                const float v = INT8 ? acc[b] * sc : acc[b];
+                const size_t o = (size_t)b * p.N + row;
+                if (p.out_bf16) reinterpret_cast<uint16_t*>(p.y)[o] = f32_to_bf16_rne(v);
+                else reinterpret_cast<float*>(p.y)[o] = v;
+            }
+        }
+    }
+}
+
+// Per-output-row symmetric INT8 quantization, in fp32: a = max |w|,
+// s = a / 127, q = round-half-even(w / s) kept in [-127, 127]; a row of zeros
+// gets s = 0 and q = 0 (llm-decode-cuda, INT8 section: one fp32 scale per
+// output channel, symmetric, quantized when the weights are loaded). One
+// wave per row, two passes over it.
+constexpr int kQuantThreads = 256;
+
+__global__ void __launch_bounds__(kQuantThreads)
+quantize_rows_int8_kernel(const uint16_t* __restrict__ W, int N, int K, int8_t* __restrict__ Wq,
+                          float* __restrict__ scale) {
+    const int lane = threadIdx.x & 63;
+    const int row = (int)blockIdx.x * (kQuantThreads / 64) + (int)(threadIdx.x >> 6);
+    if (row >= N) return;
+    const uint16_t* w = W + (size_t)row * K;
+    float a = 0.f;
+    for (int e = lane * 8; e < K; e += 64 * 8) {
+        float f[8];
+        bf16x8_to_f32(*reinterpret_cast<const uint4*>(w + e), f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(f[i]));
+    }
+    // max is exact in any order
+    a = fmaxf(a, dpp_move<kDppXor1>(a));
+    a = fmaxf(a, dpp_move<kDppXor2>(a));
+    a = fmaxf(a, dpp_move<kDppHalfMirror>(a));
+    a = fmaxf(a, dpp_move<kDppMirror>(a));
+    a = across_groups_max<16>(a);
+    const float s = a / 127.f;                       // correctly rounded fp32 division
+    if (lane == 0) scale[row] = a > 0.f ? s : 0.f;
+    int8_t* q = Wq + (size_t)row * K;
+    for (int e = lane * 8; e < K; e += 64 * 8) {
+        float f[8];
+        bf16x8_to_f32(*reinterpret_cast<const uint4*>(w + e), f);
+        uint32_t packed[2] = {0u, 0u};
+        if (a > 0.f) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                float r = rintf(f[i] / s);              // fp32 quotient, ties to even
+                r = fminf(fmaxf(r, -127.f), 127.f);
+                packed[i >> 2] |= ((uint32_t)(int)r & 0xFFu) << (8 * (i & 3));
+            }
+        }
+        *reinterpret_cast<uint2*>(q + e) = make_uint2(packed[0], packed[1]);
+    }
+}
+
+}  // namespace decattn

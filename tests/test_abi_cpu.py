@@ -34,7 +34,8 @@ def test_header_declares_the_boundary():
     names = set(declared_functions())
     assert {"decode_attn", "chunk_attn", "attn_partial", "attn_merge", "decattn_workspace_bytes",
             "decattn_default_chunk", "decattn_status_str", "decattn_abi_version",
-            "decattn_probe_read", "decattn_probe_copy", "rope_kv_write", "prefill_attn"} <= names
+            "decattn_probe_read", "decattn_probe_copy", "rope_kv_write", "prefill_attn",
+            "gemv_bf16", "gemv_int8", "quantize_rows_int8"} <= names
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -188,3 +189,20 @@ def _prefill(lib, **kw):
 ])
 def test_prefill_rejects_bad_arguments(lib, kw, status):
     assert _prefill(lib, **kw) == status
+
+
+def test_gemv_entry_points_reject_bad_arguments(lib):
+    W, X, Y, S = 0x1000000, 0x2000000, 0x3000000, 0x4000000
+    g = lambda **kw: lib.gemv_bf16(kw.get("W", W), kw.get("x", X), kw.get("B", 2), kw.get("N", 64), kw.get("K", 256),
+                                   kw.get("y", Y), kw.get("od", 1), None)
+    for kw, st in [(dict(W=None), 1), (dict(x=None), 1), (dict(y=None), 1), (dict(B=0), 1), (dict(N=0), 1),
+                   (dict(K=0), 1), (dict(B=9), 2), (dict(K=100), 2), (dict(W=W + 8), 1), (dict(x=X + 2), 1),
+                   (dict(y=Y + 4), 1), (dict(od=5), 1), (dict(K=1 << 20), 2)]:
+        assert g(**kw) == st, kw
+    q = lambda **kw: lib.gemv_int8(kw.get("W", W), kw.get("s", S), X, 1, 64, kw.get("K", 256), Y, 1, None)
+    assert q(s=None) == 1 and q(K=264) == 2 and q(s=S + 2) == 1
+    z = lambda **kw: lib.quantize_rows_int8(kw.get("W", W), kw.get("N", 64), kw.get("K", 256), kw.get("q", X),
+                                            kw.get("s", S), None)
+    for kw, st in [(dict(W=None), 1), (dict(q=None), 1), (dict(s=None), 1), (dict(N=0), 1), (dict(K=24), 2),
+                   (dict(q=W + 64), 1), (dict(s=W + 16), 1), (dict(q=X + 8), 1)]:
+        assert z(**kw) == st, kw

@@ -1,0 +1,176 @@
+"""HIP GEMV (bf16 and INT8 weight-only) and the INT8 quantizer vs the fp64
+oracle on the same seeded bytes, through the C ABI.
+
+Two checks for each product:
+  * small-integer data (weights and activations in {-3..3}, codes in
+    {-127..127} with power-of-two scales): every product and partial sum is
+    an integer the fp32 accumulator holds exactly, so the GPU must equal the
+    oracle bit for bit -- a dropped, repeated or misplaced term cannot hide;
+  * N(0,1) data: |y_gpu - y| <= a worst-case fp32 bound derived from the
+    kernel's summation (per lane at most 8 * ceil(K / 8 / 16) roundings in
+    its chain of dot2 steps, the 16/32/64-lane tree, the row scale):
+    (8 * ceil(K / 128) + 8) * 2^-24 * sum_k |W x|, and for bf16 output the
+    result rounded to one of the bf16 values bracketing that interval.
+The quantizer is compared bit for bit (codes and scales), both sides taking
+the integer decisions in fp32.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import stream_decode_attention_amd as sda
+import workloads
+from oracle.bf16 import bf16_bracket
+from tests.gpu_util import bits_of, dev_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def _f32(bits):
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _small_int_bits(shape, seed, lo=-3, hi=3):
+    v = np.random.default_rng(seed).integers(lo, hi + 1, size=shape).astype(np.float32)
+    return (v.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def _bound(Wf, xf):
+    K = Wf.shape[1]
+    steps = 8 * -(-K // 128) + 8
+    return steps * 2.0 ** -24 * (np.abs(xf.astype(np.float64)) @ np.abs(Wf.astype(np.float64)).T)
+
+
+def _check_f32(out, ref, bound):
+    got = out.cpu().double().numpy()
+    err = np.abs(got - ref)
+    assert np.all(np.isfinite(got))
+    assert np.all(err <= bound), f"max err {err.max():.3e}, worst ratio {(err / np.maximum(bound, 1e-300)).max():.2f}"
+
+
+def _check_bf16(out, ref, bound):
+    bits = bits_of(out)
+    lo, _ = bf16_bracket(ref - bound)
+    _, hi = bf16_bracket(ref + bound)
+    got = _f32(bits).astype(np.float64)
+    assert np.all((got >= _f32(lo)) & (got <= _f32(hi)))
+
+
+SHAPES = [
+    # B, N, K   (lanes per row: K/8 chunks >= 256 -> 64, >= 128 -> 32, else 16)
+    (1, 1600, 960),       # SmolLM2-360M fused q/k/v, 16 lanes per row
+    (3, 960, 2560),       # SmolLM2 down projection, 64 lanes
+    (8, 77, 1024),        # 32 lanes, ragged row count
+    (2, 5, 968),          # 121 chunks: a partial round of the 16-lane group
+    (8, 256, 14336),      # Llama-3-8B down-projection width: two launches of <= 5 vectors
+    (1, 1, 64),
+]
+
+
+@pytest.mark.parametrize("B,N,K", SHAPES)
+def test_gemv_bf16_integer_data_is_exact(B, N, K):
+    W = _small_int_bits((N, K), 700 + K)
+    x = _small_int_bits((B, K), 701 + N)
+    ref = oracle.gemv(W, x)
+    y = torch.empty((B, N), dtype=torch.float32, device="cuda")
+    sda.gemv_bf16(dev_bits(W), dev_bits(x), y)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().double().numpy(), ref)
+
+
+@pytest.mark.parametrize("B,N,K", SHAPES)
+def test_gemv_bf16_random_data_within_bound(B, N, K):
+    W = workloads.bf16_randn((N, K), 710 + K)
+    x = workloads.bf16_randn((B, K), 711 + N)
+    ref = oracle.gemv(W, x)
+    bound = _bound(_f32(W), _f32(x))
+    dW, dx = dev_bits(W), dev_bits(x)
+    y32 = torch.empty((B, N), dtype=torch.float32, device="cuda")
+    y16 = torch.empty((B, N), dtype=torch.bfloat16, device="cuda")
+    sda.gemv_bf16(dW, dx, y32)
+    sda.gemv_bf16(dW, dx, y16)
+    torch.cuda.synchronize()
+    _check_f32(y32, ref, bound)
+    _check_bf16(y16, ref, bound)
+
+
+@pytest.mark.parametrize("N,K", [(1600, 960), (960, 2560), (33, 4096), (4, 16)])
+def test_quantize_rows_matches_oracle_bit_for_bit(N, K):
+    W = workloads.bf16_randn((N, K), 720 + K)
+    W[min(2, N - 1)] = 0                                   # a row of zeros
+    if N > 3:
+        W[3] = 0
+        W[3, K // 2] = 0xBF80                              # a row with a single -1.0
+    q_ref, s_ref = oracle.quantize_rows_int8(W)
+    dq = torch.empty((N, K), dtype=torch.int8, device="cuda")
+    ds = torch.empty((N,), dtype=torch.float32, device="cuda")
+    sda.quantize_rows_int8(dev_bits(W), dq, ds)
+    torch.cuda.synchronize()
+    assert np.array_equal(dq.cpu().numpy(), q_ref)
+    assert np.array_equal(ds.cpu().numpy(), s_ref)
+
+
+def _codes(shape, seed):
+    return np.random.default_rng(seed).integers(-127, 128, size=shape).astype(np.int8)
+
+
+@pytest.mark.parametrize("B,N,K", [(1, 1600, 960), (4, 960, 2560), (8, 77, 1024), (8, 64, 14336), (2, 3, 16)])
+def test_gemv_int8_integer_data_is_exact(B, N, K):
+    q = _codes((N, K), 730 + K)
+    s = (2.0 ** np.random.default_rng(731).integers(-8, 1, size=N)).astype(np.float32)
+    x = _small_int_bits((B, K), 732 + N)
+    ref = oracle.gemv_int8(q, s, x)
+    y = torch.empty((B, N), dtype=torch.float32, device="cuda")
+    sda.gemv_int8(torch.from_numpy(q).cuda(), torch.from_numpy(s).cuda(), dev_bits(x), y)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().double().numpy(), ref)
+
+
+@pytest.mark.parametrize("B,N,K", [(1, 1600, 960), (4, 960, 2560), (8, 256, 14336)])
+def test_quantize_then_gemv_int8_random_data(B, N, K):
+    """The load-time quantizer feeding the INT8 product, as a model would use
+    them: codes and scales from the GPU (equal to the oracle's), product
+    within the fp32 bound of the oracle's INT8 product."""
+    W = workloads.bf16_randn((N, K), 740 + K)
+    x = workloads.bf16_randn((B, K), 741 + N)
+    dq = torch.empty((N, K), dtype=torch.int8, device="cuda")
+    ds = torch.empty((N,), dtype=torch.float32, device="cuda")
+    sda.quantize_rows_int8(dev_bits(W), dq, ds)
+    y32 = torch.empty((B, N), dtype=torch.float32, device="cuda")
+    y16 = torch.empty((B, N), dtype=torch.bfloat16, device="cuda")
+    dx = dev_bits(x)
+    sda.gemv_int8(dq, ds, dx, y32)
+    sda.gemv_int8(dq, ds, dx, y16)
+    torch.cuda.synchronize()
+    q, s = oracle.quantize_rows_int8(W)
+    assert np.array_equal(dq.cpu().numpy(), q) and np.array_equal(ds.cpu().numpy(), s)
+    ref = oracle.gemv_int8(q, s, x)
+    bound = _bound(q.astype(np.float32) * s[:, None], _f32(x))
+    _check_f32(y32, ref, bound)
+    _check_bf16(y16, ref, bound)
+
+
+def test_gemv_graph_replay_with_new_activations():
+    N, K, B = 512, 2048, 4
+    W = workloads.bf16_randn((N, K), 750)
+    dW = dev_bits(W)
+    x = torch.empty((B, K), dtype=torch.int16, device="cuda")
+    y = torch.empty((B, N), dtype=torch.float32, device="cuda")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        x.copy_(dev_bits(workloads.bf16_randn((B, K), 751)))
+        sda.gemv_bf16(dW, x, y, stream=s)
+        s.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            sda.gemv_bf16(dW, x, y, stream=s)
+    for t in range(3):
+        xt = workloads.bf16_randn((B, K), 760 + t)
+        with torch.cuda.stream(s):
+            x.copy_(dev_bits(xt))
+            g.replay()
+        s.synchronize()
+        _check_f32(y, oracle.gemv(W, xt), _bound(_f32(W), _f32(xt)))
