@@ -318,6 +318,10 @@ def main():
     if not args.headline_only:
         result["prefill_attn"] = prefill_runs(up, sda, workloads, np, torch, stream, flush)
 
+    # ----------------------------------------------- weight products (GEMV)
+    if not args.headline_only:
+        result["gemv"] = gemv_runs(sda, np, torch, stream, flush)
+
     # ------------------------------------------------------- other workloads
     if not args.headline_only:
         result["workloads"] = other_workloads(args, dev, up, sda, workloads, rf, np, torch, stream, flush)
@@ -442,6 +446,65 @@ def prefill_runs(up, sda, workloads, np, torch, stream, flush):
             f"({entry['bf16_out']['TFLOPs']:.0f} TFLOP/s), fp32 out {entry['f32_out']['us_per_call']:.1f} us "
             f"({entry['f32_out']['TFLOPs']:.0f} TFLOP/s)")
         res.append(entry)
+    return res
+
+
+GEMV_MODELS = {
+    # one decoder layer's weight products, fused as the pages' engine does:
+    # q/k/v, o, gate/up, down ([N, K] row-major)
+    "llama3-8b-layer": ([(6144, 4096), (4096, 4096), (28672, 4096), (4096, 14336)], 3),
+    "smollm2-360m-32-layers": ([(1600, 960), (960, 960), (5120, 960), (960, 2560)], 32),
+}
+
+
+def gemv_runs(sda, np, torch, stream, flush):
+    """Weight products of decode steps: every layer's four matrices in one
+    graph (layer copies rotate, so each matrix was last read hundreds of MB
+    earlier), bf16 and INT8 weight-only, B = 1 and 8, GB/s of weight bytes
+    read (INT8: codes and scales) against the 8 TB/s HBM peak."""
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(800)
+    res = []
+    for name, (mats, nl) in GEMV_MODELS.items():
+        layers = [[torch.randn(m, generator=g, device=dev).to(torch.bfloat16) for m in mats] for _ in range(nl)]
+        qlayers = []
+        for L in layers:
+            ql = []
+            for W in L:
+                q = torch.empty(W.shape, dtype=torch.int8, device=dev)
+                sc = torch.empty(W.shape[0], dtype=torch.float32, device=dev)
+                sda.quantize_rows_int8(W, q, sc)
+                ql.append((q, sc))
+            qlayers.append(ql)
+        torch.cuda.synchronize()
+        entry = {"workload": name, "matrices_NxK": [list(m) for m in mats], "layers_in_graph": nl}
+        for int8 in (False, True):
+            for B in (1, 8):
+                xs = {K: torch.randn((B, K), generator=g, device=dev).to(torch.bfloat16) for _, K in mats}
+                ys = [torch.empty((B, N), dtype=torch.bfloat16, device=dev) for N, _ in mats]
+
+                def step(l, int8=int8, xs=xs, ys=ys):
+                    for i, (N, K) in enumerate(mats):
+                        if int8:
+                            sda.gemv_int8(qlayers[l][i][0], qlayers[l][i][1], xs[K], ys[i], stream=stream)
+                        else:
+                            sda.gemv_bf16(layers[l][i], xs[K], ys[i], stream=stream)
+                with torch.cuda.stream(stream):
+                    step(0)
+                    stream.synchronize()
+                gr = graph_of(torch, stream, [lambda l=l: step(l) for l in range(nl)])
+                us = float(np.median([back_to_back_us(torch, stream, [gr], 1, 1, busy=flush) for _ in range(5)]))
+                wbytes = nl * sum(N * K * (1 if int8 else 2) + (4 * N if int8 else 0) for N, K in mats)
+                gbps = wbytes / us / 1e3
+                entry[f"{'int8' if int8 else 'bf16'}_B{B}"] = {
+                    "us_per_graph": round(us, 1), "launches": 4 * nl, "weight_bytes": wbytes,
+                    "GBps": round(gbps, 1), "frac_of_hbm_peak": round(gbps / 8000.0, 4)}
+                log(f"gemv {name} {'int8' if int8 else 'bf16'} B={B}: {us:.1f} us for {4 * nl} products, "
+                    f"{gbps:.0f} GB/s of weights")
+                del gr
+        res.append(entry)
+        del layers, qlayers
     return res
 
 

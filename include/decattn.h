@@ -144,7 +144,8 @@ int prefill_attn(const void* q, const void* k_cache, const void* v_cache,
  * Products accumulate in fp32. K must be a multiple of 8 (bf16) or 16 (int8);
  * B in 1..8 (vectors beyond what 144 KB of LDS holds at this K go to further
  * launches, each reading the weights again). One launch per group, no host
- * sync, capturable. W, Wq, x, y 16-byte aligned; scale 4-byte aligned. */
+ * sync, capturable. W, Wq, x, y 16-byte aligned; scale 4-byte aligned;
+ * (N + 64) * K weight bytes below 2^32. */
 int gemv_bf16(const void* W, const void* x, int B, int N, int K,
               void* y, int out_dtype, void* stream);
 int gemv_int8(const void* Wq, const float* scale, const void* x, int B, int N, int K,

@@ -305,7 +305,8 @@ int launch_gemv_b(const GemvParams& gp, size_t lds, hipStream_t s) {
     const void* fn = reinterpret_cast<const void*>(&gemv_kernel<LPR, B, INT8>);
     long long grid = resident_blocks(fn, kGemvThreads, lds);
     if (grid <= 0) return DECATTN_ERR_HIP;
-    const long long groups = ((long long)gp.N + 64 / LPR - 1) / (64 / LPR);
+    const long long rows_per_wave = (64 / LPR) * gemv_rows_per_group<B, INT8>();
+    const long long groups = ((long long)gp.N + rows_per_wave - 1) / rows_per_wave;
     const long long need = (groups + kGemvThreads / 64 - 1) / (kGemvThreads / 64);
     if (grid > need) grid = need;
     hipLaunchKernelGGL((gemv_kernel<LPR, B, INT8>), dim3((unsigned)grid), dim3(kGemvThreads), lds, s, gp);
@@ -340,7 +341,9 @@ int gemv_common(const void* W, const float* scale, const void* x, int B, int N, 
         return DECATTN_ERR_INVALID_ARG;
     int st = check_out(y, out_dtype);
     if (st != DECATTN_OK) return st;
-    if ((long long)N * K > (1LL << 40)) return DECATTN_ERR_UNSUPPORTED;
+    // one buffer resource spans W: its bytes, plus the rows of the last
+    // group past N, must stay below 2^32
+    if ((long long)(N + 64) * K * (int8 ? 1 : 2) >= (1LL << 32)) return DECATTN_ERR_UNSUPPORTED;
     GemvParams gp{};
     gp.W = W;
     gp.scale = scale;
