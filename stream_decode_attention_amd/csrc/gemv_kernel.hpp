@@ -124,6 +124,9 @@ gemv_kernel(const GemvParams p) {
             uint4 w[RB][U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
+                // rounds past the padded row are not loaded (uniform test):
+                // they would read the next rows again
+                if (c0 + u * LPR >= p.KCP) break;
                 const int c = c0 + u * LPR + sub;
 #pragma unroll
                 for (int r = 0; r < RB; ++r) {
