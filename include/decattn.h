@@ -159,6 +159,45 @@ int gemv_int8(const void* Wq, const float* scale, const void* x, int B, int N, i
  * the three buffers must not overlap. */
 int quantize_rows_int8(const void* W, int N, int K, void* Wq, float* scale, void* stream);
 
+/* The accept/reject step of speculative decoding after the verify pass, with
+ * the rollback of the cache lengths, on the device (tinydecode README,
+ * "speculative decoding"; the FlashSpec page's correctness paragraph, which
+ * restates Leviathan et al. 2023, Algorithm 1). Per row b, gamma = T - 1:
+ *   p_i = softmax(logits[b][i] / tau) for the T verified positions (position
+ *   i scores the token after draft i-1; position gamma is the bonus row);
+ *   draft i is kept while log u_i < log p_i(d_i) - log q_i(d_i) (log 0 = -inf,
+ *   so u_i = 0 or q_i(d_i) = 0 keeps it; an id outside [0, V) is rejected);
+ *   n = the number kept before the first rejection;
+ *   the next token is drawn with r[b] by inverse CDF in vocabulary order from
+ *   max(0, p_n - q_n) (n < gamma; from p_n if that has no positive mass) or
+ *   from p_gamma (n = gamma): the first index k with positive weight whose
+ *   running sum exceeds r * total (the last positive index if rounding leaves
+ *   none);
+ *   tau == 0 is greedy: draft i is kept while it equals argmax logits[b][i]
+ *   (first index on ties) and the next token is argmax logits[b][n];
+ *   lens[b] <- min(clamp(lens[b], 0, S_max) + n + 1, S_max): the pending token
+ *   and the kept drafts stay in the cache, entries past the new length are
+ *   stale and never read; the next token is the next pending one.
+ *   logits   fp32 [B][T][V], finite or -inf, at least one finite per row
+ *   q        fp32 [B][T-1][V]: the draft distributions the drafts came from
+ *            (sampling only; NULL allowed when tau == 0 or T == 1)
+ *   drafts   int32 [B][T-1] (NULL allowed when T == 1)
+ *   u        fp32 [B][T-1] uniforms in [0, 1); r fp32 [B] uniforms in [0, 1)
+ *            (sampling only; NULL allowed when tau == 0, u also when T == 1)
+ *   tau      0 (greedy) or a positive temperature with log2(e)/tau finite
+ *   lens     int32 [B], device, read and written: the length before the verify
+ *            pass (ctx_lens of chunk_attn)
+ *   result   int32 [B][2]: {n, next token}, one device-to-host read per step
+ *   workspace >= spec_accept_workspace_bytes(B, T, V) bytes, 16-byte aligned;
+ *            overwritten; calls that share it must be ordered on one stream
+ * T in 1..32, V in 1..2^24. lens, result and workspace must not overlap each
+ * other or the inputs (checked). Two launches on `stream`, no host sync,
+ * capturable. */
+size_t spec_accept_workspace_bytes(int B, int T, int V);
+int spec_accept(const float* logits, const float* q, const int32_t* drafts, const float* u, const float* r,
+                float tau, int B, int T, int V, int S_max, int32_t* lens, int32_t* result,
+                void* workspace, size_t workspace_bytes, void* stream);
+
 /* The two phases of decode_attn / chunk_attn as separate launches, for callers
  * that time them apart or merge partial state produced elsewhere.
  * `causal` = 0 gives decode (T must be 1, lens = seq_lens); 1 gives chunk

@@ -141,7 +141,8 @@ def accept_reject(logits, q, drafts, u, r, tau: float, ctx_lens, S_max: int, tra
     """Every row of the step (S1-S6).
 
     logits float32 [B][T][V]; q float32 [B][T-1][V]; drafts int [B][T-1];
-    u float32 [B][T-1]; r float32 [B]; ctx_lens int [B].
+    u float32 [B][T-1]; r float32 [B]; ctx_lens int [B]; q, u and r may be
+    None when tau == 0.
     Returns (n_kept int32 [B], next_token int32 [B], new_lens int32 [B]).
     `traces`, if a list, receives one trace dict per row.
     """
@@ -152,7 +153,8 @@ def accept_reject(logits, q, drafts, u, r, tau: float, ctx_lens, S_max: int, tra
     lens = np.zeros(B, dtype=np.int32)
     for b in range(B):
         tr = {} if traces is not None else None
-        n, k = accept_reject_row(logits[b], q[b], drafts[b], u[b], float(r[b]), float(tau), tr)
+        n, k = accept_reject_row(logits[b], None if q is None else q[b], drafts[b],
+                                 None if u is None else u[b], 0.0 if r is None else float(r[b]), float(tau), tr)
         n_acc[b], nxt[b] = n, k
         lens[b] = new_length(ctx_lens[b], n, S_max)
         if traces is not None:

@@ -17,7 +17,8 @@ __all__ = [
     "DecattnError", "load_library", "abi_version", "status_str", "default_chunk",
     "workspace_bytes", "decode_attn", "chunk_attn", "attn_partial", "attn_merge",
     "probe_read", "probe_copy", "rope_kv_write", "RopeParams", "prefill_attn",
-    "gemv_bf16", "gemv_int8", "quantize_rows_int8", "OUT_BF16", "OUT_F32", "LIB_PATH",
+    "gemv_bf16", "gemv_int8", "quantize_rows_int8", "spec_accept", "spec_accept_workspace_bytes",
+    "OUT_BF16", "OUT_F32", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdecattn.so")
@@ -51,6 +52,8 @@ _SIGNATURES = {
     "attn_merge": ([_vp, _i, _i, _i, _i, _i, _i, _i, _vp, _i, _vp, _sz, _i, _vp], _i),
     "rope_kv_write": ([_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, ctypes.POINTER(RopeParams), _vp, _vp, _vp,
                        _vp], _i),
+    "spec_accept_workspace_bytes": ([_i, _i, _i], _sz),
+    "spec_accept": ([_vp, _vp, _vp, _vp, _vp, _f, _i, _i, _i, _i, _vp, _vp, _vp, _sz, _vp], _i),
     "decattn_probe_read": ([_vp, _sz, _vp, _vp], _i),
     "decattn_probe_copy": ([_vp, _vp, _sz, _vp], _i),
 }
@@ -226,6 +229,40 @@ def quantize_rows_int8(W, Wq, scale, stream=None):
     st = load_library().quantize_rows_int8(_ptr(W, "W", _BF16), N, K, _ptr(Wq, "Wq", (torch.int8,)),
                                            _ptr(scale, "scale", (torch.float32,)), _stream(stream, W.device))
     _check("quantize_rows_int8", st)
+
+
+def spec_accept_workspace_bytes(B: int, T: int, V: int) -> int:
+    return load_library().spec_accept_workspace_bytes(B, T, V)
+
+
+def _opt_ptr(t, name, dtypes) -> Optional[int]:
+    return None if t is None else _ptr(t, name, dtypes)
+
+
+def spec_accept(logits, q, drafts, u, r, tau: float, lens, result, workspace, S_max: int, stream=None):
+    """Accept/reject of speculative drafts and rollback of ``lens``, on the device.
+
+    logits fp32 [B,T,V]; q fp32 [B,T-1,V] (None when tau == 0); drafts int32
+    [B,T-1]; u fp32 [B,T-1] and r fp32 [B] (None when tau == 0); lens int32 [B]
+    (read and written); result int32 [B,2] receives (accepted drafts, next
+    token); workspace uint8 of at least spec_accept_workspace_bytes(B, T, V).
+    See include/decattn.h.
+    """
+    B, T, V = logits.shape
+    G = T - 1
+    if tuple(lens.shape) != (B,) or tuple(result.shape) != (B, 2):
+        raise ValueError("lens must be [B] and result [B, 2]")
+    for name, t, shape in (("q", q, (B, G, V)), ("drafts", drafts, (B, G)), ("u", u, (B, G)), ("r", r, (B,))):
+        if t is not None and tuple(t.shape) != shape:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
+    st = load_library().spec_accept(
+        _ptr(logits, "logits", (torch.float32,)), _opt_ptr(q, "q", (torch.float32,)),
+        _opt_ptr(drafts, "drafts", (torch.int32,)), _opt_ptr(u, "u", (torch.float32,)),
+        _opt_ptr(r, "r", (torch.float32,)), float(tau), B, T, V, int(S_max),
+        _ptr(lens, "lens", (torch.int32,)), _ptr(result, "result", (torch.int32,)),
+        _ptr(workspace, "workspace", (torch.uint8,)), workspace.numel(), _stream(stream, logits.device))
+    _check("spec_accept", st)
+    return result
 
 
 def attn_partial(q, k_cache, v_cache, lens, scale: float, workspace, causal: bool = False,

@@ -21,6 +21,7 @@
 #include "prefill_kernel.hpp"
 #include "probe_kernel.hpp"
 #include "rope_kernel.hpp"
+#include "spec_kernel.hpp"
 #include "verify_kernel.hpp"
 
 namespace decattn {
@@ -379,6 +380,57 @@ int gemv_common(const void* W, const float* scale, const void* x, int B, int N, 
     return DECATTN_OK;
 }
 
+// ---- speculative accept/reject ----------------------------------------------
+
+constexpr int kSpecMaxV = 1 << 24;
+constexpr int kSpecMaxNC = 2048;          // chunk sums one wave scans in the finish kernel
+#ifndef DECATTN_SPEC_TARGET_BLOCKS
+#define DECATTN_SPEC_TARGET_BLOCKS 2048
+#endif
+
+struct SpecPlan {
+    int U, NC;
+    size_t stats_bytes, parts_bytes, total_bytes;
+};
+
+// Chunks of 1024*U vocabulary entries, U in {1, 2, 4, 8}: the largest U that
+// still leaves DECATTN_SPEC_TARGET_BLOCKS first-kernel workgroups over the
+// B*T rows (small batches want many short chunks, since each workgroup's
+// latency dominates; big ones want long chunks), and at most kSpecMaxNC
+// chunks; U only grows while that cuts the chunk count.
+int spec_plan(int B, int T, int V, SpecPlan* sp) {
+    if (B <= 0 || T <= 0 || V <= 0) return DECATTN_ERR_INVALID_ARG;
+    if (T > kSpecMaxT || V > kSpecMaxV) return DECATTN_ERR_UNSUPPORTED;
+    auto nc = [V](int u) { return (V + u * kSpecSeg - 1) / (u * kSpecSeg); };
+    int U = 1;
+    while (U < 8 && nc(2 * U) < nc(U) &&
+           ((long long)B * T * nc(2 * U) >= DECATTN_SPEC_TARGET_BLOCKS || nc(U) > kSpecMaxNC))
+        U *= 2;
+    const int NC = nc(U);
+    if ((long long)B * T * NC > 0x7FFFFFFF) return DECATTN_ERR_UNSUPPORTED;
+    sp->U = U;
+    sp->NC = NC;
+    sp->stats_bytes = round_up((size_t)B * T * NC * sizeof(float2), kAlign);
+    sp->parts_bytes = round_up((size_t)B * NC * sizeof(float2), kAlign);
+    sp->total_bytes = sp->stats_bytes + sp->parts_bytes + round_up((size_t)B * sizeof(uint32_t), kAlign);
+    return DECATTN_OK;
+}
+
+template <int U, bool VEC, bool GREEDY>
+int spec_launch(const SpecParams& sp, int B, hipStream_t s) {
+    const dim3 blk(kSpecThreads);
+    hipLaunchKernelGGL((spec_stats_kernel<U, VEC, GREEDY>), dim3((unsigned)(B * sp.T * sp.NC)), blk, 0, s, sp);
+    hipLaunchKernelGGL((spec_finish_kernel<U, VEC, GREEDY>), dim3((unsigned)(GREEDY ? B : B * sp.NC)), blk, 0, s,
+                       sp);
+    return hipGetLastError() == hipSuccess ? DECATTN_OK : DECATTN_ERR_HIP;
+}
+
+template <int U>
+int spec_launch_u(const SpecParams& sp, int B, bool vec, bool greedy, hipStream_t s) {
+    if (vec) return greedy ? spec_launch<U, true, true>(sp, B, s) : spec_launch<U, true, false>(sp, B, s);
+    return greedy ? spec_launch<U, false, true>(sp, B, s) : spec_launch<U, false, false>(sp, B, s);
+}
+
 }  // namespace
 }  // namespace decattn
 
@@ -576,6 +628,74 @@ int quantize_rows_int8(const void* W, int N, int K, void* Wq, float* scale, void
                        static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(W), N, K,
                        static_cast<int8_t*>(Wq), scale);
     return hipGetLastError() == hipSuccess ? DECATTN_OK : DECATTN_ERR_HIP;
+}
+
+size_t spec_accept_workspace_bytes(int B, int T, int V) {
+    SpecPlan sp;
+    return spec_plan(B, T, V, &sp) == DECATTN_OK ? sp.total_bytes : 0;
+}
+
+int spec_accept(const float* logits, const float* q, const int32_t* drafts, const float* u, const float* r,
+                float tau, int B, int T, int V, int S_max, int32_t* lens, int32_t* result, void* workspace,
+                size_t workspace_bytes, void* stream) {
+    SpecPlan plan;
+    int st = spec_plan(B, T, V, &plan);
+    if (st != DECATTN_OK) return st;
+    if (S_max <= 0 || !std::isfinite(tau) || !(tau >= 0.f)) return DECATTN_ERR_INVALID_ARG;
+    const bool greedy = tau == 0.f;
+    float c2 = 0.f;
+    if (!greedy) {
+        const double c = 1.4426950408889634 / (double)tau;     // log2(e) / tau
+        if (!(c <= (double)FLT_MAX)) return DECATTN_ERR_INVALID_ARG;
+        c2 = (float)c;
+    }
+    const int gamma = T - 1;
+    if (!logits || !lens || !result || !workspace) return DECATTN_ERR_INVALID_ARG;
+    if (gamma > 0 && !drafts) return DECATTN_ERR_INVALID_ARG;
+    if (!greedy && (!r || (gamma > 0 && (!q || !u)))) return DECATTN_ERR_INVALID_ARG;
+    const void* word_ptrs[7] = {logits, q, drafts, u, r, lens, result};
+    for (const void* ptr : word_ptrs)
+        if (reinterpret_cast<uintptr_t>(ptr) & 3u) return DECATTN_ERR_INVALID_ARG;
+    if (!aligned16(workspace)) return DECATTN_ERR_INVALID_ARG;
+    if (workspace_bytes < plan.total_bytes) return DECATTN_ERR_WORKSPACE;
+    // what the call writes (lengths, results, workspace) must not overlap
+    // anything else it reads or writes; lens itself is read and written
+    const size_t lb = (size_t)B * T * V * 4, qb = (size_t)B * gamma * V * 4, db = (size_t)B * gamma * 4;
+    const void* ins[5] = {logits, greedy ? nullptr : q, drafts, greedy ? nullptr : u, greedy ? nullptr : r};
+    const size_t in_sz[5] = {lb, qb, db, db, (size_t)B * 4};
+    const void* outs[3] = {lens, result, workspace};
+    const size_t out_sz[3] = {(size_t)B * 4, (size_t)B * 8, plan.total_bytes};
+    for (int a = 0; a < 3; ++a) {
+        for (int c = 0; c < 5; ++c)
+            if (ins[c] && in_sz[c] && overlaps(outs[a], out_sz[a], ins[c], in_sz[c])) return DECATTN_ERR_INVALID_ARG;
+        for (int c = a + 1; c < 3; ++c)
+            if (overlaps(outs[a], out_sz[a], outs[c], out_sz[c])) return DECATTN_ERR_INVALID_ARG;
+    }
+    SpecParams sp{};
+    sp.logits = logits;
+    sp.q = q;
+    sp.drafts = drafts;
+    sp.u = u;
+    sp.r = r;
+    sp.lens = lens;
+    sp.result = result;
+    char* ws = static_cast<char*>(workspace);
+    sp.stats = reinterpret_cast<float2*>(ws);
+    sp.parts = reinterpret_cast<float2*>(ws + plan.stats_bytes);
+    sp.counters = reinterpret_cast<uint32_t*>(ws + plan.stats_bytes + plan.parts_bytes);
+    sp.c2 = c2;
+    sp.T = T;
+    sp.V = V;
+    sp.NC = plan.NC;
+    sp.S_max = S_max;
+    const bool vec = V % 4 == 0 && aligned16(logits) && (greedy || gamma == 0 || aligned16(q));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    switch (plan.U) {
+        case 1: return spec_launch_u<1>(sp, B, vec, greedy, s);
+        case 2: return spec_launch_u<2>(sp, B, vec, greedy, s);
+        case 4: return spec_launch_u<4>(sp, B, vec, greedy, s);
+        default: return spec_launch_u<8>(sp, B, vec, greedy, s);
+    }
 }
 
 int decattn_probe_read(const void* buf, size_t bytes, void* sink, void* stream) {

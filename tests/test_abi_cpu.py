@@ -35,7 +35,8 @@ def test_header_declares_the_boundary():
     assert {"decode_attn", "chunk_attn", "attn_partial", "attn_merge", "decattn_workspace_bytes",
             "decattn_default_chunk", "decattn_status_str", "decattn_abi_version",
             "decattn_probe_read", "decattn_probe_copy", "rope_kv_write", "prefill_attn",
-            "gemv_bf16", "gemv_int8", "quantize_rows_int8"} <= names
+            "gemv_bf16", "gemv_int8", "quantize_rows_int8", "spec_accept",
+            "spec_accept_workspace_bytes"} <= names
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -206,3 +207,40 @@ def test_gemv_entry_points_reject_bad_arguments(lib):
     for kw, st in [(dict(W=None), 1), (dict(q=None), 1), (dict(s=None), 1), (dict(N=0), 1), (dict(K=24), 2),
                    (dict(q=W + 64), 1), (dict(s=W + 16), 1), (dict(q=X + 8), 1)]:
         assert z(**kw) == st, kw
+
+
+_SPEC = dict(logits=0x10000000, q=0x20000000, drafts=0x30000000, u=0x31000000, r=0x32000000, tau=1.0,
+             B=2, T=4, V=1000, S=512, lens=0x40000000, result=0x41000000, ws=0x50000000, wsb=1 << 20)
+
+
+def _spec(lib, **kw):
+    a = dict(_SPEC, **kw)
+    return lib.spec_accept(a["logits"], a["q"], a["drafts"], a["u"], a["r"], a["tau"], a["B"], a["T"], a["V"],
+                           a["S"], a["lens"], a["result"], a["ws"], a["wsb"], None)
+
+
+def test_spec_workspace_bytes(lib):
+    w = lib.spec_accept_workspace_bytes
+    assert w(1, 6, 128256) > 0 and w(0, 6, 100) == 0 and w(1, 0, 100) == 0 and w(1, 6, 0) == 0
+    assert w(1, 33, 100) == 0 and w(1, 6, (1 << 24) + 1) == 0
+    # at least the chunk statistics of every position, the chunk sums and a counter per row
+    for B, T, V in [(1, 6, 128256), (64, 6, 128256), (3, 1, 50257), (8, 32, 1 << 24)]:
+        nc_max = -(-V // 1024)
+        nc_min = -(-V // 8192)
+        assert (B * T * nc_min + B * nc_min) * 8 + 4 * B <= w(B, T, V) <= (B * T * nc_max + B * nc_max) * 8 + 4 * B + 768
+        assert w(B, T, V) % 256 == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(logits=None), 1), (dict(lens=None), 1), (dict(result=None), 1), (dict(ws=None), 1),
+    (dict(drafts=None), 1), (dict(r=None), 1), (dict(q=None), 1), (dict(u=None), 1),
+    (dict(tau=-1.0), 1), (dict(tau=float("nan")), 1), (dict(tau=float("inf")), 1), (dict(tau=1e-45), 1),
+    (dict(B=0), 1), (dict(T=0), 1), (dict(V=0), 1), (dict(S=0), 1), (dict(T=33), 2), (dict(V=(1 << 24) + 1), 2),
+    (dict(logits=0x10000002), 1), (dict(lens=0x40000001), 1), (dict(ws=0x50000008), 1), (dict(wsb=64), 3),
+    (dict(result=0x10000010), 1),               # result inside logits
+    (dict(result=0x40000004), 1),               # result overlaps lens
+    (dict(ws=0x20000100), 1),                   # workspace inside q
+    (dict(lens=0x32000004), 1),                 # lens overlaps r
+])
+def test_spec_accept_rejects_bad_arguments(lib, kw, status):
+    assert _spec(lib, **kw) == status

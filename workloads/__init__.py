@@ -34,6 +34,7 @@ import numpy as np
 __all__ = [
     "Workload", "CONFIGS", "bf16_randn", "make_case", "make_config",
     "seed_for", "bf16_scale", "uniform_mask", "ragged_lens", "BF16_NAN",
+    "SPEC_VOCABS", "spec_sampling_case", "spec_greedy_case",
 ]
 
 # A quiet-NaN bf16 pattern, used by tests to poison cache slots that must never be read.
@@ -201,3 +202,79 @@ def make_config(cfg: int, layer: int = 0, n: int | None = None) -> dict:
     else:
         lens = np.full((w.B,), max(w.lens) if n is None else n, dtype=np.int32)
     return {"q": q, "k": k, "v": v, "lens": lens, "scale": w.scale, "workload": w}
+
+
+# ---------------------------------------------------------------------------
+# Inputs of the speculative accept/reject step.
+#
+# The verify pass of the pages' speculative loops scores k + 1 positions of
+# a target model: tinydecode's example pairs Llama-3.2-3B with a Llama-3.2-1B
+# draft at k = 5 (tinydecode README, "using it"); FlashSpec sweeps gamma over
+# 1..16 with a Qwen2.5-1.5B target and a 0.5B drafter (FlashSpec page, results
+# tables). Their vocabularies set V; 50257 is a size that is not a multiple
+# of 4, which takes the library's scalar-load path.
+#
+# Stand-ins for model outputs: target logits are float32 N(0, sigma^2)
+# (sigma = 3 gives a spread of about 27 over 128k entries, peaked like a
+# language model's); the draft distribution q is the softmax of the target
+# logits plus N(0, draft_noise^2) noise at the same temperature (a drafter
+# that mostly agrees with its target); draft tokens are drawn from q with
+# NumPy's choice; u and r are float32 uniforms in [0, 1).
+# ---------------------------------------------------------------------------
+
+SPEC_VOCABS = {"llama3": 128256, "qwen2.5": 151936, "ragged": 50257}
+
+
+def spec_sampling_case(B: int, T: int, V: int, seed: int, *, tau: float = 1.0, sigma: float = 3.0,
+                       draft_noise: float = 1.0, ctx_max: int = 8192) -> dict:
+    """Seeded inputs of one sampling step: logits [B][T][V], q [B][T-1][V],
+    drafts [B][T-1], u [B][T-1], r [B], ctx [B], tau (a float32 value)."""
+    rng = np.random.default_rng(seed)
+    G = T - 1
+    logits = rng.standard_normal((B, T, V), dtype=np.float32) * np.float32(sigma)
+    tau = float(np.float32(tau))
+    q = np.zeros((B, G, V), dtype=np.float32)
+    drafts = np.zeros((B, G), dtype=np.int32)
+    for b in range(B):
+        for i in range(G):
+            z = (logits[b, i].astype(np.float64) + rng.standard_normal(V) * draft_noise) / tau
+            e = np.exp(z - z.max())
+            q64 = e / e.sum()
+            q[b, i] = q64
+            drafts[b, i] = rng.choice(V, p=q64)
+    u = rng.random((B, G), dtype=np.float32)
+    r = rng.random(B, dtype=np.float32)
+    ctx = rng.integers(0, ctx_max, B).astype(np.int32)
+    return {"logits": logits, "q": q, "drafts": drafts, "u": u, "r": r, "ctx": ctx, "tau": tau}
+
+
+def spec_greedy_case(B: int, T: int, V: int, seed: int, *, sigma: float = 3.0, tie_frac: float = 0.25,
+                     ctx_max: int = 8192) -> dict:
+    """Seeded inputs of one greedy step with planted maxima.
+
+    Position i of row b gets one entry raised 1 above the row's largest
+    logit (in a `tie_frac` share of positions, two entries share that value:
+    the top token is then the smaller index). The drafts equal the top tokens
+    of the first m[b] positions (m uniform in 0..T-1) and differ from it at
+    position m[b]. Returns the step's inputs plus `top` [B][T] and `m` [B]."""
+    rng = np.random.default_rng(seed)
+    G = T - 1
+    logits = rng.standard_normal((B, T, V), dtype=np.float32) * np.float32(sigma)
+    top = np.zeros((B, T), dtype=np.int32)
+    for b in range(B):
+        for i in range(T):
+            hi = np.float32(logits[b, i].max() + 1)
+            g = int(rng.integers(V))
+            logits[b, i, g] = hi
+            if V > 1 and rng.random() < tie_frac:
+                g2 = int((g + 1 + rng.integers(V - 1)) % V)
+                logits[b, i, g2] = hi
+                g = min(g, g2)
+            top[b, i] = g
+    m = rng.integers(0, T, B).astype(np.int32)
+    drafts = np.zeros((B, G), dtype=np.int32)
+    for b in range(B):
+        for i in range(G):
+            drafts[b, i] = top[b, i] if i < m[b] else (top[b, i] + 1 + rng.integers(max(V - 1, 1))) % V
+    ctx = rng.integers(0, ctx_max, B).astype(np.int32)
+    return {"logits": logits, "drafts": drafts, "ctx": ctx, "tau": 0.0, "top": top, "m": m}
