@@ -191,8 +191,8 @@ int quantize_rows_int8(const void* W, int N, int K, void* Wq, float* scale, void
  *   workspace >= spec_accept_workspace_bytes(B, T, V) bytes, 16-byte aligned;
  *            overwritten; calls that share it must be ordered on one stream
  * T in 1..32, V in 1..2^24. lens, result and workspace must not overlap each
- * other or the inputs (checked). Two launches on `stream`, no host sync,
- * capturable. */
+ * other or the inputs (checked). Three launches on `stream` (two when
+ * tau == 0), no host sync, capturable. */
 size_t spec_accept_workspace_bytes(int B, int T, int V);
 int spec_accept(const float* logits, const float* q, const int32_t* drafts, const float* u, const float* r,
                 float tau, int B, int T, int V, int S_max, int32_t* lens, int32_t* result,

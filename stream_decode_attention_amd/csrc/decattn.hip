@@ -383,21 +383,23 @@ int gemv_common(const void* W, const float* scale, const void* x, int B, int N, 
 // ---- speculative accept/reject ----------------------------------------------
 
 constexpr int kSpecMaxV = 1 << 24;
-constexpr int kSpecMaxNC = 2048;          // chunk sums one wave scans in the finish kernel
+constexpr int kSpecMaxNC = kSpecStage / 2;   // chunk sums staged in LDS by the select kernel
 #ifndef DECATTN_SPEC_TARGET_BLOCKS
 #define DECATTN_SPEC_TARGET_BLOCKS 2048
 #endif
 
 struct SpecPlan {
     int U, NC;
-    size_t stats_bytes, parts_bytes, total_bytes;
+    size_t stats_bytes, parts_bytes, rowinfo_bytes, total_bytes;
 };
 
 // Chunks of 1024*U vocabulary entries, U in {1, 2, 4, 8}: the largest U that
 // still leaves DECATTN_SPEC_TARGET_BLOCKS first-kernel workgroups over the
 // B*T rows (small batches want many short chunks, since each workgroup's
 // latency dominates; big ones want long chunks), and at most kSpecMaxNC
-// chunks; U only grows while that cuts the chunk count.
+// chunks; U only grows while that cuts the chunk count. The workspace holds
+// the chunk statistics [B][T][NC], the residual chunk sums [B][NC] and one
+// float4 per row and per draft.
 int spec_plan(int B, int T, int V, SpecPlan* sp) {
     if (B <= 0 || T <= 0 || V <= 0) return DECATTN_ERR_INVALID_ARG;
     if (T > kSpecMaxT || V > kSpecMaxV) return DECATTN_ERR_UNSUPPORTED;
@@ -407,12 +409,14 @@ int spec_plan(int B, int T, int V, SpecPlan* sp) {
            ((long long)B * T * nc(2 * U) >= DECATTN_SPEC_TARGET_BLOCKS || nc(U) > kSpecMaxNC))
         U *= 2;
     const int NC = nc(U);
-    if ((long long)B * T * NC > 0x7FFFFFFF) return DECATTN_ERR_UNSUPPORTED;
+    if (NC > kSpecMaxNC || (long long)B * T * NC > 0x7FFFFFFF) return DECATTN_ERR_UNSUPPORTED;
     sp->U = U;
     sp->NC = NC;
     sp->stats_bytes = round_up((size_t)B * T * NC * sizeof(float2), kAlign);
     sp->parts_bytes = round_up((size_t)B * NC * sizeof(float2), kAlign);
-    sp->total_bytes = sp->stats_bytes + sp->parts_bytes + round_up((size_t)B * sizeof(uint32_t), kAlign);
+    sp->rowinfo_bytes = round_up((size_t)B * sizeof(float4), kAlign);
+    sp->total_bytes = sp->stats_bytes + sp->parts_bytes + sp->rowinfo_bytes +
+                      round_up((size_t)B * (T > 1 ? T - 1 : 1) * sizeof(float4), kAlign);
     return DECATTN_OK;
 }
 
@@ -422,6 +426,7 @@ int spec_launch(const SpecParams& sp, int B, hipStream_t s) {
     hipLaunchKernelGGL((spec_stats_kernel<U, VEC, GREEDY>), dim3((unsigned)(B * sp.T * sp.NC)), blk, 0, s, sp);
     hipLaunchKernelGGL((spec_finish_kernel<U, VEC, GREEDY>), dim3((unsigned)(GREEDY ? B : B * sp.NC)), blk, 0, s,
                        sp);
+    if (!GREEDY) hipLaunchKernelGGL((spec_select_kernel<U, VEC>), dim3((unsigned)B), blk, 0, s, sp);
     return hipGetLastError() == hipSuccess ? DECATTN_OK : DECATTN_ERR_HIP;
 }
 
@@ -682,7 +687,8 @@ int spec_accept(const float* logits, const float* q, const int32_t* drafts, cons
     char* ws = static_cast<char*>(workspace);
     sp.stats = reinterpret_cast<float2*>(ws);
     sp.parts = reinterpret_cast<float2*>(ws + plan.stats_bytes);
-    sp.counters = reinterpret_cast<uint32_t*>(ws + plan.stats_bytes + plan.parts_bytes);
+    sp.rowinfo = reinterpret_cast<float4*>(ws + plan.stats_bytes + plan.parts_bytes);
+    sp.dinfo = reinterpret_cast<float4*>(ws + plan.stats_bytes + plan.parts_bytes + plan.rowinfo_bytes);
     sp.c2 = c2;
     sp.T = T;
     sp.V = V;

@@ -6,7 +6,7 @@
 // FlashSpec page, correctness paragraph: Leviathan et al. 2023, Algorithm 1,
 // the test taken in log space).
 //
-// Two launches, no host sync:
+// Launches, no host sync:
 //   spec_stats_kernel   one workgroup per (row b, position i, vocabulary
 //                       chunk): the chunk's max logit and sum of
 //                       exp2((l - max) * log2(e) / tau), or for greedy its
@@ -17,13 +17,14 @@
 //                       the row reaches the same bits) and takes the accept
 //                       decisions; it then sums the residual weights of its
 //                       chunk for the first rejected position (or p of the
-//                       bonus row). The last workgroup of the row to arrive
-//                       scans the chunk sums in index order, rescans the one
-//                       chunk that holds the draw, and writes the accept count,
-//                       the token and the new length. Greedy needs no residual,
-//                       so its finish is one workgroup per row.
-// The arrival counters of the second kernel are zeroed by the first, so the
-// workspace needs no clearing between calls.
+//                       bonus row). Greedy needs no residual, so its finish is
+//                       one workgroup per row and writes the result itself;
+//   spec_select_kernel  (sampling) one workgroup per row: scans the chunk sums
+//                       in index order, rescans the one chunk that holds the
+//                       draw, and writes the accept count, the token and the
+//                       new length.
+// Each kernel only reads what earlier launches wrote, so the kernel
+// boundaries order every exchange: no atomics, fences or counters.
 #pragma once
 
 #include <climits>
@@ -36,6 +37,8 @@ constexpr int kSpecThreads = 256;
 constexpr int kSpecWaves = kSpecThreads / 64;
 constexpr int kSpecSeg = kSpecThreads * 4;    // elements per segment: one float4 per thread
 constexpr int kSpecMaxT = 32;                 // gamma + 1 positions: one ballot decides them all
+constexpr int kSpecStage = 4096;              // chunk statistics staged in LDS at once (float2)
+
 
 struct SpecParams {
     const float* logits;      // [B][T][V]
@@ -47,7 +50,8 @@ struct SpecParams {
     int32_t* result;          // [B][2]: accepted drafts, next token
     float2* stats;            // [B][T][NC]
     float2* parts;            // [B][NC]
-    uint32_t* counters;       // [B]
+    float4* rowinfo;          // [B]: max and 1/sum of the drawing position's softmax, accept count
+    float4* dinfo;            // [B][T-1]: each draft's target logit, q and u, and its id (sampling)
     float c2;                 // log2(e) / tau
     int T, V, NC, S_max;
 };
@@ -131,7 +135,6 @@ __global__ __launch_bounds__(kSpecThreads) void spec_stats_kernel(const SpecPara
     const int row = blockIdx.x / p.NC;               // b * T + i
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int c0 = c * (U * kSpecSeg);
-    if (t == 0 && c == 0 && row % p.T == 0) p.counters[row / p.T] = 0u;
     float x[4 * U];
     spec_load<U, VEC>(p.logits + (size_t)row * p.V, p.V, c0, kNegInf, x);
     __shared__ float sh_v[kSpecWaves], sh_s[kSpecWaves];
@@ -164,6 +167,24 @@ __global__ __launch_bounds__(kSpecThreads) void spec_stats_kernel(const SpecPara
 #pragma unroll
             for (int k = 0; k < 4 * U; ++k) s += fast_exp2((x[k] - m) * p.c2);
         }
+        // the workgroup whose chunk holds draft i's token records that token's
+        // logit, q and u for the decision (row 0 of the chunk holds the id of
+        // a draft outside the vocabulary)
+        const int gamma = p.T - 1, i = row % p.T, b = row / p.T;
+        if (i < gamma) {
+            const int d = p.drafts[(size_t)b * gamma + i];
+            const int li = d - c0;
+            if (d >= 0 && d < p.V && li < U * kSpecSeg && li >= 0 && (li % kSpecSeg) / 4 == t) {
+                float ld = 0.f;
+#pragma unroll
+                for (int k = 0; k < 4 * U; ++k)
+                    if (k == 4 * (li / kSpecSeg) + li % 4) ld = x[k];
+                const size_t di = (size_t)b * gamma + i;
+                p.dinfo[di] = make_float4(ld, p.q[di * p.V + d], p.u[di], __int_as_float(d));
+            } else if ((d < 0 || d >= p.V) && c == 0 && t == 0) {
+                p.dinfo[(size_t)b * gamma + i] = make_float4(0.f, 0.f, 0.f, __int_as_float(d));
+            }
+        }
         const float M = wave_max(m);
         s = wave_sum(spec_rescale(s, m, M, p.c2));
         if (lane == 0) { sh_v[w] = M; sh_s[w] = s; }
@@ -195,45 +216,58 @@ __global__ __launch_bounds__(kSpecThreads) void spec_finish_kernel(const SpecPar
     __shared__ int sh_n;
 
     // the draft side of each position (threads t < gamma, all in wave 0):
-    // its token id and, for sampling, u and the target logit and q at that id
+    // its token id and, for sampling, the target logit, q and u at that id
+    // as the first kernel recorded them
     int d = -1;
     float ld = 0.f, qd = 0.f, ud = 0.f;
     if (t < gamma) {
-        d = p.drafts[(size_t)b * gamma + t];
-        if (!GREEDY && d >= 0 && d < V) {
-            ld = p.logits[((size_t)b * T + t) * V + d];
-            qd = p.q[((size_t)b * gamma + t) * V + d];
-            ud = p.u[(size_t)b * gamma + t];
+        if constexpr (GREEDY) {
+            d = p.drafts[(size_t)b * gamma + t];
+        } else {
+            const float4 di = p.dinfo[(size_t)b * gamma + t];
+            ld = di.x; qd = di.y; ud = di.z;
+            d = __float_as_int(di.w);
         }
     }
 
-    // merge the chunk statistics of every position; one wave per position
-    for (int i = w; i < T; i += kSpecWaves) {
-        const float2* st = p.stats + ((size_t)b * T + i) * p.NC;
-        if constexpr (GREEDY) {
-            float bv = kNegInf;
-            int bi = INT_MAX;
-            for (int k = lane; k < p.NC; k += 64) {
-                const float2 v = st[k];
-                const int vi = __float_as_int(v.y);
-                if (spec_better(v.x, vi, bv, bi)) { bv = v.x; bi = vi; }
+    // merge the chunk statistics of every position: stage tiles of whole
+    // positions in LDS (one batch of loads), then one wave per position
+    __shared__ float2 st_lds[kSpecStage];
+    const int NC = p.NC;
+    const int rpt = kSpecStage / NC;                  // NC <= kSpecStage / 2
+    for (int i0 = 0; i0 < T; i0 += rpt) {
+        const int nr = T - i0 < rpt ? T - i0 : rpt;
+        const float2* src = p.stats + ((size_t)b * T + i0) * NC;
+#pragma unroll 4
+        for (int e = t; e < nr * NC; e += kSpecThreads) st_lds[e] = src[e];
+        __syncthreads();
+        for (int i = i0 + w; i < i0 + nr; i += kSpecWaves) {
+            const float2* st = st_lds + (size_t)(i - i0) * NC;
+            if constexpr (GREEDY) {
+                float bv = kNegInf;
+                int bi = INT_MAX;
+                for (int k = lane; k < NC; k += 64) {
+                    const float2 v = st[k];
+                    const int vi = __float_as_int(v.y);
+                    if (spec_better(v.x, vi, bv, bi)) { bv = v.x; bi = vi; }
+                }
+                wave_argmax(bv, bi);
+                if (lane == 0) row_i[i] = bi;
+            } else {
+                float m = kNegInf, s = 0.f;
+                for (int k = lane; k < NC; k += 64) {
+                    const float2 v = st[k];
+                    const float M2 = fmaxf(m, v.x);
+                    s = spec_rescale(s, m, M2, p.c2) + spec_rescale(v.y, v.x, M2, p.c2);
+                    m = M2;
+                }
+                const float M = wave_max(m);
+                s = wave_sum(spec_rescale(s, m, M, p.c2));
+                if (lane == 0) { row_m[i] = M; row_s[i] = s; }
             }
-            wave_argmax(bv, bi);
-            if (lane == 0) row_i[i] = bi;
-        } else {
-            float m = kNegInf, s = 0.f;
-            for (int k = lane; k < p.NC; k += 64) {
-                const float2 v = st[k];
-                const float M2 = fmaxf(m, v.x);
-                s = spec_rescale(s, m, M2, p.c2) + spec_rescale(v.y, v.x, M2, p.c2);
-                m = M2;
-            }
-            const float M = wave_max(m);
-            s = wave_sum(spec_rescale(s, m, M, p.c2));
-            if (lane == 0) { row_m[i] = M; row_s[i] = s; }
         }
+        __syncthreads();
     }
-    __syncthreads();
 
     // keep draft i iff log2 u_i < log2 p_i(d_i) - log2 q_i(d_i) (greedy: d_i is
     // the argmax); n = the first position not kept, or gamma
@@ -295,128 +329,148 @@ __global__ __launch_bounds__(kSpecThreads) void spec_finish_kernel(const SpecPar
             }
         }
 
-        // the last workgroup of row b to arrive draws the token: release the
-        // chunk sum, count the arrival, acquire everyone else's sums
-        __shared__ int sh_last;
-        __threadfence();
-        __syncthreads();
-        if (t == 0) sh_last = atomicAdd(&p.counters[b], 1u) == (unsigned)(p.NC - 1);
-        __syncthreads();
-        if (!sh_last) return;
-        __threadfence();
+        if (c == 0 && t == 0) p.rowinfo[b] = make_float4(M, inv_s, __int_as_float(n), 0.f);
+    }
+}
 
-        // which chunk holds the draw: running sums over chunks in index order
-        __shared__ int sh_c, sh_mode, sh_use_p;
-        __shared__ float sh_t, sh_base;
-        if (w == 0) {
-            const float2* pr = p.parts + (size_t)b * p.NC;
-            float tw = 0.f, tp = 0.f;                     // totals, by the same scan as below
-            for (int k0 = 0; k0 < p.NC; k0 += 64) {
-                const int k = k0 + lane;
-                const float2 v = k < p.NC ? pr[k] : make_float2(0.f, 0.f);
-                tw += __shfl(wave_incl_scan(v.x), 63);
-                tp += __shfl(wave_incl_scan(v.y), 63);
-            }
-            const bool use_p = bonus || !(tw > 0.f);
-            const float total = use_p ? tp : tw;
-            const float thr = p.r[b] * total;
-            int found = -1, last_pos = -1;
-            float base = 0.f, carry = 0.f;
-            for (int k0 = 0; k0 < p.NC; k0 += 64) {
-                const int k = k0 + lane;
-                const float2 v2 = k < p.NC ? pr[k] : make_float2(0.f, 0.f);
-                const float v = use_p ? v2.y : v2.x;
-                const float inc = wave_incl_scan(v);
-                const float cum = carry + inc;
-                const float up = __shfl_up(inc, 1);          // every lane takes part in the shuffle
-                const float excl = carry + (lane ? up : 0.f);
-                const unsigned long long hit = __ballot(k < p.NC && v > 0.f && cum > thr);
-                if (hit) {
-                    const int L = __ffsll(hit) - 1;
-                    found = k0 + L;
-                    base = __shfl(excl, L);
-                    break;
-                }
-                const unsigned long long pos = __ballot(k < p.NC && v > 0.f);
-                if (pos) last_pos = k0 + 63 - __clzll(pos);
-                carry += __shfl(inc, 63);
-            }
-            if (lane == 0) {
-                sh_use_p = use_p;
-                sh_t = thr;
-                sh_base = base;
-                // 0: first entry whose running sum passes thr; 1: rounding left
-                // thr at or past the total, take the last positive entry;
-                // 2: no positive weight at all (rows that break the input rules)
-                sh_mode = found >= 0 ? 0 : (last_pos >= 0 ? 1 : 2);
-                sh_c = found >= 0 ? found : (last_pos >= 0 ? last_pos : 0);
-            }
-        }
-        __syncthreads();
+template <int U, bool VEC>
+__global__ __launch_bounds__(kSpecThreads) void spec_select_kernel(const SpecParams p) {
+    constexpr int CH = U * kSpecSeg;
+    const int b = blockIdx.x;
+    const int T = p.T, gamma = T - 1, V = p.V;
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const float4 info = p.rowinfo[b];
+    const float M = info.x, inv_s = info.y;
+    const int n = __float_as_int(info.z);
+    const bool bonus = n == gamma;
+    const float* lrow = p.logits + ((size_t)b * T + n) * V;
+    const float* qrow = bonus ? nullptr : p.q + ((size_t)b * gamma + n) * V;
 
-        // rescan the chosen chunk: its weights into LDS in index order, then
-        // one wave runs the sum on from the chunk's base
-        __shared__ __attribute__((aligned(16))) float wbuf[CH];
-        __shared__ int sh_lastpos;
-        if (t == 0) sh_lastpos = -1;
-        __syncthreads();
-        const int cs = sh_c, mode = sh_mode;
-        const bool use_p = sh_use_p;
-        {
-            float x[4 * U], y[4 * U];
-            spec_load<U, VEC>(lrow, V, cs * CH, kNegInf, x);
-            if (bonus) {
-#pragma unroll
-                for (int k = 0; k < 4 * U; ++k) y[k] = 0.f;
-            } else {
-                spec_load<U, VEC>(qrow, V, cs * CH, 0.f, y);
-            }
-            int lp = -1;
-#pragma unroll
-            for (int j = 0; j < U; ++j)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int li = j * kSpecSeg + 4 * t + e;
-                    const float wk = spec_weight(x[4 * j + e], y[4 * j + e], M, p.c2, inv_s, use_p);
-                    wbuf[li] = wk;
-                    if (wk > 0.f) lp = li > lp ? li : lp;
-                }
-            if (lp >= 0) atomicMax(&sh_lastpos, lp);
+    // which chunk holds the draw: running sums over chunks in index order,
+    // from the chunk sums staged in LDS
+    __shared__ int sh_c, sh_mode, sh_use_p;
+    __shared__ float sh_t, sh_base;
+    __shared__ float2 pr[kSpecStage / 2];
+    {
+        const float2* src = p.parts + (size_t)b * p.NC;
+#pragma unroll 4
+        for (int e = t; e < p.NC; e += kSpecThreads) pr[e] = src[e];
+    }
+    __syncthreads();
+    if (w == 0) {
+        float tw = 0.f, tp = 0.f;                     // totals, by the same scan as below
+        for (int k0 = 0; k0 < p.NC; k0 += 64) {
+            const int k = k0 + lane;
+            const float2 v = k < p.NC ? pr[k] : make_float2(0.f, 0.f);
+            tw += __shfl(wave_incl_scan(v.x), 63);
+            tp += __shfl(wave_incl_scan(v.y), 63);
         }
-        __syncthreads();
-        if (w == 0) {
-            int pick = -1;
-            if (mode == 0) {
-                const float thr = sh_t;
-                float carry = sh_base;
-                for (int s0 = 0; s0 < CH; s0 += 256) {
-                    const float4 v = *reinterpret_cast<const float4*>(&wbuf[s0 + 4 * lane]);
-                    const float a0 = v.x, a1 = a0 + v.y, a2 = a1 + v.z, a3 = a2 + v.w;
-                    const float inc = wave_incl_scan(a3);
-                    const float up = __shfl_up(inc, 1);
-                    const float pre = carry + (lane ? up : 0.f);
-                    int ef = 4;
-                    if (v.w > 0.f && pre + a3 > thr) ef = 3;
-                    if (v.z > 0.f && pre + a2 > thr) ef = 2;
-                    if (v.y > 0.f && pre + a1 > thr) ef = 1;
-                    if (v.x > 0.f && pre + a0 > thr) ef = 0;
-                    const unsigned long long hit = __ballot(ef < 4);
-                    if (hit) {
-                        const int L = __ffsll(hit) - 1;
-                        pick = s0 + 4 * L + __shfl(ef, L);
-                        break;
-                    }
-                    carry += __shfl(inc, 63);
-                }
+        const bool use_p = bonus || !(tw > 0.f);
+        const float total = use_p ? tp : tw;
+        const float thr = p.r[b] * total;
+        int found = -1, last_pos = -1;
+        float base = 0.f, carry = 0.f;
+        for (int k0 = 0; k0 < p.NC; k0 += 64) {
+            const int k = k0 + lane;
+            const float2 v2 = k < p.NC ? pr[k] : make_float2(0.f, 0.f);
+            const float v = use_p ? v2.y : v2.x;
+            const float inc = wave_incl_scan(v);
+            const float cum = carry + inc;
+            const float up = __shfl_up(inc, 1);          // every lane takes part in the shuffle
+            const float excl = carry + (lane ? up : 0.f);
+            const unsigned long long hit = __ballot(k < p.NC && v > 0.f && cum > thr);
+            if (hit) {
+                const int L = __ffsll(hit) - 1;
+                found = k0 + L;
+                base = __shfl(excl, L);
+                break;
             }
-            if (pick < 0) pick = mode == 2 ? 0 : sh_lastpos;
-            if (pick < 0) pick = 0;
-            if (lane == 0) {
-                p.result[2 * (size_t)b] = n;
-                p.result[2 * (size_t)b + 1] = cs * CH + pick;
-                p.lens[b] = spec_new_len(p.lens[b], n, p.S_max);
-            }
+            const unsigned long long pos = __ballot(k < p.NC && v > 0.f);
+            if (pos) last_pos = k0 + 63 - __clzll(pos);
+            carry += __shfl(inc, 63);
         }
+        if (lane == 0) {
+            sh_use_p = use_p;
+            sh_t = thr;
+            sh_base = base;
+            // 0: first entry whose running sum passes thr; 1: rounding left
+            // thr at or past the total, take the last positive entry;
+            // 2: no positive weight at all (rows that break the input rules)
+            sh_mode = found >= 0 ? 0 : (last_pos >= 0 ? 1 : 2);
+            sh_c = found >= 0 ? found : (last_pos >= 0 ? last_pos : 0);
+        }
+    }
+    __syncthreads();
+
+    // rescan the chosen chunk: its weights into LDS in index order; thread t
+    // then owns the run of R consecutive entries [tR, tR + R), adds the
+    // running sum of the runs before it to the chunk's base, and walks its
+    // run; the first entry (smallest index) whose running sum passes thr wins
+    constexpr int R = CH / kSpecThreads;
+    __shared__ __attribute__((aligned(16))) float wbuf[CH];
+    __shared__ int sh_lastpos, sh_pick;
+    __shared__ float sh_wtot[kSpecWaves];
+    if (t == 0) { sh_lastpos = -1; sh_pick = INT_MAX; }
+    __syncthreads();
+    const int cs = sh_c, mode = sh_mode;
+    const bool use_p = sh_use_p;
+    {
+        float x[4 * U], y[4 * U];
+        spec_load<U, VEC>(lrow, V, cs * CH, kNegInf, x);
+        if (bonus) {
+#pragma unroll
+            for (int k = 0; k < 4 * U; ++k) y[k] = 0.f;
+        } else {
+            spec_load<U, VEC>(qrow, V, cs * CH, 0.f, y);
+        }
+        int lp = -1;
+#pragma unroll
+        for (int j = 0; j < U; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int li = j * kSpecSeg + 4 * t + e;
+                const float wk = spec_weight(x[4 * j + e], y[4 * j + e], M, p.c2, inv_s, use_p);
+                wbuf[li] = wk;
+                if (wk > 0.f) lp = li > lp ? li : lp;
+            }
+        if (lp >= 0) atomicMax(&sh_lastpos, lp);
+    }
+    __syncthreads();
+    float run[R];
+#pragma unroll
+    for (int k = 0; k < R; k += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(&wbuf[t * R + k]);
+        run[k] = v.x; run[k + 1] = v.y; run[k + 2] = v.z; run[k + 3] = v.w;
+    }
+    float rs = 0.f;
+#pragma unroll
+    for (int k = 0; k < R; ++k) rs += run[k];
+    const float inc = wave_incl_scan(rs);
+    const float up = __shfl_up(inc, 1);
+    if (lane == 63) sh_wtot[w] = inc;
+    __syncthreads();
+    if (mode == 0) {
+        float c = sh_base;
+        for (int k = 0; k < w; ++k) c += sh_wtot[k];
+        c += lane ? up : 0.f;
+        const float thr = sh_t;
+        int cand = INT_MAX;
+#pragma unroll
+        for (int k = 0; k < R; ++k) {
+            c += run[k];
+            if (cand == INT_MAX && run[k] > 0.f && c > thr) cand = t * R + k;
+        }
+        if (cand != INT_MAX) atomicMin(&sh_pick, cand);
+    }
+    __syncthreads();
+    if (t == 0) {
+        // no entry passed thr (rounding in the last chunk, or modes 1 and 2):
+        // the chunk's last positive entry
+        int pick = sh_pick != INT_MAX ? sh_pick : (mode == 2 ? 0 : sh_lastpos);
+        if (pick < 0) pick = 0;
+        p.result[2 * (size_t)b] = n;
+        p.result[2 * (size_t)b + 1] = cs * CH + pick;
+        p.lens[b] = spec_new_len(p.lens[b], n, p.S_max);
     }
 }
 
