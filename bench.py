@@ -322,6 +322,10 @@ def main():
     if not args.headline_only:
         result["gemv"] = gemv_runs(sda, np, torch, stream, flush)
 
+    # ---------------------------------------- speculative accept/reject step
+    if not args.headline_only:
+        result["spec_accept"] = spec_runs(sda, workloads, np, torch, stream, flush)
+
     # ------------------------------------------------------- other workloads
     if not args.headline_only:
         result["workloads"] = other_workloads(args, dev, up, sda, workloads, rf, np, torch, stream, flush)
@@ -505,6 +509,55 @@ def gemv_runs(sda, np, torch, stream, flush):
                 del gr
         res.append(entry)
         del layers, qlayers
+    return res
+
+
+SPEC_CASES = [
+    # name, B, T (= k + 1), V
+    ("llama3.2-3b-verify-k5", 1, 6, 128256),      # tinydecode's example pairing, k = 5
+    ("qwen2.5-verify-gamma8", 1, 9, 151936),      # FlashSpec's Qwen2.5 pair, gamma = 8
+    ("llama3-vocab-batch64-k5", 64, 6, 128256),   # a batch of 64 rows: the bandwidth case
+]
+
+
+def spec_runs(sda, workloads, np, torch, stream, flush):
+    """spec_accept per call, sampling (tau = 1) and greedy: graphs of 4 calls
+    alternating between two copies of the inputs, median of 5 rounds. GB/s of
+    algorithmic bytes: every logit read once (B*T*V*4) plus, when sampling,
+    the one draft-probability row the residual needs (B*V*4)."""
+    res = []
+    for ci, (name, B, T, V) in enumerate(SPEC_CASES):
+        entry = {"workload": name, "B": B, "T": T, "V": V, "calls_per_graph": 4}
+        for tau, tag in ((1.0, "sampling"), (0.0, "greedy")):
+            c = (workloads.spec_sampling_case(B, T, V, seed=700 + ci, tau=tau) if tau
+                 else workloads.spec_greedy_case(B, T, V, seed=710 + ci))
+            copies = []
+            for _ in range(2):
+                d = {k: torch.from_numpy(np.ascontiguousarray(c[k])).cuda()
+                     for k in ("logits", "q", "drafts", "u", "r") if k in c}
+                d["lens"] = torch.from_numpy(c["ctx"]).cuda()
+                d["res"] = torch.empty((B, 2), dtype=torch.int32, device="cuda")
+                d["ws"] = torch.empty(sda.spec_accept_workspace_bytes(B, T, V), dtype=torch.uint8, device="cuda")
+                copies.append(d)
+
+            def call(d):
+                sda.spec_accept(d["logits"], d.get("q"), d["drafts"], d.get("u"), d.get("r"), tau, d["lens"],
+                                d["res"], d["ws"], 1 << 30, stream=stream)
+            with torch.cuda.stream(stream):
+                call(copies[0])
+                stream.synchronize()
+            n_kept = copies[0]["res"][:, 0].float().mean().item()
+            g = graph_of(torch, stream, [lambda d=d: call(d) for d in copies * 2])
+            us = float(np.median([back_to_back_us(torch, stream, [g], 1, 1, busy=flush) / 4 for _ in range(5)]))
+            alg = B * T * V * 4 + (B * V * 4 if tau else 0)
+            gbps = alg / us / 1e3
+            entry[tag] = {"us_per_call": round(us, 2), "algorithmic_bytes": alg, "GBps": round(gbps, 1),
+                          "frac_of_hbm_peak": round(gbps / 8000.0, 4), "mean_drafts_kept": round(n_kept, 2),
+                          "launches": 2 if tau == 0 else 3}
+            log(f"spec_accept {name} {tag}: {us:.1f} us per call, {gbps:.0f} GB/s, "
+                f"{n_kept:.2f} of {T - 1} drafts kept on average")
+            del g, copies
+        res.append(entry)
     return res
 
 

@@ -383,23 +383,25 @@ int gemv_common(const void* W, const float* scale, const void* x, int B, int N, 
 // ---- speculative accept/reject ----------------------------------------------
 
 constexpr int kSpecMaxV = 1 << 24;
-constexpr int kSpecMaxNC = kSpecStage / 2;   // chunk sums staged in LDS by the select kernel
 #ifndef DECATTN_SPEC_TARGET_BLOCKS
 #define DECATTN_SPEC_TARGET_BLOCKS 2048
 #endif
 
 struct SpecPlan {
-    int U, NC;
+    int U, NC, U2, NC2;
     size_t stats_bytes, parts_bytes, rowinfo_bytes, total_bytes;
 };
 
-// Chunks of 1024*U vocabulary entries, U in {1, 2, 4, 8}: the largest U that
-// still leaves DECATTN_SPEC_TARGET_BLOCKS first-kernel workgroups over the
-// B*T rows (small batches want many short chunks, since each workgroup's
-// latency dominates; big ones want long chunks), and at most kSpecMaxNC
-// chunks; U only grows while that cuts the chunk count. The workspace holds
-// the chunk statistics [B][T][NC], the residual chunk sums [B][NC] and one
-// float4 per row and per draft.
+// Chunks of 1024*U vocabulary entries for the statistics kernel, U in
+// {1, 2, 4, 8}: the largest U that still leaves DECATTN_SPEC_TARGET_BLOCKS
+// workgroups over the B*T rows (small batches want many short chunks, since
+// each workgroup's latency dominates; big ones want long chunks), and at most
+// kSpecMaxNC chunks; U only grows while that cuts the chunk count. The draw
+// (sampling) uses the same chunks (U2 = U): its second launch repeats the
+// decision in every workgroup, so it wants few of them at large batch, and
+// the final rescan of one chunk is cheap at any size. The workspace holds the
+// chunk statistics [B][T][NC], the draw chunks' masses [B][NC2], one float4
+// per row and one per draft.
 int spec_plan(int B, int T, int V, SpecPlan* sp) {
     if (B <= 0 || T <= 0 || V <= 0) return DECATTN_ERR_INVALID_ARG;
     if (T > kSpecMaxT || V > kSpecMaxV) return DECATTN_ERR_UNSUPPORTED;
@@ -412,8 +414,10 @@ int spec_plan(int B, int T, int V, SpecPlan* sp) {
     if (NC > kSpecMaxNC || (long long)B * T * NC > 0x7FFFFFFF) return DECATTN_ERR_UNSUPPORTED;
     sp->U = U;
     sp->NC = NC;
+    sp->U2 = U;
+    sp->NC2 = NC;
     sp->stats_bytes = round_up((size_t)B * T * NC * sizeof(float2), kAlign);
-    sp->parts_bytes = round_up((size_t)B * NC * sizeof(float2), kAlign);
+    sp->parts_bytes = round_up((size_t)B * sp->NC2 * sizeof(float2), kAlign);
     sp->rowinfo_bytes = round_up((size_t)B * sizeof(float4), kAlign);
     sp->total_bytes = sp->stats_bytes + sp->parts_bytes + sp->rowinfo_bytes +
                       round_up((size_t)B * (T > 1 ? T - 1 : 1) * sizeof(float4), kAlign);
@@ -421,19 +425,29 @@ int spec_plan(int B, int T, int V, SpecPlan* sp) {
 }
 
 template <int U, bool VEC, bool GREEDY>
-int spec_launch(const SpecParams& sp, int B, hipStream_t s) {
-    const dim3 blk(kSpecThreads);
-    hipLaunchKernelGGL((spec_stats_kernel<U, VEC, GREEDY>), dim3((unsigned)(B * sp.T * sp.NC)), blk, 0, s, sp);
-    hipLaunchKernelGGL((spec_finish_kernel<U, VEC, GREEDY>), dim3((unsigned)(GREEDY ? B : B * sp.NC)), blk, 0, s,
-                       sp);
-    if (!GREEDY) hipLaunchKernelGGL((spec_select_kernel<U, VEC>), dim3((unsigned)B), blk, 0, s, sp);
-    return hipGetLastError() == hipSuccess ? DECATTN_OK : DECATTN_ERR_HIP;
+void spec_launch_stats(const SpecParams& sp, int B, hipStream_t s) {
+    hipLaunchKernelGGL((spec_stats_kernel<U, VEC, GREEDY>), dim3((unsigned)(B * sp.T * sp.NC)), dim3(kSpecThreads), 0,
+                       s, sp);
+}
+
+template <int U, bool VEC>
+void spec_launch_draw(const SpecParams& sp, int B, hipStream_t s) {
+    hipLaunchKernelGGL((spec_resid_kernel<U, VEC>), dim3((unsigned)(B * sp.NC2)), dim3(kSpecThreads),
+                       (size_t)sp.stage_n * sizeof(float2), s, sp);
+    hipLaunchKernelGGL((spec_select_kernel<U, VEC>), dim3((unsigned)B), dim3(kSpecThreads),
+                       (size_t)sp.NC2 * sizeof(float2), s, sp);
 }
 
 template <int U>
-int spec_launch_u(const SpecParams& sp, int B, bool vec, bool greedy, hipStream_t s) {
-    if (vec) return greedy ? spec_launch<U, true, true>(sp, B, s) : spec_launch<U, true, false>(sp, B, s);
-    return greedy ? spec_launch<U, false, true>(sp, B, s) : spec_launch<U, false, false>(sp, B, s);
+void spec_launch_u(const SpecParams& sp, int B, bool vec, bool greedy, hipStream_t s) {
+    if (vec) greedy ? spec_launch_stats<U, true, true>(sp, B, s) : spec_launch_stats<U, true, false>(sp, B, s);
+    else greedy ? spec_launch_stats<U, false, true>(sp, B, s) : spec_launch_stats<U, false, false>(sp, B, s);
+}
+
+template <int U>
+void spec_launch_draw_u(const SpecParams& sp, int B, bool vec, hipStream_t s) {
+    if (vec) spec_launch_draw<U, true>(sp, B, s);
+    else spec_launch_draw<U, false>(sp, B, s);
 }
 
 }  // namespace
@@ -693,15 +707,29 @@ int spec_accept(const float* logits, const float* q, const int32_t* drafts, cons
     sp.T = T;
     sp.V = V;
     sp.NC = plan.NC;
+    sp.NC2 = plan.NC2;
+    sp.stage_n = T * plan.NC < kSpecStage ? T * plan.NC : kSpecStage;
     sp.S_max = S_max;
     const bool vec = V % 4 == 0 && aligned16(logits) && (greedy || gamma == 0 || aligned16(q));
     const hipStream_t s = static_cast<hipStream_t>(stream);
     switch (plan.U) {
-        case 1: return spec_launch_u<1>(sp, B, vec, greedy, s);
-        case 2: return spec_launch_u<2>(sp, B, vec, greedy, s);
-        case 4: return spec_launch_u<4>(sp, B, vec, greedy, s);
-        default: return spec_launch_u<8>(sp, B, vec, greedy, s);
+        case 1: spec_launch_u<1>(sp, B, vec, greedy, s); break;
+        case 2: spec_launch_u<2>(sp, B, vec, greedy, s); break;
+        case 4: spec_launch_u<4>(sp, B, vec, greedy, s); break;
+        default: spec_launch_u<8>(sp, B, vec, greedy, s); break;
     }
+    if (greedy) {
+        hipLaunchKernelGGL(spec_greedy_kernel, dim3((unsigned)B), dim3(kSpecThreads),
+                           (size_t)sp.stage_n * sizeof(float2), s, sp);
+    } else {
+        switch (plan.U2) {
+            case 1: spec_launch_draw_u<1>(sp, B, vec, s); break;
+            case 2: spec_launch_draw_u<2>(sp, B, vec, s); break;
+            case 4: spec_launch_draw_u<4>(sp, B, vec, s); break;
+            default: spec_launch_draw_u<8>(sp, B, vec, s); break;
+        }
+    }
+    return hipGetLastError() == hipSuccess ? DECATTN_OK : DECATTN_ERR_HIP;
 }
 
 int decattn_probe_read(const void* buf, size_t bytes, void* sink, void* stream) {

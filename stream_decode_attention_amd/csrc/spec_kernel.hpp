@@ -6,25 +6,27 @@
 // FlashSpec page, correctness paragraph: Leviathan et al. 2023, Algorithm 1,
 // the test taken in log space).
 //
-// Launches, no host sync:
+// Launches (no host sync):
 //   spec_stats_kernel   one workgroup per (row b, position i, vocabulary
 //                       chunk): the chunk's max logit and sum of
 //                       exp2((l - max) * log2(e) / tau), or for greedy its
-//                       largest logit and first index of it;
-//   spec_finish_kernel  per (row b, chunk): every workgroup merges the chunk
-//                       statistics of all positions of its row (the same
-//                       instructions on the same data, so every workgroup of
-//                       the row reaches the same bits) and takes the accept
-//                       decisions; it then sums the residual weights of its
-//                       chunk for the first rejected position (or p of the
-//                       bonus row). Greedy needs no residual, so its finish is
-//                       one workgroup per row and writes the result itself;
-//   spec_select_kernel  (sampling) one workgroup per row: scans the chunk sums
-//                       in index order, rescans the one chunk that holds the
-//                       draw, and writes the accept count, the token and the
-//                       new length.
-// Each kernel only reads what earlier launches wrote, so the kernel
-// boundaries order every exchange: no atomics, fences or counters.
+//                       largest logit and first index of it; the workgroup
+//                       whose chunk holds a draft's token also records that
+//                       token's logit, q and u;
+//   spec_greedy_kernel  (tau = 0) one workgroup per row: merges the chunk
+//                       statistics of every position, takes the decisions and
+//                       writes the accept count, the argmax and the length;
+//   spec_resid_kernel   (sampling) one workgroup per (row, chunk): the same
+//                       merge and decisions (the same instructions on the same
+//                       data, so every workgroup of a row reaches the same
+//                       bits), then the chunk's mass of the draw weights;
+//   spec_select_kernel  (sampling) one workgroup per row: finds the chunk
+//                       holding the draw, rescans it, writes the results.
+// Each launch reads only what earlier launches wrote, so the kernel
+// boundaries order every exchange: no atomics, fences or counters (a
+// last-arriving-workgroup scheme would need an L2 write-back per workgroup
+// to publish its chunk sum across the chip's eight L2s, which costs more
+// than the extra launch).
 #pragma once
 
 #include <climits>
@@ -38,6 +40,7 @@ constexpr int kSpecWaves = kSpecThreads / 64;
 constexpr int kSpecSeg = kSpecThreads * 4;    // elements per segment: one float4 per thread
 constexpr int kSpecMaxT = 32;                 // gamma + 1 positions: one ballot decides them all
 constexpr int kSpecStage = 4096;              // chunk statistics staged in LDS at once (float2)
+constexpr int kSpecMaxNC = kSpecStage / 2;    // chunks per position: two positions fit the stage
 
 
 struct SpecParams {
@@ -49,11 +52,13 @@ struct SpecParams {
     int32_t* lens;            // [B] in: length before the verify pass; out: after the rollback
     int32_t* result;          // [B][2]: accepted drafts, next token
     float2* stats;            // [B][T][NC]
-    float2* parts;            // [B][NC]
-    float4* rowinfo;          // [B]: max and 1/sum of the drawing position's softmax, accept count
+    float2* parts;            // [B][NC2]: each draw chunk's residual mass and p mass (sampling)
+    float4* rowinfo;          // [B]: max and 1/sum of p_n, and n (sampling)
     float4* dinfo;            // [B][T-1]: each draft's target logit, q and u, and its id (sampling)
     float c2;                 // log2(e) / tau
     int T, V, NC, S_max;
+    int NC2;                  // chunks of the draw (sampling), 1024 * U2 entries each
+    int stage_n;              // float2 entries of LDS the decision stages: min(T * NC, kSpecStage)
 };
 
 // Chunk element (j, e) of thread t has vocabulary index c0 + j*kSpecSeg + 4t + e:
@@ -83,38 +88,79 @@ __device__ __forceinline__ bool spec_better(float v, int i, float bv, int bi) {
     return bi == INT_MAX ? i != INT_MAX : (v > bv || (v == bv && i < bi));
 }
 
+// Wave-wide reductions and scans on DPP lane moves inside 16-lane rows and
+// the gfx950 lane swaps across rows (no LDS traffic). Every lane of a
+// reduction ends with the same bits.
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float& bv, int& bi) {
+    const float ov = dpp_copy<CTRL>(bv);
+    const int oi = dpp_copy_i<CTRL>(bi);
+    if (spec_better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+}
+
 __device__ __forceinline__ void wave_argmax(float& bv, int& bi) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        const float ov = __shfl_xor(bv, off);
-        const int oi = __shfl_xor(bi, off);
-        if (spec_better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-    }
+    argmax_step<kDppXor1>(bv, bi);
+    argmax_step<kDppXor2>(bv, bi);
+    argmax_step<kDppHalfMirror>(bv, bi);
+    argmax_step<kDppMirror>(bv, bi);
+    // rows (0, 1) and (2, 3), then the two halves: every lane compares the
+    // same pair in the same order
+    const f32x2 v1 = swap16(bv, bv), i1 = swap16(__int_as_float(bi), __int_as_float(bi));
+    bv = v1.x; bi = __float_as_int(i1.x);
+    if (spec_better(v1.y, __float_as_int(i1.y), bv, bi)) { bv = v1.y; bi = __float_as_int(i1.y); }
+    const f32x2 v2 = swap32(bv, bv), i2 = swap32(__int_as_float(bi), __int_as_float(bi));
+    bv = v2.x; bi = __float_as_int(i2.x);
+    if (spec_better(v2.y, __float_as_int(i2.y), bv, bi)) { bv = v2.y; bi = __float_as_int(i2.y); }
 }
 
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-    return x;
+    x = fmaxf(x, dpp_copy<kDppXor1>(x));
+    x = fmaxf(x, dpp_copy<kDppXor2>(x));
+    x = fmaxf(x, dpp_copy<kDppHalfMirror>(x));
+    x = fmaxf(x, dpp_copy<kDppMirror>(x));
+    return across_groups_max<16>(x);
 }
 
-// Butterfly sum: every lane ends with the same bits.
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-    return x;
+    return across_groups_sum<16>(group_sum<16>(x));
 }
 
-// Inclusive prefix sum over the wave. Shuffles read the source lane's
-// register only while that lane is active, so every lane must execute them.
+// Inclusive prefix sum over the wave in lane order: a shift-and-add scan
+// inside each 16-lane row (lanes shifted in from outside the row read 0),
+// then each row adds the totals of the rows before it.
 __device__ __forceinline__ float wave_incl_scan(float x) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const float o = __shfl_up(x, d);
-        if (lane >= d) x += o;
+    x += dpp_move<0x111>(x);          // row_shr:1
+    x += dpp_move<0x112>(x);          // row_shr:2
+    x += dpp_move<0x114>(x);          // row_shr:4
+    x += dpp_move<0x118>(x);          // row_shr:8
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 15));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 31));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 47));
+    const float o2 = r0 + r1, o3 = o2 + r2;
+    const int row = (threadIdx.x & 63) >> 4;
+    return row == 0 ? x : x + (row == 1 ? r0 : (row == 2 ? o2 : o3));
+}
+
+// Runs of consecutive entries are laid out by lane in index order, so the
+// first candidate of a wave is the lowest lane's and the last positive entry
+// the highest lane's: one LDS atomic per wave instead of one per lane (those
+// on one word serialize).
+__device__ __forceinline__ void wave_first_min(int* dst, int v, bool has) {
+    const unsigned long long m = __ballot(has);
+    if (m) {
+        const int L = __ffsll(m) - 1;
+        const int x = __shfl(v, L);
+        if ((threadIdx.x & 63) == 0) atomicMin(dst, x);
     }
-    return x;
+}
+
+__device__ __forceinline__ void wave_last_max(int* dst, int v, bool has) {
+    const unsigned long long m = __ballot(has);
+    if (m) {
+        const int L = 63 - __clzll((long long)m);
+        const int x = __shfl(v, L);
+        if ((threadIdx.x & 63) == 0) atomicMax(dst, x);
+    }
 }
 
 // Rescale a partial sum s taken relative to max m onto the max M >= m.
@@ -204,20 +250,22 @@ __device__ __forceinline__ int spec_new_len(int ctx, int n, int s_max) {
     return v > s_max ? s_max : (int)v;
 }
 
-template <int U, bool VEC, bool GREEDY>
-__global__ __launch_bounds__(kSpecThreads) void spec_finish_kernel(const SpecParams p) {
-    constexpr int CH = U * kSpecSeg;
-    const int NCB = GREEDY ? 1 : p.NC;
-    const int c = blockIdx.x % NCB, b = blockIdx.x / NCB;
-    const int T = p.T, gamma = T - 1, V = p.V;
+
+// Merge the chunk statistics of every position of row b and take the accept
+// decisions; returns n, the number of drafts kept, in every thread. Fills
+// row_m/row_s (sampling: max logit and sum of exp2((l - max) * c2)) or row_i
+// (greedy: first index of the largest logit). `stage` holds p.stage_n
+// float2 (dynamic LDS). Whole positions are staged in LDS with one batch of
+// loads, then one wave merges each position.
+template <int WAVES, bool GREEDY>
+__device__ __forceinline__ int spec_decide(const SpecParams& p, int b, float2* stage, float* row_m, float* row_s,
+                                           int* row_i, int* sh_n) {
+    const int T = p.T, gamma = T - 1, V = p.V, NC = p.NC;
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-    __shared__ float row_m[kSpecMaxT], row_s[kSpecMaxT];
-    __shared__ int row_i[kSpecMaxT];
-    __shared__ int sh_n;
 
     // the draft side of each position (threads t < gamma, all in wave 0):
     // its token id and, for sampling, the target logit, q and u at that id
-    // as the first kernel recorded them
+    // as the statistics kernel recorded them
     int d = -1;
     float ld = 0.f, qd = 0.f, ud = 0.f;
     if (t < gamma) {
@@ -230,19 +278,15 @@ __global__ __launch_bounds__(kSpecThreads) void spec_finish_kernel(const SpecPar
         }
     }
 
-    // merge the chunk statistics of every position: stage tiles of whole
-    // positions in LDS (one batch of loads), then one wave per position
-    __shared__ float2 st_lds[kSpecStage];
-    const int NC = p.NC;
-    const int rpt = kSpecStage / NC;                  // NC <= kSpecStage / 2
+    const int rpt = p.stage_n / NC;                   // >= 1: stage_n >= min(T, 2) * NC
     for (int i0 = 0; i0 < T; i0 += rpt) {
         const int nr = T - i0 < rpt ? T - i0 : rpt;
         const float2* src = p.stats + ((size_t)b * T + i0) * NC;
 #pragma unroll 4
-        for (int e = t; e < nr * NC; e += kSpecThreads) st_lds[e] = src[e];
+        for (int e = t; e < nr * NC; e += WAVES * 64) stage[e] = src[e];
         __syncthreads();
-        for (int i = i0 + w; i < i0 + nr; i += kSpecWaves) {
-            const float2* st = st_lds + (size_t)(i - i0) * NC;
+        for (int i = i0 + w; i < i0 + nr; i += WAVES) {
+            const float2* st = stage + (size_t)(i - i0) * NC;
             if constexpr (GREEDY) {
                 float bv = kNegInf;
                 int bi = INT_MAX;
@@ -282,195 +326,195 @@ __global__ __launch_bounds__(kSpecThreads) void spec_finish_kernel(const SpecPar
             }
         }
         const unsigned long long rej = __ballot(lane < gamma && !keep);
-        if (lane == 0) sh_n = rej ? __ffsll(rej) - 1 : gamma;
+        if (lane == 0) *sh_n = rej ? __ffsll(rej) - 1 : gamma;
     }
     __syncthreads();
-    const int n = sh_n;
+    return *sh_n;
+}
 
-    if constexpr (GREEDY) {
-        if (t == 0) {
-            p.result[2 * (size_t)b] = n;
-            p.result[2 * (size_t)b + 1] = row_i[n];
-            p.lens[b] = spec_new_len(p.lens[b], n, p.S_max);
-        }
-        return;
-    } else {
-        const float M = row_m[n];
-        const float inv_s = 1.0f / row_s[n];
-        const bool bonus = n == gamma;
-        const float* lrow = p.logits + ((size_t)b * T + n) * V;
-        const float* qrow = bonus ? nullptr : p.q + ((size_t)b * gamma + n) * V;
-
-        // this chunk's residual mass and p mass, summed in a fixed order
-        {
-            float x[4 * U], y[4 * U];
-            spec_load<U, VEC>(lrow, V, c * CH, kNegInf, x);
-            if (bonus) {
-#pragma unroll
-                for (int k = 0; k < 4 * U; ++k) y[k] = 0.f;
-            } else {
-                spec_load<U, VEC>(qrow, V, c * CH, 0.f, y);
-            }
-            float ws = 0.f, ps = 0.f;
-#pragma unroll
-            for (int k = 0; k < 4 * U; ++k) {
-                ws += spec_weight(x[k], y[k], M, p.c2, inv_s, bonus);
-                ps += spec_weight(x[k], 0.f, M, p.c2, inv_s, true);
-            }
-            ws = wave_sum(ws);
-            ps = wave_sum(ps);
-            __shared__ float sh_w[kSpecWaves], sh_p[kSpecWaves];
-            if (lane == 0) { sh_w[w] = ws; sh_p[w] = ps; }
-            __syncthreads();
-            if (t == 0) {
-                float a = 0.f, e = 0.f;
-                for (int k = 0; k < kSpecWaves; ++k) { a += sh_w[k]; e += sh_p[k]; }
-                p.parts[(size_t)b * p.NC + c] = make_float2(a, e);
-            }
-        }
-
-        if (c == 0 && t == 0) p.rowinfo[b] = make_float4(M, inv_s, __int_as_float(n), 0.f);
+// Greedy finish: one workgroup per row writes n, the argmax of position n and
+// the new length.
+__global__ __launch_bounds__(kSpecThreads) void spec_greedy_kernel(const SpecParams p) {
+    extern __shared__ float2 stage[];
+    __shared__ float row_m[kSpecMaxT], row_s[kSpecMaxT];
+    __shared__ int row_i[kSpecMaxT], sh_n;
+    const int b = blockIdx.x;
+    const int ctx = p.lens[b];
+    const int n = spec_decide<kSpecWaves, true>(p, b, stage, row_m, row_s, row_i, &sh_n);
+    if (threadIdx.x == 0) {
+        p.result[2 * (size_t)b] = n;
+        p.result[2 * (size_t)b + 1] = row_i[n];
+        p.lens[b] = spec_new_len(ctx, n, p.S_max);
     }
 }
 
+// Sampling, second launch: per (row b, chunk c of the draw's own chunking),
+// the decision, then the chunk's mass of the draw weights: the residual
+// max(0, p_n - q_n) of the first rejected position n (and p_n, for a
+// residual with no positive mass), or p of the bonus row. Chunk 0 also
+// records n, the max and 1 / sum of p_n.
+
+template <int U, bool VEC>
+__global__ __launch_bounds__(kSpecThreads) void spec_resid_kernel(const SpecParams p) {
+    constexpr int CH = U * kSpecSeg;
+    extern __shared__ float2 stage[];
+    __shared__ float row_m[kSpecMaxT], row_s[kSpecMaxT];
+    __shared__ int row_i[kSpecMaxT], sh_n;
+    __shared__ float sh_w[kSpecWaves], sh_p[kSpecWaves];
+    const int c = blockIdx.x % p.NC2, b = blockIdx.x / p.NC2;
+    const int T = p.T, gamma = T - 1, V = p.V;
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const float* lrows = p.logits + (size_t)b * T * V;
+    const float* qrows = p.q + (size_t)b * gamma * V;
+    const int n = spec_decide<kSpecWaves, false>(p, b, stage, row_m, row_s, row_i, &sh_n);
+    float x[4 * U], y[4 * U];
+    spec_load<U, VEC>(lrows + (size_t)n * V, V, c * CH, kNegInf, x);
+    if (n < gamma) spec_load<U, VEC>(qrows + (size_t)n * V, V, c * CH, 0.f, y);
+    const float M = row_m[n];
+    const float inv_s = 1.0f / row_s[n];
+    const bool bonus = n == gamma;
+    float ws = 0.f, ps = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4 * U; ++k) {
+        ws += spec_weight(x[k], bonus ? 0.f : y[k], M, p.c2, inv_s, bonus);
+        ps += spec_weight(x[k], 0.f, M, p.c2, inv_s, true);
+    }
+    ws = wave_sum(ws);
+    ps = wave_sum(ps);
+    if (lane == 0) { sh_w[w] = ws; sh_p[w] = ps; }
+    __syncthreads();
+    if (t == 0) {
+        float a = 0.f, e = 0.f;
+        for (int k = 0; k < kSpecWaves; ++k) { a += sh_w[k]; e += sh_p[k]; }
+        p.parts[(size_t)b * p.NC2 + c] = make_float2(a, e);
+        if (c == 0) p.rowinfo[b] = make_float4(M, inv_s, __int_as_float(n), 0.f);
+    }
+}
+
+// Sampling, third launch: one workgroup per row draws the token. Thread t
+// takes the chunks [t*RC, t*RC + RC) in index order; a block-wide running
+// sum over those runs finds the first chunk whose running mass passes
+// r * total, which is then rescanned entry by entry the same way.
 template <int U, bool VEC>
 __global__ __launch_bounds__(kSpecThreads) void spec_select_kernel(const SpecParams p) {
     constexpr int CH = U * kSpecSeg;
+    constexpr int R = CH / kSpecThreads;
+    extern __shared__ float2 pr[];                      // p.NC2 entries
+    __shared__ __attribute__((aligned(16))) float wbuf[CH];
+    __shared__ float sh_tw[kSpecWaves], sh_tp[kSpecWaves], sh_base;
+    __shared__ int sh_pick, sh_last;
     const int b = blockIdx.x;
-    const int T = p.T, gamma = T - 1, V = p.V;
+    const int T = p.T, gamma = T - 1, V = p.V, NC = p.NC2;
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+
+    // everything read here was written by earlier launches or is an input:
+    // one batch of loads
     const float4 info = p.rowinfo[b];
+    const float rb = p.r[b];
+    const int ctx = p.lens[b];
+    {
+        const float2* src = p.parts + (size_t)b * NC;
+#pragma unroll 4
+        for (int e = t; e < NC; e += kSpecThreads) pr[e] = src[e];
+    }
+    if (t == 0) { sh_pick = INT_MAX; sh_last = -1; }
+    __syncthreads();
     const float M = info.x, inv_s = info.y;
     const int n = __float_as_int(info.z);
     const bool bonus = n == gamma;
-    const float* lrow = p.logits + ((size_t)b * T + n) * V;
-    const float* qrow = bonus ? nullptr : p.q + ((size_t)b * gamma + n) * V;
 
-    // which chunk holds the draw: running sums over chunks in index order,
-    // from the chunk sums staged in LDS
-    __shared__ int sh_c, sh_mode, sh_use_p;
-    __shared__ float sh_t, sh_base;
-    __shared__ float2 pr[kSpecStage / 2];
-    {
-        const float2* src = p.parts + (size_t)b * p.NC;
-#pragma unroll 4
-        for (int e = t; e < p.NC; e += kSpecThreads) pr[e] = src[e];
-    }
+    // the chunk: per-thread masses, block running sum, each thread walks its run
+    const int RC = (NC + kSpecThreads - 1) / kSpecThreads;
+    const int k0 = t * RC < NC ? t * RC : NC, k1 = k0 + RC < NC ? k0 + RC : NC;
+    float aw = 0.f, ap = 0.f;
+    for (int k = k0; k < k1; ++k) { aw += pr[k].x; ap += pr[k].y; }
+    const float iw = wave_incl_scan(aw), ip = wave_incl_scan(ap);
+    const float uw = __shfl_up(iw, 1), up = __shfl_up(ip, 1);
+    if (lane == 63) { sh_tw[w] = iw; sh_tp[w] = ip; }
     __syncthreads();
-    if (w == 0) {
-        float tw = 0.f, tp = 0.f;                     // totals, by the same scan as below
-        for (int k0 = 0; k0 < p.NC; k0 += 64) {
-            const int k = k0 + lane;
-            const float2 v = k < p.NC ? pr[k] : make_float2(0.f, 0.f);
-            tw += __shfl(wave_incl_scan(v.x), 63);
-            tp += __shfl(wave_incl_scan(v.y), 63);
+    float tw = 0.f, tp = 0.f;
+    for (int k = 0; k < kSpecWaves; ++k) { tw += sh_tw[k]; tp += sh_tp[k]; }
+    // a residual with no positive mass (only through rounding): draw from p
+    const bool use_p = bonus || !(tw > 0.f);
+    const float thr = rb * (use_p ? tp : tw);
+    float run = 0.f;
+    for (int k = 0; k < w; ++k) run += use_p ? sh_tp[k] : sh_tw[k];
+    run += lane ? (use_p ? up : uw) : 0.f;
+    int cand = INT_MAX, lastp = -1;
+    float cbase = 0.f;
+    for (int k = k0; k < k1; ++k) {
+        const float v = use_p ? pr[k].y : pr[k].x;
+        if (v > 0.f) {
+            lastp = k;
+            if (cand == INT_MAX && run + v > thr) { cand = k; cbase = run; }
         }
-        const bool use_p = bonus || !(tw > 0.f);
-        const float total = use_p ? tp : tw;
-        const float thr = p.r[b] * total;
-        int found = -1, last_pos = -1;
-        float base = 0.f, carry = 0.f;
-        for (int k0 = 0; k0 < p.NC; k0 += 64) {
-            const int k = k0 + lane;
-            const float2 v2 = k < p.NC ? pr[k] : make_float2(0.f, 0.f);
-            const float v = use_p ? v2.y : v2.x;
-            const float inc = wave_incl_scan(v);
-            const float cum = carry + inc;
-            const float up = __shfl_up(inc, 1);          // every lane takes part in the shuffle
-            const float excl = carry + (lane ? up : 0.f);
-            const unsigned long long hit = __ballot(k < p.NC && v > 0.f && cum > thr);
-            if (hit) {
-                const int L = __ffsll(hit) - 1;
-                found = k0 + L;
-                base = __shfl(excl, L);
-                break;
-            }
-            const unsigned long long pos = __ballot(k < p.NC && v > 0.f);
-            if (pos) last_pos = k0 + 63 - __clzll(pos);
-            carry += __shfl(inc, 63);
-        }
-        if (lane == 0) {
-            sh_use_p = use_p;
-            sh_t = thr;
-            sh_base = base;
-            // 0: first entry whose running sum passes thr; 1: rounding left
-            // thr at or past the total, take the last positive entry;
-            // 2: no positive weight at all (rows that break the input rules)
-            sh_mode = found >= 0 ? 0 : (last_pos >= 0 ? 1 : 2);
-            sh_c = found >= 0 ? found : (last_pos >= 0 ? last_pos : 0);
-        }
+        run += v;
     }
+    wave_first_min(&sh_pick, cand, cand != INT_MAX);
+    wave_last_max(&sh_last, lastp, lastp >= 0);
+    __syncthreads();
+    if (cand != INT_MAX && cand == sh_pick) sh_base = cbase;
+    // 0: first chunk whose running mass passes thr; 1: rounding left thr at
+    // or past the total, take the last positive entry; 2: no positive weight
+    // at all (rows that break the input rules)
+    const int mode = sh_pick != INT_MAX ? 0 : (sh_last >= 0 ? 1 : 2);
+    const int cs = mode == 0 ? sh_pick : (mode == 1 ? sh_last : 0);
     __syncthreads();
 
-    // rescan the chosen chunk: its weights into LDS in index order; thread t
-    // then owns the run of R consecutive entries [tR, tR + R), adds the
-    // running sum of the runs before it to the chunk's base, and walks its
-    // run; the first entry (smallest index) whose running sum passes thr wins
-    constexpr int R = CH / kSpecThreads;
-    __shared__ __attribute__((aligned(16))) float wbuf[CH];
-    __shared__ int sh_lastpos, sh_pick;
-    __shared__ float sh_wtot[kSpecWaves];
-    if (t == 0) { sh_lastpos = -1; sh_pick = INT_MAX; }
-    __syncthreads();
-    const int cs = sh_c, mode = sh_mode;
-    const bool use_p = sh_use_p;
+    // the chunk's weights into LDS in index order; thread t walks [tR, tR + R)
     {
         float x[4 * U], y[4 * U];
-        spec_load<U, VEC>(lrow, V, cs * CH, kNegInf, x);
+        spec_load<U, VEC>(p.logits + ((size_t)b * T + n) * V, V, cs * CH, kNegInf, x);
         if (bonus) {
 #pragma unroll
             for (int k = 0; k < 4 * U; ++k) y[k] = 0.f;
         } else {
-            spec_load<U, VEC>(qrow, V, cs * CH, 0.f, y);
+            spec_load<U, VEC>(p.q + ((size_t)b * gamma + n) * V, V, cs * CH, 0.f, y);
         }
-        int lp = -1;
 #pragma unroll
         for (int j = 0; j < U; ++j)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int li = j * kSpecSeg + 4 * t + e;
-                const float wk = spec_weight(x[4 * j + e], y[4 * j + e], M, p.c2, inv_s, use_p);
-                wbuf[li] = wk;
-                if (wk > 0.f) lp = li > lp ? li : lp;
-            }
-        if (lp >= 0) atomicMax(&sh_lastpos, lp);
+            for (int e = 0; e < 4; ++e)
+                wbuf[j * kSpecSeg + 4 * t + e] = spec_weight(x[4 * j + e], y[4 * j + e], M, p.c2, inv_s, use_p);
     }
+    if (t == 0) { sh_pick = INT_MAX; sh_last = -1; }
     __syncthreads();
-    float run[R];
+    float rw[R];
 #pragma unroll
     for (int k = 0; k < R; k += 4) {
         const float4 v = *reinterpret_cast<const float4*>(&wbuf[t * R + k]);
-        run[k] = v.x; run[k + 1] = v.y; run[k + 2] = v.z; run[k + 3] = v.w;
+        rw[k] = v.x; rw[k + 1] = v.y; rw[k + 2] = v.z; rw[k + 3] = v.w;
     }
     float rs = 0.f;
 #pragma unroll
-    for (int k = 0; k < R; ++k) rs += run[k];
+    for (int k = 0; k < R; ++k) rs += rw[k];
     const float inc = wave_incl_scan(rs);
-    const float up = __shfl_up(inc, 1);
-    if (lane == 63) sh_wtot[w] = inc;
+    const float upe = __shfl_up(inc, 1);
+    if (lane == 63) sh_tw[w] = inc;
     __syncthreads();
-    if (mode == 0) {
-        float c = sh_base;
-        for (int k = 0; k < w; ++k) c += sh_wtot[k];
-        c += lane ? up : 0.f;
-        const float thr = sh_t;
-        int cand = INT_MAX;
+    float c2 = sh_base;
+    for (int k = 0; k < w; ++k) c2 += sh_tw[k];
+    c2 += lane ? upe : 0.f;
+    int pick = INT_MAX, lp = -1;
 #pragma unroll
-        for (int k = 0; k < R; ++k) {
-            c += run[k];
-            if (cand == INT_MAX && run[k] > 0.f && c > thr) cand = t * R + k;
+    for (int k = 0; k < R; ++k) {
+        c2 += rw[k];
+        if (rw[k] > 0.f) {
+            lp = t * R + k;
+            if (mode == 0 && pick == INT_MAX && c2 > thr) pick = t * R + k;
         }
-        if (cand != INT_MAX) atomicMin(&sh_pick, cand);
     }
+    wave_first_min(&sh_pick, pick, pick != INT_MAX);
+    wave_last_max(&sh_last, lp, lp >= 0);
     __syncthreads();
     if (t == 0) {
         // no entry passed thr (rounding in the last chunk, or modes 1 and 2):
         // the chunk's last positive entry
-        int pick = sh_pick != INT_MAX ? sh_pick : (mode == 2 ? 0 : sh_lastpos);
-        if (pick < 0) pick = 0;
+        int k = sh_pick != INT_MAX ? sh_pick : (mode == 2 ? 0 : sh_last);
+        if (k < 0) k = 0;
         p.result[2 * (size_t)b] = n;
-        p.result[2 * (size_t)b + 1] = cs * CH + pick;
-        p.lens[b] = spec_new_len(p.lens[b], n, p.S_max);
+        p.result[2 * (size_t)b + 1] = cs * CH + k;
+        p.lens[b] = spec_new_len(ctx, n, p.S_max);
     }
 }
 

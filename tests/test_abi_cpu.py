@@ -223,11 +223,14 @@ def test_spec_workspace_bytes(lib):
     w = lib.spec_accept_workspace_bytes
     assert w(1, 6, 128256) > 0 and w(0, 6, 100) == 0 and w(1, 0, 100) == 0 and w(1, 6, 0) == 0
     assert w(1, 33, 100) == 0 and w(1, 6, (1 << 24) + 1) == 0
-    # at least the chunk statistics of every position, the chunk sums and a counter per row
+    # the chunk statistics of every position and the residual mass of every
+    # chunk (8 bytes per chunk of 1024 to 8192 entries), 16 bytes per row and
+    # per draft, each rounded up to 256 bytes
     for B, T, V in [(1, 6, 128256), (64, 6, 128256), (3, 1, 50257), (8, 32, 1 << 24)]:
         nc_max = -(-V // 1024)
         nc_min = -(-V // 8192)
-        assert (B * T * nc_min + B * nc_min) * 8 + 4 * B <= w(B, T, V) <= (B * T * nc_max + B * nc_max) * 8 + 4 * B + 768
+        small = 16 * B + 16 * B * max(T - 1, 1)
+        assert (B * T + B) * nc_min * 8 + small <= w(B, T, V) <= (B * T + B) * nc_max * 8 + small + 1024
         assert w(B, T, V) % 256 == 0
 
 
