@@ -18,7 +18,10 @@ the same launches with every length 0. "one_call_per_graph" reports a graph
 of a single call, warm and after a 1 GiB read that evicts the Infinity Cache,
 with its own floor (each graph launch costs several µs on its own). The
 partial kernel alone is replayed the same way for the roofline entry. The
-other four workloads are timed the same way and reported under "workloads".
+other four workloads are timed the same way and reported under "workloads";
+the steps around attention (rope_kv_write, prefill_attn, the GEMV weight
+products, the speculative accept/reject step spec_accept) under their own
+keys.
 The fp64 CPU oracle is timed on the headline workload on this host as
 "cpu_baseline".
 

@@ -64,7 +64,14 @@ struct SpecParams {
 // Chunk element (j, e) of thread t has vocabulary index c0 + j*kSpecSeg + 4t + e:
 // each segment j is one coalesced float4 read by the workgroup. Indices at or
 // past V read as `fill`.
-template <int U, bool VEC>
+// STREAM marks data read once (the statistics pass over every position):
+// non-temporal loads, which keep it from displacing what is read again.
+#ifndef DECATTN_SPEC_NT
+#define DECATTN_SPEC_NT 1
+#endif
+typedef float spec_f4 __attribute__((ext_vector_type(4)));
+
+template <int U, bool VEC, bool STREAM = false>
 __device__ __forceinline__ void spec_load(const float* __restrict__ row, int V, int c0, float fill,
                                           float (&x)[4 * U]) {
     const int t = threadIdx.x;
@@ -72,8 +79,11 @@ __device__ __forceinline__ void spec_load(const float* __restrict__ row, int V, 
     for (int j = 0; j < U; ++j) {
         const int e0 = c0 + j * kSpecSeg + 4 * t;
         if constexpr (VEC) {
-            float4 v = make_float4(fill, fill, fill, fill);
-            if (e0 < V) v = *reinterpret_cast<const float4*>(row + e0);     // V % 4 == 0 here
+            spec_f4 v = {fill, fill, fill, fill};
+            if (e0 < V) {                                                   // V % 4 == 0 here
+                const spec_f4* src = reinterpret_cast<const spec_f4*>(row + e0);
+                v = (STREAM && DECATTN_SPEC_NT) ? __builtin_nontemporal_load(src) : *src;
+            }
             x[4 * j] = v.x; x[4 * j + 1] = v.y; x[4 * j + 2] = v.z; x[4 * j + 3] = v.w;
         } else {
 #pragma unroll
@@ -182,7 +192,7 @@ __global__ __launch_bounds__(kSpecThreads) void spec_stats_kernel(const SpecPara
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int c0 = c * (U * kSpecSeg);
     float x[4 * U];
-    spec_load<U, VEC>(p.logits + (size_t)row * p.V, p.V, c0, kNegInf, x);
+    spec_load<U, VEC, true>(p.logits + (size_t)row * p.V, p.V, c0, kNegInf, x);
     __shared__ float sh_v[kSpecWaves], sh_s[kSpecWaves];
     __shared__ int sh_i[kSpecWaves];
     if constexpr (GREEDY) {

@@ -42,3 +42,27 @@ def test_ragged_lengths_in_range():
     assert lens.dtype == np.int32 and lens.shape == (8,)
     assert lens.min() >= 1 and lens.max() <= 32768
     assert np.array_equal(lens, workloads.ragged_lens(4, 8, 32768))
+
+
+def test_spec_sampling_case_shapes_and_ranges():
+    c = workloads.spec_sampling_case(3, 5, 1000, seed=1)
+    assert c["logits"].shape == (3, 5, 1000) and c["logits"].dtype == np.float32
+    assert c["q"].shape == (3, 4, 1000) and c["q"].dtype == np.float32
+    assert np.allclose(c["q"].astype(np.float64).sum(-1), 1.0, atol=1e-5) and np.all(c["q"] >= 0)
+    assert c["drafts"].shape == (3, 4) and np.all((c["drafts"] >= 0) & (c["drafts"] < 1000))
+    assert np.all((c["u"] >= 0) & (c["u"] < 1)) and np.all((c["r"] >= 0) & (c["r"] < 1))
+    assert c["tau"] == float(np.float32(c["tau"]))
+    d = workloads.spec_sampling_case(3, 5, 1000, seed=1)
+    assert all(np.array_equal(c[k], d[k]) for k in ("logits", "q", "drafts", "u", "r", "ctx"))
+
+
+def test_spec_greedy_case_plants_the_top_tokens():
+    c = workloads.spec_greedy_case(6, 5, 300, seed=2)
+    for b in range(6):
+        for i in range(5):
+            row = c["logits"][b, i]
+            assert int(np.flatnonzero(row == row.max())[0]) == c["top"][b, i]
+        m = c["m"][b]
+        assert list(c["drafts"][b, :m]) == list(c["top"][b, :m])
+        if m < 4:
+            assert c["drafts"][b, m] != c["top"][b, m]
