@@ -367,6 +367,29 @@ int gemv_common(const void* W, const float* scale, const void* x, int B, int N, 
     gp.out_bf16 = out_dtype == DECATTN_OUT_BF16;
     const size_t osz = gp.out_bf16 ? 2 : 4;
     const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (B >= (int8 ? DECATTN_GEMV_MFMA_MIN_B_INT8 : DECATTN_GEMV_MFMA_MIN_B_BF16)) {
+        // the matrix cores: every vector in one pass over the weights
+        if ((size_t)B * K * 2 + 16 >= (1ull << 32)) return DECATTN_ERR_UNSUPPORTED;
+        GemvMfmaParams mp{};
+        mp.W = W;
+        mp.scale = scale;
+        mp.x = static_cast<const uint16_t*>(x);
+        mp.y = y;
+        mp.out_bf16 = gp.out_bf16;
+        mp.B = B;
+        mp.N = N;
+        mp.K = K;
+        mp.row_bytes = (uint32_t)K * (int8 ? 1 : 2);
+        const unsigned grid = (unsigned)((N + 15) / 16);
+        const size_t lds = (size_t)kGemvMfmaWaves * 16 * kGemvPitch;
+        const void* fn = int8 ? reinterpret_cast<const void*>(&gemv_mfma_kernel<1, true>)
+                              : reinterpret_cast<const void*>(&gemv_mfma_kernel<1, false>);
+        // sets the dynamic-LDS limit of this kernel on the current device (cached)
+        if (resident_blocks(fn, kGemvMfmaThreads, lds) <= 0) return DECATTN_ERR_HIP;
+        if (int8) hipLaunchKernelGGL((gemv_mfma_kernel<1, true>), dim3(grid), dim3(kGemvMfmaThreads), lds, s, mp);
+        else hipLaunchKernelGGL((gemv_mfma_kernel<1, false>), dim3(grid), dim3(kGemvMfmaThreads), lds, s, mp);
+        return hipGetLastError() == hipSuccess ? DECATTN_OK : DECATTN_ERR_HIP;
+    }
     for (int b0 = 0; b0 < B; b0 += bmax) {
         const int nb = B - b0 < bmax ? B - b0 : bmax;
         gp.x = static_cast<const uint16_t*>(x) + (size_t)b0 * K;

@@ -207,6 +207,162 @@ gemv_kernel(const GemvParams p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core path for more vectors (B >= 5 bf16, B >= 4 INT8): y^T = W x^T as
+// 16 x 16 x 32 bf16 products (v_mfma_f32_16x16x32_bf16): 16 weight rows by
+// 32 k times 32 k by 16 vectors (columns past B are zero). Each activation
+// fragment then serves 16 weight rows, where the dot-product path reads it
+// once per row and is bound by those reads at B = 8; the multiplies cost
+// nothing next to the weight stream.
+//
+// A workgroup of 8 waves owns 16 * RT rows (RT = 1: two tiles cost
+// registers, and spilled, for no gain); the waves split K into 8 ranges
+// of 512-byte blocks, and the 8 partial 16 x 16 results are summed in a
+// fixed order through LDS. Activation fragments (vector lane % 16, 8 k per
+// lane) come straight from L2. Masked lanes (k past K, vectors past B,
+// blocks past the wave's range) read at the end of a buffer resource's
+// range, which returns zeros (the host keeps every range and offset + 16
+// below 2^32): every load is issued without a branch. INT8 codes are widened
+// to exact bf16 as the fragments are read.
+typedef __bf16 gemv_bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float gemv_f32x4_t __attribute__((ext_vector_type(4)));
+
+// Measured on MI355X over one Llama-3-8B layer (GB/s of weights, dot-product
+// path / matrix cores): bf16 B = 4 4791 / 4624, B = 8 2967 / 4302; INT8
+// B = 3 3438 / 3276, B = 4 3108 / 3257, B = 8 1809 / 3056.
+#ifndef DECATTN_GEMV_MFMA_MIN_B_BF16
+#define DECATTN_GEMV_MFMA_MIN_B_BF16 5
+#endif
+#ifndef DECATTN_GEMV_MFMA_MIN_B_INT8
+#define DECATTN_GEMV_MFMA_MIN_B_INT8 4
+#endif
+constexpr int kGemvMfmaWaves = 8;
+constexpr int kGemvMfmaThreads = 64 * kGemvMfmaWaves;
+#ifndef DECATTN_GEMV_MFMA_U
+#define DECATTN_GEMV_MFMA_U 4
+#endif
+constexpr int kGemvMfmaU = DECATTN_GEMV_MFMA_U;
+
+struct GemvMfmaParams {
+    const void* W;            // bf16 [N][K] or int8 [N][K]
+    const float* scale;       // [N], INT8 weights only
+    const uint16_t* x;        // bf16 [B][K]
+    void* y;                  // [B][N], fp32 or bf16
+    int out_bf16;
+    int B, N, K;
+    uint32_t row_bytes;       // K * 2 (bf16) or K (int8)
+};
+
+__device__ __forceinline__ gemv_bf16x8_t gemv_frag(uint4 v) { return __builtin_bit_cast(gemv_bf16x8_t, v); }
+
+// Weight rows go through LDS: each wave loads blocks of 256 k of each of its
+// rows (512 bytes bf16, 256 bytes INT8; 2 or 4 rows of whole 128-byte lines
+// per instruction) with the block's activation fragments, the next block's
+// loads in flight while the current one is stored to the wave's own LDS
+// tile and read back as MFMA fragments (16 rows x 64 or 32 bytes per read).
+constexpr int kGemvPitch = 512 + 16;         // LDS row pitch (bank spread)
+
+template <int RT, bool INT8>
+__global__ void __launch_bounds__(kGemvMfmaThreads)
+gemv_mfma_kernel(const GemvMfmaParams p) {
+    constexpr int ESZ = INT8 ? 1 : 2;              // bytes per weight
+    constexpr int BLK = INT8 ? 256 : 512;          // bytes of a row per block
+    constexpr int BLK_K = BLK / ESZ;               // k per block (256)
+    constexpr int LPRW = BLK / 16;                 // lanes per row in a load
+    constexpr int RPL = 64 / LPRW;                 // rows per load instruction
+    constexpr int NLD = 16 * RT / RPL;             // 16-byte weight loads per lane per block
+    constexpr int STEPS = BLK_K / 32;              // MFMA k-steps per block (8)
+    extern __shared__ __align__(16) char gemv_lds[];            // [waves][16 RT][kGemvPitch]
+    __shared__ float red[kGemvMfmaWaves][RT][16][16];           // [wave][tile][vector][row]
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int i = lane & 15, g = lane >> 4;
+    char* tile = gemv_lds + (size_t)wave * 16 * RT * kGemvPitch;
+    const int row0 = (int)blockIdx.x * 16 * RT;
+    const int nblk = (p.K + BLK_K - 1) / BLK_K;
+    const int b0 = (int)((long long)wave * nblk / kGemvMfmaWaves);
+    const int b1 = (int)((long long)(wave + 1) * nblk / kGemvMfmaWaves);
+    const uint32_t w_end = (uint32_t)((size_t)p.N * p.row_bytes), x_end = (uint32_t)((size_t)p.B * p.K * 2);
+    const __amdgpu_buffer_rsrc_t wrs = make_rsrc(p.W, w_end);
+    const __amdgpu_buffer_rsrc_t xrs = make_rsrc(p.x, x_end);
+    const bool xl = i < p.B;
+    // load lane layout: load j covers rows RPL j .. RPL j + RPL - 1 of the
+    // block, this lane's 16 bytes at column 16 * (lane % LPRW)
+    const int lrow = lane / LPRW, lcol = (lane % LPRW) * 16;
+
+    gemv_f32x4_t acc[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) acc[r] = (gemv_f32x4_t){0.f, 0.f, 0.f, 0.f};
+
+    // a block's weights and activation fragments, all issued together
+    auto load = [&](uint4 (&w)[NLD], uint4 (&xv)[STEPS], int blk) {
+        const int kb = blk * BLK + lcol;           // byte offset in the row
+        const bool in = blk < b1 && kb < (int)p.row_bytes;
+#pragma unroll
+        for (int j = 0; j < NLD; ++j) {
+            const uint32_t off = (uint32_t)(row0 + RPL * j + lrow) * p.row_bytes + (uint32_t)kb;
+            w[j] = buffer_load16_policy<DECATTN_GEMV_POLICY>(wrs, in ? off : w_end);
+        }
+#pragma unroll
+        for (int t = 0; t < STEPS; ++t) {
+            const int k = blk * BLK_K + 32 * t + 8 * g;
+            xv[t] = buffer_load16_policy<0>(xrs, blk < b1 && xl && k < p.K ? (uint32_t)(i * p.K + k) * 2 : x_end);
+        }
+    };
+    auto block = [&](const uint4 (&w)[NLD], const uint4 (&xv)[STEPS]) {
+#pragma unroll
+        for (int j = 0; j < NLD; ++j)
+            *reinterpret_cast<uint4*>(tile + (RPL * j + lrow) * kGemvPitch + lcol) = w[j];
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int t = 0; t < STEPS; ++t) {
+#pragma unroll
+            for (int r = 0; r < RT; ++r) {
+                const char* src = tile + (16 * r + i) * kGemvPitch + (32 * t + 8 * g) * ESZ;
+                uint4 a;
+                if constexpr (INT8) {
+                    const uint2 c = *reinterpret_cast<const uint2*>(src);
+                    a = make_uint4(int8x2_to_bf16x2(c.x, 0), int8x2_to_bf16x2(c.x, 16),
+                                   int8x2_to_bf16x2(c.y, 0), int8x2_to_bf16x2(c.y, 16));
+                } else {
+                    a = *reinterpret_cast<const uint4*>(src);
+                }
+                acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gemv_frag(a), gemv_frag(xv[t]), acc[r], 0, 0, 0);
+            }
+        }
+        __builtin_amdgcn_wave_barrier();           // the next block rewrites the tile
+    };
+    uint4 wa[NLD], wb[NLD], xa[STEPS], xb[STEPS];
+    load(wa, xa, b0);
+    for (int blk = b0; blk < b1; blk += 2) {
+        load(wb, xb, blk + 1);
+        block(wa, xa);
+        if (blk + 1 >= b1) break;
+        load(wa, xa, blk + 2);
+        block(wb, xb);
+    }
+    // lane (i, g) holds rows 4g .. 4g + 3 of vector i; sum the waves in order
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) red[wave][r][i][4 * g + j] = acc[r][j];
+    __syncthreads();
+    for (int t = threadIdx.x; t < RT * 16 * p.B; t += kGemvMfmaThreads) {
+        const int r = t / (16 * p.B);
+        const int b = (t / 16) % p.B;
+        const int rr = t % 16;
+        float v = 0.f;
+#pragma unroll
+        for (int w = 0; w < kGemvMfmaWaves; ++w) v += red[w][r][b][rr];
+        const int row = row0 + 16 * r + rr;
+        if (row < p.N) {
+            if constexpr (INT8) v *= p.scale[row];
+            const size_t o = (size_t)b * p.N + row;
+            if (p.out_bf16) reinterpret_cast<uint16_t*>(p.y)[o] = f32_to_bf16_rne(v);
+            else reinterpret_cast<float*>(p.y)[o] = v;
+        }
+    }
+}
+
 // Per-output-row symmetric INT8 quantization, in fp32: a = max |w|,
 // s = a / 127, q = round-half-even(w / s) kept in [-127, 127]; a row of zeros
 // gets s = 0 and q = 0 (llm-decode-cuda, INT8 section: one fp32 scale per

@@ -7,10 +7,13 @@ Two checks for each product:
     an integer the fp32 accumulator holds exactly, so the GPU must equal the
     oracle bit for bit -- a dropped, repeated or misplaced term cannot hide;
   * N(0,1) data: |y_gpu - y| <= a worst-case fp32 bound derived from the
-    kernel's summation (per lane at most 8 * ceil(K / 8 / 16) roundings in
-    its chain of dot2 steps, the 16/32/64-lane tree, the row scale):
-    (8 * ceil(K / 128) + 8) * 2^-24 * sum_k |W x|, and for bf16 output the
-    result rounded to one of the bf16 values bracketing that interval.
+    kernels' summation (vector units: per lane at most 8 * ceil(K / 8 / 16)
+    roundings in its chain of dot2 steps, the 16/32/64-lane tree, the row
+    scale; matrix cores: at most ceil(K / 256) blocks of 8 products of 32
+    terms per wave, each a few roundings, then 8 waves and the row scale --
+    fewer): (8 * ceil(K / 128) + 8) * 2^-24 * sum_k |W x|, and for bf16
+    output the result rounded to one of the bf16 values bracketing that
+    interval.
 The quantizer is compared bit for bit (codes and scales), both sides taking
 the integer decisions in fp32.
 """
@@ -60,13 +63,17 @@ def _check_bf16(out, ref, bound):
 
 
 SHAPES = [
-    # B, N, K   (lanes per row: K/8 chunks >= 256 -> 64, >= 128 -> 32, else 16)
+    # B, N, K   (vector units, B <= 4: lanes per row from K/8 chunks, >= 256 -> 64,
+    # >= 128 -> 32, else 16; matrix cores, B >= 5: 16-row tiles, 256-k blocks)
     (1, 1600, 960),       # SmolLM2-360M fused q/k/v, 16 lanes per row
     (3, 960, 2560),       # SmolLM2 down projection, 64 lanes
     (8, 77, 1024),        # 32 lanes, ragged row count
     (2, 5, 968),          # 121 chunks: a partial round of the 16-lane group
-    (8, 256, 14336),      # Llama-3-8B down-projection width: two launches of <= 5 vectors
+    (8, 256, 14336),      # Llama-3-8B down-projection width (matrix cores, 56 blocks of 256 k)
     (1, 1, 64),
+    (4, 77, 968),         # the last batch on the vector units (bf16)
+    (5, 77, 968),         # the first on the matrix cores: ragged rows and a partial 256-k block
+    (7, 1, 64),           # one row, one partial block
 ]
 
 
@@ -117,7 +124,8 @@ def _codes(shape, seed):
     return np.random.default_rng(seed).integers(-127, 128, size=shape).astype(np.int8)
 
 
-@pytest.mark.parametrize("B,N,K", [(1, 1600, 960), (4, 960, 2560), (8, 77, 1024), (8, 64, 14336), (2, 3, 16)])
+@pytest.mark.parametrize("B,N,K", [(1, 1600, 960), (4, 960, 2560), (8, 77, 1024), (8, 64, 14336), (2, 3, 16),
+                                   (3, 77, 976), (4, 77, 976), (5, 3, 16)])
 def test_gemv_int8_integer_data_is_exact(B, N, K):
     q = _codes((N, K), 730 + K)
     s = (2.0 ** np.random.default_rng(731).integers(-8, 1, size=N)).astype(np.float32)
