@@ -128,7 +128,7 @@ int chunk_attn(const void* q, const void* k_cache, const void* v_cache,
  * bf16 output uses bf16 softmax weights in p.V; fp32 output carries them as
  * bf16 hi + lo parts (about 16 bits), which keeps |out - exact| within 1e-4.
  * One launch, no host sync, capturable. D in {64, 128}; G = Hq/Hkv in 1..8;
- * (S_max + 256) * D * 2 < 2^32. Rows with no key (ctx + i + 1 <= 0) output 0. */
+ * (S_max + 512) * D * 2 < 2^32. Rows with no key (ctx + i + 1 <= 0) output 0. */
 int prefill_attn(const void* q, const void* k_cache, const void* v_cache,
                  const int32_t* ctx_lens,
                  int B, int T, int Hq, int Hkv, int D, int S_max, float scale,

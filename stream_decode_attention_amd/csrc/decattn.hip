@@ -559,7 +559,7 @@ int prefill_attn(const void* q, const void* k_cache, const void* v_cache, const 
     int st = check_out(out, out_dtype);
     if (st != DECATTN_OK) return st;
     // one kv head's cache must be addressable by a 32-bit buffer offset
-    if ((long long)(S_max + 4 * kPrefillKeys) * D * 2 > 0xFFFFFFFFLL) return DECATTN_ERR_UNSUPPORTED;
+    if ((long long)(S_max + 4 * kPrefillMaxKeys) * D * 2 > 0xFFFFFFFFLL) return DECATTN_ERR_UNSUPPORTED;
     if ((long long)B * T * Hq > 0x7FFFFFFF) return DECATTN_ERR_UNSUPPORTED;
     PrefillParams pp{};
     pp.q = static_cast<const uint16_t*>(q);
@@ -570,26 +570,47 @@ int prefill_attn(const void* q, const void* k_cache, const void* v_cache, const 
     pp.out_bf16 = out_dtype == DECATTN_OUT_BF16;
     pp.B = B; pp.T = T; pp.Hq = Hq; pp.Hkv = Hkv; pp.G = G; pp.S_max = S_max;
     pp.PW = 32 / G;
-    pp.NQB = (T + kPrefillWaves * pp.PW - 1) / (kPrefillWaves * pp.PW);
     pp.qscale = log2_scale(scale);
+    // 8 waves on 128-key tiles when that still gives 512 workgroups
+    const long long nqb8 = (T + 8LL * pp.PW - 1) / (8LL * pp.PW);
+    const bool wide = (long long)B * Hkv * nqb8 >= 512;
+    const int waves = wide ? 8 : 4;
+    pp.NQB = (T + waves * pp.PW - 1) / (waves * pp.PW);
     const long long grid = (long long)B * Hkv * pp.NQB;
     if (grid > 0x7FFFFFFF) return DECATTN_ERR_UNSUPPORTED;
-    const size_t lds = (size_t)prefill_lds_bytes(D);
+    const size_t lds = (size_t)prefill_lds_bytes(D, wide ? 128 : 64);
     const void* fn;
-    if (D == 64) fn = pp.out_bf16 ? reinterpret_cast<const void*>(&prefill_attn_mfma<64, false>)
-                                  : reinterpret_cast<const void*>(&prefill_attn_mfma<64, true>);
-    else fn = pp.out_bf16 ? reinterpret_cast<const void*>(&prefill_attn_mfma<128, false>)
-                          : reinterpret_cast<const void*>(&prefill_attn_mfma<128, true>);
-    // sets the dynamic-LDS limit of this kernel on the current device (cached)
-    if (resident_blocks(fn, 256, lds) <= 0) return DECATTN_ERR_HIP;
-    const hipStream_t s = static_cast<hipStream_t>(stream);
-    const dim3 g((unsigned)grid), blk(256);
-    if (D == 64) {
-        if (pp.out_bf16) hipLaunchKernelGGL((prefill_attn_mfma<64, false>), g, blk, lds, s, pp);
-        else hipLaunchKernelGGL((prefill_attn_mfma<64, true>), g, blk, lds, s, pp);
+    if (wide) {
+        if (D == 64) fn = pp.out_bf16 ? reinterpret_cast<const void*>(&prefill_attn_mfma<64, false, 8, 128>)
+                                      : reinterpret_cast<const void*>(&prefill_attn_mfma<64, true, 8, 128>);
+        else fn = pp.out_bf16 ? reinterpret_cast<const void*>(&prefill_attn_mfma<128, false, 8, 128>)
+                              : reinterpret_cast<const void*>(&prefill_attn_mfma<128, true, 8, 128>);
     } else {
-        if (pp.out_bf16) hipLaunchKernelGGL((prefill_attn_mfma<128, false>), g, blk, lds, s, pp);
-        else hipLaunchKernelGGL((prefill_attn_mfma<128, true>), g, blk, lds, s, pp);
+        if (D == 64) fn = pp.out_bf16 ? reinterpret_cast<const void*>(&prefill_attn_mfma<64, false, 4, 64>)
+                                      : reinterpret_cast<const void*>(&prefill_attn_mfma<64, true, 4, 64>);
+        else fn = pp.out_bf16 ? reinterpret_cast<const void*>(&prefill_attn_mfma<128, false, 4, 64>)
+                              : reinterpret_cast<const void*>(&prefill_attn_mfma<128, true, 4, 64>);
+    }
+    // sets the dynamic-LDS limit of this kernel on the current device (cached)
+    if (resident_blocks(fn, 64 * waves, lds) <= 0) return DECATTN_ERR_HIP;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const dim3 g((unsigned)grid), blk(64 * waves);
+    if (wide) {
+        if (D == 64) {
+            if (pp.out_bf16) hipLaunchKernelGGL((prefill_attn_mfma<64, false, 8, 128>), g, blk, lds, s, pp);
+            else hipLaunchKernelGGL((prefill_attn_mfma<64, true, 8, 128>), g, blk, lds, s, pp);
+        } else {
+            if (pp.out_bf16) hipLaunchKernelGGL((prefill_attn_mfma<128, false, 8, 128>), g, blk, lds, s, pp);
+            else hipLaunchKernelGGL((prefill_attn_mfma<128, true, 8, 128>), g, blk, lds, s, pp);
+        }
+    } else {
+        if (D == 64) {
+            if (pp.out_bf16) hipLaunchKernelGGL((prefill_attn_mfma<64, false, 4, 64>), g, blk, lds, s, pp);
+            else hipLaunchKernelGGL((prefill_attn_mfma<64, true, 4, 64>), g, blk, lds, s, pp);
+        } else {
+            if (pp.out_bf16) hipLaunchKernelGGL((prefill_attn_mfma<128, false, 4, 64>), g, blk, lds, s, pp);
+            else hipLaunchKernelGGL((prefill_attn_mfma<128, true, 4, 64>), g, blk, lds, s, pp);
+        }
     }
     return hipGetLastError() == hipSuccess ? DECATTN_OK : DECATTN_ERR_HIP;
 }

@@ -46,21 +46,23 @@ struct PrefillParams {
     float qscale;            // scale * log2(e), signed
 };
 
-constexpr int kPrefillWaves = 4;
-#ifndef DECATTN_PREFILL_KEYS
-#define DECATTN_PREFILL_KEYS 64
-#endif
-constexpr int kPrefillKeys = DECATTN_PREFILL_KEYS;   // keys per tile
+// Two shapes of workgroup: 4 waves on 64-key tiles, or 8 waves (256 query
+// rows sharing every K/V tile, half the tile traffic) on 128-key tiles, the
+// latter when it still gives 512 workgroups. Measured on MI355X (TFLOP/s,
+// bf16 output, 4 x 64 / 8 x 128): Llama-3-8B T = 4096 756 / 817, a 2048-token
+// chunk after 8192 923 / 992, TinyLlama T = 4096 743 / 787, SmolLM2-360M
+// T = 4096 (260 workgroups of 8 waves) 485 / 430.
+constexpr int kPrefillMaxKeys = 128;
 
 // LDS row strides in bytes: K rows padded by 16 bytes (the A-operand reads of
 // 32 lanes hit 32 rows at one column), V rows by 64 (as the verify kernel's,
 // for the transposing reads).
 __host__ __device__ constexpr int prefill_krow(int D) { return D * 2 + 16; }
 __host__ __device__ constexpr int prefill_vrow(int D) { return D * 2 + 64; }
-__host__ __device__ constexpr int prefill_tile_bytes(int D) {
-    return kPrefillKeys * (prefill_krow(D) + prefill_vrow(D));
+__host__ __device__ constexpr int prefill_tile_bytes(int D, int KT) {
+    return KT * (prefill_krow(D) + prefill_vrow(D));
 }
-__host__ __device__ constexpr int prefill_lds_bytes(int D) { return 2 * prefill_tile_bytes(D); }
+__host__ __device__ constexpr int prefill_lds_bytes(int D, int KT) { return 2 * prefill_tile_bytes(D, KT); }
 
 // A pointer every lane holds the same value of, moved to scalar registers.
 __device__ __forceinline__ const uint16_t* uniform_ptr(const uint16_t* ptr) {
@@ -77,20 +79,20 @@ __device__ __forceinline__ const uint16_t* uniform_ptr(const uint16_t* ptr) {
 #define DECATTN_PREFILL_WPE 2
 #endif
 
-template <int D, bool SPLIT>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DECATTN_PREFILL_WPE)))
+template <int D, bool SPLIT, int WAVES, int KT>
+__global__ void __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(DECATTN_PREFILL_WPE)))
 prefill_attn_mfma(const PrefillParams p) {
+    constexpr int kPrefillWaves = WAVES;
+    constexpr int kPrefillThreads = 64 * WAVES;
     constexpr int KS = D / 16;              // 16-dim steps of the score product
     constexpr int DB = D / 32;              // 32-dim blocks of the output
-    constexpr int KT = kPrefillKeys;
     constexpr int KBLK = KT / 32;           // 32-key blocks per tile
     constexpr int KROW = prefill_krow(D);
     constexpr int VROW = prefill_vrow(D);
-    constexpr int TILE = prefill_tile_bytes(D);
     constexpr int LPR = D / 8;              // 16-byte pieces per key row
-    constexpr int PPT = KT * LPR / 256;     // pieces per thread per tensor per tile
+    constexpr int PPT = KT * LPR / kPrefillThreads;   // pieces per thread per tensor per tile
     static_assert(D == 64 || D == 128, "head dim 64 or 128");
-    static_assert(PPT * 256 == KT * LPR, "whole pieces per thread");
+    static_assert(PPT * kPrefillThreads == KT * LPR, "whole pieces per thread");
 
     extern __shared__ __align__(16) char lds[];
 
@@ -147,14 +149,14 @@ prefill_attn_mfma(const PrefillParams p) {
     auto gload_k = [&](int t) {
 #pragma unroll
         for (int r = 0; r < PPT; ++r) {
-            const int pc = tid + 256 * r;
+            const int pc = tid + kPrefillThreads * r;
             kst[r] = buffer_load16_policy<0>(krs, (uint32_t)(t * KT + pc / LPR) * (D * 2) + (pc % LPR) * 16);
         }
     };
     auto gload_v = [&](int t) {
 #pragma unroll
         for (int r = 0; r < PPT; ++r) {
-            const int pc = tid + 256 * r;
+            const int pc = tid + kPrefillThreads * r;
             vst[r] = buffer_load16_policy<0>(vrs, (uint32_t)(t * KT + pc / LPR) * (D * 2) + (pc % LPR) * 16);
         }
     };
@@ -162,7 +164,7 @@ prefill_attn_mfma(const PrefillParams p) {
         char* kt = kbase_lds + buf * (KT * KROW);
 #pragma unroll
         for (int r = 0; r < PPT; ++r) {
-            const int pc = tid + 256 * r;
+            const int pc = tid + kPrefillThreads * r;
             *reinterpret_cast<uint4*>(kt + (pc / LPR) * KROW + (pc % LPR) * 16) = kst[r];
         }
     };
@@ -170,7 +172,7 @@ prefill_attn_mfma(const PrefillParams p) {
         char* vt = vbase_lds + buf * (KT * VROW);
 #pragma unroll
         for (int r = 0; r < PPT; ++r) {
-            const int pc = tid + 256 * r;
+            const int pc = tid + kPrefillThreads * r;
             *reinterpret_cast<uint4*>(vt + (pc / LPR) * VROW + (pc % LPR) * 16) = vst[r];
         }
     };
