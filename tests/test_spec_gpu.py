@@ -257,3 +257,15 @@ def test_emitted_tokens_follow_target_chi_squared(gamma):
         second = np.where(n >= 2, case["drafts"][:, 1], k)
         second[again] = np.where(n2 >= 1, step2["drafts"][:, 0], k2)
         assert chi(second) < 15.086
+
+
+@pytest.mark.parametrize("V", [(1 << 21) + 4, (1 << 21) + 3])
+def test_vocabulary_past_the_chunk_cap(V):
+    """More than 2048 chunks of 1024 entries: the chunks widen to stay within
+    the LDS stage of the decision (and V % 4 != 0 takes the scalar loads)."""
+    case = workloads.spec_sampling_case(2, 3, V, seed=1800 + V % 7)
+    _compare(case, 16384, _run(case, 16384))
+    g = workloads.spec_greedy_case(2, 3, V, seed=1810 + V % 7)
+    got = _run(g, 16384)
+    _compare(g, 16384, got)
+    assert np.array_equal(got[0], g["m"])
