@@ -303,15 +303,20 @@ constexpr int kGemvMaxB = 8;
 
 template <int LPR, int B, bool INT8>
 int launch_gemv_b(const GemvParams& gp, size_t lds, hipStream_t s) {
-    const void* fn = reinterpret_cast<const void*>(&gemv_kernel<LPR, B, INT8>);
-    long long grid = resident_blocks(fn, kGemvThreads, lds);
-    if (grid <= 0) return DECATTN_ERR_HIP;
-    const long long rows_per_wave = (64 / LPR) * gemv_rows_per_group<B, INT8>();
-    const long long groups = ((long long)gp.N + rows_per_wave - 1) / rows_per_wave;
-    const long long need = (groups + kGemvThreads / 64 - 1) / (kGemvThreads / 64);
-    if (grid > need) grid = need;
-    hipLaunchKernelGGL((gemv_kernel<LPR, B, INT8>), dim3((unsigned)grid), dim3(kGemvThreads), lds, s, gp);
-    return hipGetLastError() == hipSuccess ? DECATTN_OK : DECATTN_ERR_HIP;
+    // batches from the matrix-core threshold up never reach the dot products
+    if constexpr (B >= (INT8 ? DECATTN_GEMV_MFMA_MIN_B_INT8 : DECATTN_GEMV_MFMA_MIN_B_BF16)) {
+        return DECATTN_ERR_UNSUPPORTED;
+    } else {
+        const void* fn = reinterpret_cast<const void*>(&gemv_kernel<LPR, B, INT8>);
+        long long grid = resident_blocks(fn, kGemvThreads, lds);
+        if (grid <= 0) return DECATTN_ERR_HIP;
+        const long long rows_per_wave = (64 / LPR) * gemv_rows_per_group<B, INT8>();
+        const long long groups = ((long long)gp.N + rows_per_wave - 1) / rows_per_wave;
+        const long long need = (groups + kGemvThreads / 64 - 1) / (kGemvThreads / 64);
+        if (grid > need) grid = need;
+        hipLaunchKernelGGL((gemv_kernel<LPR, B, INT8>), dim3((unsigned)grid), dim3(kGemvThreads), lds, s, gp);
+        return hipGetLastError() == hipSuccess ? DECATTN_OK : DECATTN_ERR_HIP;
+    }
 }
 
 template <int LPR, bool INT8>
@@ -381,7 +386,7 @@ int gemv_common(const void* W, const float* scale, const void* x, int B, int N, 
         mp.K = K;
         mp.row_bytes = (uint32_t)K * (int8 ? 1 : 2);
         const unsigned grid = (unsigned)((N + 15) / 16);
-        const size_t lds = (size_t)kGemvMfmaWaves * 16 * kGemvPitch;
+        const size_t lds = (size_t)kGemvMfmaWaves * 16 * gemv_mfma_pitch(int8);
         const void* fn = int8 ? reinterpret_cast<const void*>(&gemv_mfma_kernel<1, true>)
                               : reinterpret_cast<const void*>(&gemv_mfma_kernel<1, false>);
         // sets the dynamic-LDS limit of this kernel on the current device (cached)

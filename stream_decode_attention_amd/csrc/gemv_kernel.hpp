@@ -217,7 +217,7 @@ gemv_kernel(const GemvParams p) {
 //
 // A workgroup of 8 waves owns 16 * RT rows (RT = 1: two tiles cost
 // registers, and spilled, for no gain); the waves split K into 8 ranges
-// of 512-byte blocks, and the 8 partial 16 x 16 results are summed in a
+// of 128-byte blocks, and the 8 partial 16 x 16 results are summed in a
 // fixed order through LDS. Activation fragments (vector lane % 16, 8 k per
 // lane) come straight from L2. Masked lanes (k past K, vectors past B,
 // blocks past the wave's range) read at the end of a buffer resource's
@@ -227,16 +227,21 @@ gemv_kernel(const GemvParams p) {
 typedef __bf16 gemv_bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float gemv_f32x4_t __attribute__((ext_vector_type(4)));
 
-// Measured on MI355X over one Llama-3-8B layer (GB/s of weights, dot-product
-// path / matrix cores): bf16 B = 4 4791 / 4624, B = 8 2967 / 4302; INT8
-// B = 3 3438 / 3276, B = 4 3108 / 3257, B = 8 1809 / 3056.
+// Measured on MI355X over one Llama-3-8B layer (us per layer, dot-product
+// path / matrix cores): bf16 B = 2 80.6 / 75.4, B = 4 90.8 / 76.1, B = 8
+// 100.8 / 79.7; INT8 B = 2 54.8 / 53.8, B = 4 67.0 / 54.9. At B = 1 the
+// dot products win on most shapes (Llama-3-8B's 6144 x 4096: 10.8 / 13.0;
+// the matrix-core grid is N / 16 workgroups, 1.5 per CU there).
 #ifndef DECATTN_GEMV_MFMA_MIN_B_BF16
-#define DECATTN_GEMV_MFMA_MIN_B_BF16 5
+#define DECATTN_GEMV_MFMA_MIN_B_BF16 2
 #endif
 #ifndef DECATTN_GEMV_MFMA_MIN_B_INT8
-#define DECATTN_GEMV_MFMA_MIN_B_INT8 4
+#define DECATTN_GEMV_MFMA_MIN_B_INT8 2
 #endif
-constexpr int kGemvMfmaWaves = 8;
+#ifndef DECATTN_GEMV_MFMA_WAVES
+#define DECATTN_GEMV_MFMA_WAVES 8
+#endif
+constexpr int kGemvMfmaWaves = DECATTN_GEMV_MFMA_WAVES;
 constexpr int kGemvMfmaThreads = 64 * kGemvMfmaWaves;
 #ifndef DECATTN_GEMV_MFMA_U
 #define DECATTN_GEMV_MFMA_U 4
@@ -255,28 +260,41 @@ struct GemvMfmaParams {
 
 __device__ __forceinline__ gemv_bf16x8_t gemv_frag(uint4 v) { return __builtin_bit_cast(gemv_bf16x8_t, v); }
 
-// Weight rows go through LDS: each wave loads blocks of 256 k of each of its
-// rows (512 bytes bf16, 256 bytes INT8; 2 or 4 rows of whole 128-byte lines
-// per instruction) with the block's activation fragments, the next block's
+// Weight rows go through LDS: each wave loads blocks of 128 bytes of each
+// of its rows (64 k bf16, 128 k INT8; 8 rows of one whole 128-byte line per
+// instruction) with the block's activation fragments, the next block's
 // loads in flight while the current one is stored to the wave's own LDS
 // tile and read back as MFMA fragments (16 rows x 64 or 32 bytes per read).
-constexpr int kGemvPitch = 512 + 16;         // LDS row pitch (bank spread)
+// Small blocks keep the kernel at 68 (bf16) / 76 (INT8) registers, 7 or 6
+// waves per SIMD; 512- and 256-byte blocks (194 registers) took 26% longer
+// at B = 8, 64-byte blocks slower again.
+#ifndef DECATTN_GEMV_MFMA_BLK_BF16
+#define DECATTN_GEMV_MFMA_BLK_BF16 128
+#endif
+#ifndef DECATTN_GEMV_MFMA_BLK_INT8
+#define DECATTN_GEMV_MFMA_BLK_INT8 128
+#endif
+constexpr int gemv_mfma_blk(bool int8) { return int8 ? DECATTN_GEMV_MFMA_BLK_INT8 : DECATTN_GEMV_MFMA_BLK_BF16; }
+// LDS row pitch: the block plus 16 bytes, so that the 16 rows of a fragment
+// read start on different banks
+constexpr int gemv_mfma_pitch(bool int8) { return gemv_mfma_blk(int8) + 16; }
 
 template <int RT, bool INT8>
 __global__ void __launch_bounds__(kGemvMfmaThreads)
 gemv_mfma_kernel(const GemvMfmaParams p) {
     constexpr int ESZ = INT8 ? 1 : 2;              // bytes per weight
-    constexpr int BLK = INT8 ? 256 : 512;          // bytes of a row per block
-    constexpr int BLK_K = BLK / ESZ;               // k per block (256)
+    constexpr int BLK = gemv_mfma_blk(INT8);       // bytes of a row per block
+    constexpr int BLK_K = BLK / ESZ;               // k per block
     constexpr int LPRW = BLK / 16;                 // lanes per row in a load
     constexpr int RPL = 64 / LPRW;                 // rows per load instruction
     constexpr int NLD = 16 * RT / RPL;             // 16-byte weight loads per lane per block
-    constexpr int STEPS = BLK_K / 32;              // MFMA k-steps per block (8)
-    extern __shared__ __align__(16) char gemv_lds[];            // [waves][16 RT][kGemvPitch]
+    constexpr int STEPS = BLK_K / 32;              // MFMA k-steps per block
+    constexpr int PITCH = gemv_mfma_pitch(INT8);
+    extern __shared__ __align__(16) char gemv_lds[];            // [waves][16 RT][PITCH]
     __shared__ float red[kGemvMfmaWaves][RT][16][16];           // [wave][tile][vector][row]
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int i = lane & 15, g = lane >> 4;
-    char* tile = gemv_lds + (size_t)wave * 16 * RT * kGemvPitch;
+    char* tile = gemv_lds + (size_t)wave * 16 * RT * PITCH;
     const int row0 = (int)blockIdx.x * 16 * RT;
     const int nblk = (p.K + BLK_K - 1) / BLK_K;
     const int b0 = (int)((long long)wave * nblk / kGemvMfmaWaves);
@@ -311,13 +329,13 @@ gemv_mfma_kernel(const GemvMfmaParams p) {
     auto block = [&](const uint4 (&w)[NLD], const uint4 (&xv)[STEPS]) {
 #pragma unroll
         for (int j = 0; j < NLD; ++j)
-            *reinterpret_cast<uint4*>(tile + (RPL * j + lrow) * kGemvPitch + lcol) = w[j];
+            *reinterpret_cast<uint4*>(tile + (RPL * j + lrow) * PITCH + lcol) = w[j];
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int t = 0; t < STEPS; ++t) {
 #pragma unroll
             for (int r = 0; r < RT; ++r) {
-                const char* src = tile + (16 * r + i) * kGemvPitch + (32 * t + 8 * g) * ESZ;
+                const char* src = tile + (16 * r + i) * PITCH + (32 * t + 8 * g) * ESZ;
                 uint4 a;
                 if constexpr (INT8) {
                     const uint2 c = *reinterpret_cast<const uint2*>(src);

@@ -198,10 +198,10 @@ def test_gemv_entry_points_reject_bad_arguments(lib):
                                    kw.get("y", Y), kw.get("od", 1), None)
     for kw, st in [(dict(W=None), 1), (dict(x=None), 1), (dict(y=None), 1), (dict(B=0), 1), (dict(N=0), 1),
                    (dict(K=0), 1), (dict(B=9), 2), (dict(K=100), 2), (dict(W=W + 8), 1), (dict(x=X + 2), 1),
-                   (dict(y=Y + 4), 1), (dict(od=5), 1), (dict(K=1 << 20), 2)]:
+                   (dict(y=Y + 4), 1), (dict(od=5), 1), (dict(K=1 << 20), 2), (dict(K=73736), 2)]:
         assert g(**kw) == st, kw
     q = lambda **kw: lib.gemv_int8(kw.get("W", W), kw.get("s", S), X, 1, 64, kw.get("K", 256), Y, 1, None)
-    assert q(s=None) == 1 and q(K=264) == 2 and q(s=S + 2) == 1
+    assert q(s=None) == 1 and q(K=264) == 2 and q(s=S + 2) == 1 and q(K=73744) == 2
     z = lambda **kw: lib.quantize_rows_int8(kw.get("W", W), kw.get("N", 64), kw.get("K", 256), kw.get("q", X),
                                             kw.get("s", S), None)
     for kw, st in [(dict(W=None), 1), (dict(q=None), 1), (dict(s=None), 1), (dict(N=0), 1), (dict(K=24), 2),

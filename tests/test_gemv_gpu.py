@@ -9,9 +9,9 @@ Two checks for each product:
   * N(0,1) data: |y_gpu - y| <= a worst-case fp32 bound derived from the
     kernels' summation (vector units: per lane at most 8 * ceil(K / 8 / 16)
     roundings in its chain of dot2 steps, the 16/32/64-lane tree, the row
-    scale; matrix cores: at most ceil(K / 256) blocks of 8 products of 32
-    terms per wave, each a few roundings, then 8 waves and the row scale --
-    fewer): (8 * ceil(K / 128) + 8) * 2^-24 * sum_k |W x|, and for bf16
+    scale; matrix cores: per wave a chain of at most ceil(K / 256) + 4
+    products of 32 terms, each a few roundings, then 8 waves and the row
+    scale -- fewer): (8 * ceil(K / 128) + 8) * 2^-24 * sum_k |W x|, and for bf16
     output the result rounded to one of the bf16 values bracketing that
     interval.
 The quantizer is compared bit for bit (codes and scales), both sides taking
@@ -63,17 +63,22 @@ def _check_bf16(out, ref, bound):
 
 
 SHAPES = [
-    # B, N, K   (vector units, B <= 4: lanes per row from K/8 chunks, >= 256 -> 64,
-    # >= 128 -> 32, else 16; matrix cores, B >= 5: 16-row tiles, 256-k blocks)
+    # B, N, K   (vector units, B = 1: lanes per row from K/8 chunks, >= 256 -> 64,
+    # >= 128 -> 32, else 16; matrix cores, B >= 2: 16-row tiles, 64-k blocks
+    # split over 8 waves)
     (1, 1600, 960),       # SmolLM2-360M fused q/k/v, 16 lanes per row
-    (3, 960, 2560),       # SmolLM2 down projection, 64 lanes
-    (8, 77, 1024),        # 32 lanes, ragged row count
-    (2, 5, 968),          # 121 chunks: a partial round of the 16-lane group
-    (8, 256, 14336),      # Llama-3-8B down-projection width (matrix cores, 56 blocks of 256 k)
+    (1, 960, 2560),       # SmolLM2 down projection, 64 lanes
+    (1, 77, 1024),        # 32 lanes, ragged row count
+    (1, 5, 968),          # 121 chunks: a partial round of the 16-lane group
     (1, 1, 64),
-    (4, 77, 968),         # the last batch on the vector units (bf16)
-    (5, 77, 968),         # the first on the matrix cores: ragged rows and a partial 256-k block
-    (7, 1, 64),           # one row, one partial block
+    (1, 77, 968),         # the last batch on the vector units
+    (2, 77, 968),         # the first on the matrix cores: ragged rows, a partial 64-k block
+    (3, 960, 2560),       # 40 blocks: 5 per wave
+    (8, 77, 1024),
+    (2, 5, 968),          # one partial 16-row tile
+    (8, 256, 14336),      # Llama-3-8B down-projection width (224 blocks of 64 k)
+    (7, 1, 64),           # one row, one block: seven waves with no work
+    (8, 33, 200),         # 4 blocks for 8 waves, the last holding 8 k
 ]
 
 
@@ -124,8 +129,9 @@ def _codes(shape, seed):
     return np.random.default_rng(seed).integers(-127, 128, size=shape).astype(np.int8)
 
 
-@pytest.mark.parametrize("B,N,K", [(1, 1600, 960), (4, 960, 2560), (8, 77, 1024), (8, 64, 14336), (2, 3, 16),
-                                   (3, 77, 976), (4, 77, 976), (5, 3, 16)])
+@pytest.mark.parametrize("B,N,K", [(1, 1600, 960), (1, 960, 2560), (1, 77, 1024), (1, 3, 16), (1, 77, 976),
+                                   (2, 77, 976), (4, 960, 2560), (8, 77, 1024), (8, 64, 14336), (2, 3, 16),
+                                   (3, 77, 976), (5, 3, 16), (8, 33, 208)])
 def test_gemv_int8_integer_data_is_exact(B, N, K):
     q = _codes((N, K), 730 + K)
     s = (2.0 ** np.random.default_rng(731).integers(-8, 1, size=N)).astype(np.float32)
