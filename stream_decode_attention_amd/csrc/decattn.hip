@@ -334,6 +334,17 @@ int launch_gemv_lpr(const GemvParams& gp, int B, size_t lds, hipStream_t s) {
     }
 }
 
+template <int RT, bool INT8>
+int launch_gemv_mfma(const GemvMfmaParams& mp, hipStream_t s) {
+    const unsigned grid = (unsigned)((mp.N + 16 * RT - 1) / (16 * RT));
+    const size_t lds = (size_t)kGemvMfmaWaves * 16 * RT * gemv_mfma_pitch(INT8);
+    // sets the dynamic-LDS limit of this kernel on the current device (cached)
+    if (resident_blocks(reinterpret_cast<const void*>(&gemv_mfma_kernel<RT, INT8>), kGemvMfmaThreads, lds) <= 0)
+        return DECATTN_ERR_HIP;
+    hipLaunchKernelGGL((gemv_mfma_kernel<RT, INT8>), dim3(grid), dim3(kGemvMfmaThreads), lds, s, mp);
+    return hipGetLastError() == hipSuccess ? DECATTN_OK : DECATTN_ERR_HIP;
+}
+
 // y = x W^T for B vectors, in launches of as many vectors as the LDS budget
 // holds (each launch reads the weights once).
 int gemv_common(const void* W, const float* scale, const void* x, int B, int N, int K, void* y, int out_dtype,
@@ -385,15 +396,10 @@ int gemv_common(const void* W, const float* scale, const void* x, int B, int N, 
         mp.N = N;
         mp.K = K;
         mp.row_bytes = (uint32_t)K * (int8 ? 1 : 2);
-        const unsigned grid = (unsigned)((N + 15) / 16);
-        const size_t lds = (size_t)kGemvMfmaWaves * 16 * gemv_mfma_pitch(int8);
-        const void* fn = int8 ? reinterpret_cast<const void*>(&gemv_mfma_kernel<1, true>)
-                              : reinterpret_cast<const void*>(&gemv_mfma_kernel<1, false>);
-        // sets the dynamic-LDS limit of this kernel on the current device (cached)
-        if (resident_blocks(fn, kGemvMfmaThreads, lds) <= 0) return DECATTN_ERR_HIP;
-        if (int8) hipLaunchKernelGGL((gemv_mfma_kernel<1, true>), dim3(grid), dim3(kGemvMfmaThreads), lds, s, mp);
-        else hipLaunchKernelGGL((gemv_mfma_kernel<1, false>), dim3(grid), dim3(kGemvMfmaThreads), lds, s, mp);
-        return hipGetLastError() == hipSuccess ? DECATTN_OK : DECATTN_ERR_HIP;
+        if (int8)
+            return N >= DECATTN_GEMV_MFMA_RT2_MIN_N_INT8 ? launch_gemv_mfma<2, true>(mp, s)
+                                                         : launch_gemv_mfma<1, true>(mp, s);
+        return launch_gemv_mfma<1, false>(mp, s);
     }
     for (int b0 = 0; b0 < B; b0 += bmax) {
         const int nb = B - b0 < bmax ? B - b0 : bmax;

@@ -215,10 +215,9 @@ gemv_kernel(const GemvParams p) {
 // once per row and is bound by those reads at B = 8; the multiplies cost
 // nothing next to the weight stream.
 //
-// A workgroup of 8 waves owns 16 * RT rows (RT = 1: two tiles cost
-// registers, and spilled, for no gain); the waves split K into 8 ranges
-// of 128-byte blocks, and the 8 partial 16 x 16 results are summed in a
-// fixed order through LDS. Activation fragments (vector lane % 16, 8 k per
+// A workgroup of 8 waves owns 16 * RT rows (RT = 1 or 2 tiles of 16 rows);
+// the waves split K into 8 ranges of 128-byte blocks, and the 8 partial
+// 16 x 16 results are summed in a fixed order through LDS. Activation fragments (vector lane % 16, 8 k per
 // lane) come straight from L2. Masked lanes (k past K, vectors past B,
 // blocks past the wave's range) read at the end of a buffer resource's
 // range, which returns zeros (the host keeps every range and offset + 16
@@ -237,6 +236,15 @@ typedef float gemv_f32x4_t __attribute__((ext_vector_type(4)));
 #endif
 #ifndef DECATTN_GEMV_MFMA_MIN_B_INT8
 #define DECATTN_GEMV_MFMA_MIN_B_INT8 2
+#endif
+// INT8 rows from N = 8192 up take two 16-row tiles per workgroup (RT = 2),
+// which halves the activation-fragment loads per weight byte: B = 8 on
+// MI355X, 28672 x 4096 34.6 -> 29.2 us, 14336 x 4096 19.0 -> 16.8 us,
+// 8192 x 8192 20.4 -> 18.3 us; below 8192 rows the halved grid loses what
+// that gains. bf16 keeps one tile: two cost registers (104, 4 waves per
+// SIMD instead of 7) and ran 19% slower on 28672 x 4096.
+#ifndef DECATTN_GEMV_MFMA_RT2_MIN_N_INT8
+#define DECATTN_GEMV_MFMA_RT2_MIN_N_INT8 8192
 #endif
 #ifndef DECATTN_GEMV_MFMA_WAVES
 #define DECATTN_GEMV_MFMA_WAVES 8

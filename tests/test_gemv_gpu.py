@@ -131,7 +131,8 @@ def _codes(shape, seed):
 
 @pytest.mark.parametrize("B,N,K", [(1, 1600, 960), (1, 960, 2560), (1, 77, 1024), (1, 3, 16), (1, 77, 976),
                                    (2, 77, 976), (4, 960, 2560), (8, 77, 1024), (8, 64, 14336), (2, 3, 16),
-                                   (3, 77, 976), (5, 3, 16), (8, 33, 208)])
+                                   (3, 77, 976), (5, 3, 16), (8, 33, 208),
+                                   (3, 8200, 208), (8, 8193, 16)])   # two 16-row tiles per workgroup from N = 8192
 def test_gemv_int8_integer_data_is_exact(B, N, K):
     q = _codes((N, K), 730 + K)
     s = (2.0 ** np.random.default_rng(731).integers(-8, 1, size=N)).astype(np.float32)
@@ -143,7 +144,7 @@ def test_gemv_int8_integer_data_is_exact(B, N, K):
     assert np.array_equal(y.cpu().double().numpy(), ref)
 
 
-@pytest.mark.parametrize("B,N,K", [(1, 1600, 960), (4, 960, 2560), (8, 256, 14336)])
+@pytest.mark.parametrize("B,N,K", [(1, 1600, 960), (4, 960, 2560), (8, 256, 14336), (8, 8208, 1024)])
 def test_quantize_then_gemv_int8_random_data(B, N, K):
     """The load-time quantizer feeding the INT8 product, as a model would use
     them: codes and scales from the GPU (equal to the oracle's), product
