@@ -489,6 +489,18 @@ void spec_launch_draw_u(const SpecParams& sp, int B, bool vec, hipStream_t s) {
 
 using namespace decattn;
 
+// ---- causal prefill attention ------------------------------------------------
+
+template <int D, bool SPLIT, int WAVES, int KT>
+int launch_prefill(const PrefillParams& pp, long long grid, hipStream_t s) {
+    const size_t lds = (size_t)prefill_lds_bytes(D, KT);
+    // sets the dynamic-LDS limit of this kernel on the current device (cached)
+    if (resident_blocks(reinterpret_cast<const void*>(&prefill_attn_mfma<D, SPLIT, WAVES, KT>), 64 * WAVES, lds) <= 0)
+        return DECATTN_ERR_HIP;
+    hipLaunchKernelGGL((prefill_attn_mfma<D, SPLIT, WAVES, KT>), dim3((unsigned)grid), dim3(64 * WAVES), lds, s, pp);
+    return hipGetLastError() == hipSuccess ? DECATTN_OK : DECATTN_ERR_HIP;
+}
+
 extern "C" {
 
 int decattn_abi_version(void) { return DECATTN_ABI_VERSION; }
@@ -582,48 +594,25 @@ int prefill_attn(const void* q, const void* k_cache, const void* v_cache, const 
     pp.B = B; pp.T = T; pp.Hq = Hq; pp.Hkv = Hkv; pp.G = G; pp.S_max = S_max;
     pp.PW = 32 / G;
     pp.qscale = log2_scale(scale);
-    // 8 waves on 128-key tiles when that still gives 512 workgroups
+    // 8 waves on 128-key tiles when that still gives 512 workgroups, else 4
+    // waves on 64-key tiles
     const long long nqb8 = (T + 8LL * pp.PW - 1) / (8LL * pp.PW);
     const bool wide = (long long)B * Hkv * nqb8 >= 512;
     const int waves = wide ? 8 : 4;
     pp.NQB = (T + waves * pp.PW - 1) / (waves * pp.PW);
     const long long grid = (long long)B * Hkv * pp.NQB;
     if (grid > 0x7FFFFFFF) return DECATTN_ERR_UNSUPPORTED;
-    const size_t lds = (size_t)prefill_lds_bytes(D, wide ? 128 : 64);
-    const void* fn;
-    if (wide) {
-        if (D == 64) fn = pp.out_bf16 ? reinterpret_cast<const void*>(&prefill_attn_mfma<64, false, 8, 128>)
-                                      : reinterpret_cast<const void*>(&prefill_attn_mfma<64, true, 8, 128>);
-        else fn = pp.out_bf16 ? reinterpret_cast<const void*>(&prefill_attn_mfma<128, false, 8, 128>)
-                              : reinterpret_cast<const void*>(&prefill_attn_mfma<128, true, 8, 128>);
-    } else {
-        if (D == 64) fn = pp.out_bf16 ? reinterpret_cast<const void*>(&prefill_attn_mfma<64, false, 4, 64>)
-                                      : reinterpret_cast<const void*>(&prefill_attn_mfma<64, true, 4, 64>);
-        else fn = pp.out_bf16 ? reinterpret_cast<const void*>(&prefill_attn_mfma<128, false, 4, 64>)
-                              : reinterpret_cast<const void*>(&prefill_attn_mfma<128, true, 4, 64>);
-    }
-    // sets the dynamic-LDS limit of this kernel on the current device (cached)
-    if (resident_blocks(fn, 64 * waves, lds) <= 0) return DECATTN_ERR_HIP;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    const dim3 g((unsigned)grid), blk(64 * waves);
     if (wide) {
-        if (D == 64) {
-            if (pp.out_bf16) hipLaunchKernelGGL((prefill_attn_mfma<64, false, 8, 128>), g, blk, lds, s, pp);
-            else hipLaunchKernelGGL((prefill_attn_mfma<64, true, 8, 128>), g, blk, lds, s, pp);
-        } else {
-            if (pp.out_bf16) hipLaunchKernelGGL((prefill_attn_mfma<128, false, 8, 128>), g, blk, lds, s, pp);
-            else hipLaunchKernelGGL((prefill_attn_mfma<128, true, 8, 128>), g, blk, lds, s, pp);
-        }
-    } else {
-        if (D == 64) {
-            if (pp.out_bf16) hipLaunchKernelGGL((prefill_attn_mfma<64, false, 4, 64>), g, blk, lds, s, pp);
-            else hipLaunchKernelGGL((prefill_attn_mfma<64, true, 4, 64>), g, blk, lds, s, pp);
-        } else {
-            if (pp.out_bf16) hipLaunchKernelGGL((prefill_attn_mfma<128, false, 4, 64>), g, blk, lds, s, pp);
-            else hipLaunchKernelGGL((prefill_attn_mfma<128, true, 4, 64>), g, blk, lds, s, pp);
-        }
+        if (D == 64) return pp.out_bf16 ? launch_prefill<64, false, 8, 128>(pp, grid, s)
+                                        : launch_prefill<64, true, 8, 128>(pp, grid, s);
+        return pp.out_bf16 ? launch_prefill<128, false, 8, 128>(pp, grid, s)
+                           : launch_prefill<128, true, 8, 128>(pp, grid, s);
     }
-    return hipGetLastError() == hipSuccess ? DECATTN_OK : DECATTN_ERR_HIP;
+    if (D == 64) return pp.out_bf16 ? launch_prefill<64, false, 4, 64>(pp, grid, s)
+                                    : launch_prefill<64, true, 4, 64>(pp, grid, s);
+    return pp.out_bf16 ? launch_prefill<128, false, 4, 64>(pp, grid, s)
+                       : launch_prefill<128, true, 4, 64>(pp, grid, s);
 }
 
 int rope_kv_write(const void* q_in, const void* k_in, const void* v_in, const int32_t* pos0, int B, int T,
