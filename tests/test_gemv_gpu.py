@@ -168,6 +168,26 @@ def test_quantize_then_gemv_int8_random_data(B, N, K):
     _check_bf16(y16, ref, bound)
 
 
+@pytest.mark.parametrize("B", [1, 2, 8])
+def test_gemv_at_the_largest_k(B):
+    """K = 73728, the largest K whose staged vector fits the 144 KB LDS budget
+    of the dot-product path (B = 1); B = 2 and 8 run on the matrix cores at
+    the same K (1152 blocks of 64 k over 8 waves). Integer data: exact."""
+    N, K = 37, 73728
+    W = _small_int_bits((N, K), 790 + B)
+    x = _small_int_bits((B, K), 791 + B)
+    y = torch.empty((B, N), dtype=torch.float32, device="cuda")
+    sda.gemv_bf16(dev_bits(W), dev_bits(x), y)
+    # codes within +-15 keep every partial sum an integer below 2^24
+    q = np.random.default_rng(792 + B).integers(-15, 16, size=(N, K)).astype(np.int8)
+    s = (2.0 ** np.random.default_rng(793).integers(-8, 1, size=N)).astype(np.float32)
+    y8 = torch.empty((B, N), dtype=torch.float32, device="cuda")
+    sda.gemv_int8(torch.from_numpy(q).cuda(), torch.from_numpy(s).cuda(), dev_bits(x), y8)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().double().numpy(), oracle.gemv(W, x))
+    assert np.array_equal(y8.cpu().double().numpy(), oracle.gemv_int8(q, s, x))
+
+
 def test_gemv_graph_replay_with_new_activations():
     N, K, B = 512, 2048, 4
     W = workloads.bf16_randn((N, K), 750)
