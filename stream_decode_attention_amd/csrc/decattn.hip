@@ -367,14 +367,7 @@ int gemv_common(const void* W, const float* scale, const void* x, int B, int N, 
     gp.N = N;
     gp.K = K;
     gp.KC = K / epc;
-#ifndef DECATTN_GEMV_LPR_RULE
-#define DECATTN_GEMV_LPR_RULE 0
-#endif
-#if DECATTN_GEMV_LPR_RULE
-    const int lpr = gp.KC >= 48 ? 64 : (gp.KC >= 24 ? 32 : 16);
-#else
     const int lpr = gp.KC >= 256 ? 64 : (gp.KC >= 128 ? 32 : 16);
-#endif
     gp.KCP = (gp.KC + lpr - 1) / lpr * lpr;
     gp.xrow = gp.KCP * epc;
     const size_t per_vec = (size_t)gp.xrow * 2;

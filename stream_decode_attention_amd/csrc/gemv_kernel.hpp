@@ -251,10 +251,6 @@ typedef float gemv_f32x4_t __attribute__((ext_vector_type(4)));
 #endif
 constexpr int kGemvMfmaWaves = DECATTN_GEMV_MFMA_WAVES;
 constexpr int kGemvMfmaThreads = 64 * kGemvMfmaWaves;
-#ifndef DECATTN_GEMV_MFMA_U
-#define DECATTN_GEMV_MFMA_U 4
-#endif
-constexpr int kGemvMfmaU = DECATTN_GEMV_MFMA_U;
 
 struct GemvMfmaParams {
     const void* W;            // bf16 [N][K] or int8 [N][K]

@@ -72,9 +72,6 @@ __device__ __forceinline__ const uint16_t* uniform_ptr(const uint16_t* ptr) {
     return reinterpret_cast<const uint16_t*>(((uint64_t)hi << 32) | lo);
 }
 
-#ifndef DECATTN_PREFILL_PIPE
-#define DECATTN_PREFILL_PIPE 0
-#endif
 #ifndef DECATTN_PREFILL_WPE
 #define DECATTN_PREFILL_WPE 2
 #endif
@@ -315,37 +312,6 @@ prefill_attn_mfma(const PrefillParams p) {
     };
 
     const int ntiles = (lim_all + KT - 1) / KT;
-#if DECATTN_PREFILL_PIPE
-    // Software pipeline: the score products of tile t+1 are issued before the
-    // softmax and p.V of tile t, so the matrix cores work while the vector
-    // ALUs take the exponentials. K runs one tile ahead of V: iteration t
-    // reads K(t+1) and V(t), then stores K(t+2) and V(t+1) into the buffers
-    // K(t) and V(t-1) left (both last read before the previous barrier).
-    // Loads past the last tile read zeros; every wave runs every tile of the
-    // workgroup (a tile past a wave's rows is all masked and adds nothing).
-    gload_k(0);
-    gload_v(0);
-    lstore_k(0);
-    lstore_v(0);
-    gload_k(1);
-    lstore_k(1);
-    __syncthreads();
-    f32x16_t s_cur[KBLK];
-    qk(s_cur, 0);
-    __syncthreads();                       // K(0) is overwritten by K(2) below
-    for (int t = 0; t < ntiles; ++t) {
-        gload_k(t + 2);
-        gload_v(t + 1);
-        f32x16_t s_nxt[KBLK];
-        qk(s_nxt, (t + 1) & 1);
-        softmax_pv(s_cur, t * KT, t & 1);
-        lstore_k(t & 1);
-        lstore_v((t + 1) & 1);
-        __syncthreads();
-#pragma unroll
-        for (int kb = 0; kb < KBLK; ++kb) s_cur[kb] = s_nxt[kb];
-    }
-#else
     // Two buffers each of K and V: tile t+1 is loaded into registers while
     // tile t is computed, then stored into the other buffers; one barrier per
     // tile. The load and store of tile t+1 are issued on every iteration (past
@@ -369,7 +335,6 @@ prefill_attn_mfma(const PrefillParams p) {
         lstore_v((t + 1) & 1);
         __syncthreads();
     }
-#endif
 
     // rows: join the two halves' sums, normalise, store 4 dims per group
     {
