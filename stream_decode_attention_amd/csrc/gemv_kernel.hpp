@@ -16,6 +16,11 @@
 // slowdown). Row sums are joined across the group with DPP and lane swaps;
 // the group's first lane applies the row scale and stores y. The grid is
 // persistent: every wave walks row groups wave, wave + all waves, ...
+//
+// By default this dot-product kernel serves one vector and the matrix-core
+// kernel further down every B from 2; the kernel itself takes up to 8
+// vectors (raising DECATTN_GEMV_MFMA_MIN_B_* hands them to it, the setting
+// the rows-per-group rule below was measured in).
 #pragma once
 
 #include "device_common.hpp"
@@ -208,17 +213,17 @@ gemv_kernel(const GemvParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Matrix-core path for more vectors (B >= 5 bf16, B >= 4 INT8): y^T = W x^T as
+// Matrix-core path for two or more vectors: y^T = W x^T as
 // 16 x 16 x 32 bf16 products (v_mfma_f32_16x16x32_bf16): 16 weight rows by
 // 32 k times 32 k by 16 vectors (columns past B are zero). Each activation
 // fragment then serves 16 weight rows, where the dot-product path reads it
-// once per row and is bound by those reads at B = 8; the multiplies cost
+// once per row and is bound by those reads from B = 2; the multiplies cost
 // nothing next to the weight stream.
 //
 // A workgroup of 8 waves owns 16 * RT rows (RT = 1 or 2 tiles of 16 rows);
 // the waves split K into 8 ranges of 128-byte blocks, and the 8 partial
-// 16 x 16 results are summed in a fixed order through LDS. Activation fragments (vector lane % 16, 8 k per
-// lane) come straight from L2. Masked lanes (k past K, vectors past B,
+// 16 x 16 results are summed in a fixed order through LDS. Activation
+// fragments (vector lane % 16, 8 k per lane) come straight from L2. Masked lanes (k past K, vectors past B,
 // blocks past the wave's range) read at the end of a buffer resource's
 // range, which returns zeros (the host keeps every range and offset + 16
 // below 2^32): every load is issued without a branch. INT8 codes are widened
