@@ -126,7 +126,42 @@ def _stream(stream, dev) -> int:
         return torch.cuda.current_stream(dev).cuda_stream
     if isinstance(stream, int):
         return stream
+    if stream.device != dev:
+        raise ValueError(f"stream is on {stream.device}, the tensors on {dev}")
     return stream.cuda_stream
+
+
+class _on_device:
+    """Checks that every tensor argument sits on one device and makes that
+    device the current one for the library call (the library launches on, and
+    sizes its grids for, the current device)."""
+
+    def __init__(self, *tensors):
+        dev = None
+        for t in tensors:
+            if t is None:
+                continue
+            if not isinstance(t, torch.Tensor) or not t.is_cuda:
+                raise ValueError("every tensor argument must be a device tensor")
+            if dev is None:
+                dev = t.device
+            elif t.device != dev:
+                raise ValueError(f"tensor arguments on {dev} and {t.device}: all must be on one device")
+        self.index = dev.index if dev is not None and dev.index is not None else None
+        self.prev = None
+
+    def __enter__(self):
+        if self.index is not None:
+            cur = torch.cuda.current_device()
+            if cur != self.index:
+                self.prev = cur
+                torch.cuda.set_device(self.index)
+        return self
+
+    def __exit__(self, *exc):
+        if self.prev is not None:
+            torch.cuda.set_device(self.prev)
+        return False
 
 
 def _out_dtype(out: torch.Tensor) -> int:
@@ -150,12 +185,13 @@ def decode_attn(q, k_cache, v_cache, seq_lens, scale: float, out, workspace, chu
     if Dk != D or tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(out.shape) != (B, Hq, D) \
             or k_cache.shape[0] != B or tuple(seq_lens.shape) != (B,):
         raise ValueError("shape mismatch between q, caches, seq_lens and out")
-    st = load_library().decode_attn(
-        _ptr(q, "q", _BF16), _ptr(k_cache, "k_cache", _BF16), _ptr(v_cache, "v_cache", _BF16),
-        _ptr(seq_lens, "seq_lens", (torch.int32,)), B, Hq, Hkv, D, S_max, float(scale),
-        _ptr(out, "out", (torch.float32,) + _BF16), _out_dtype(out),
-        _ptr(workspace, "workspace", (torch.uint8,)), workspace.numel(), int(chunk),
-        _stream(stream, q.device))
+    with _on_device(q, k_cache, v_cache, seq_lens, out, workspace):
+        st = load_library().decode_attn(
+            _ptr(q, "q", _BF16), _ptr(k_cache, "k_cache", _BF16), _ptr(v_cache, "v_cache", _BF16),
+            _ptr(seq_lens, "seq_lens", (torch.int32,)), B, Hq, Hkv, D, S_max, float(scale),
+            _ptr(out, "out", (torch.float32,) + _BF16), _out_dtype(out),
+            _ptr(workspace, "workspace", (torch.uint8,)), workspace.numel(), int(chunk),
+            _stream(stream, q.device))
     _check("decode_attn", st)
     return out
 
@@ -168,12 +204,13 @@ def chunk_attn(q, k_cache, v_cache, ctx_lens, scale: float, out, workspace, chun
     if Dk != D or tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(out.shape) != (B, T, Hq, D) \
             or k_cache.shape[0] != B or tuple(ctx_lens.shape) != (B,):
         raise ValueError("shape mismatch between q, caches, ctx_lens and out")
-    st = load_library().chunk_attn(
-        _ptr(q, "q", _BF16), _ptr(k_cache, "k_cache", _BF16), _ptr(v_cache, "v_cache", _BF16),
-        _ptr(ctx_lens, "ctx_lens", (torch.int32,)), B, T, Hq, Hkv, D, S_max, float(scale),
-        _ptr(out, "out", (torch.float32,) + _BF16), _out_dtype(out),
-        _ptr(workspace, "workspace", (torch.uint8,)), workspace.numel(), int(chunk),
-        _stream(stream, q.device))
+    with _on_device(q, k_cache, v_cache, ctx_lens, out, workspace):
+        st = load_library().chunk_attn(
+            _ptr(q, "q", _BF16), _ptr(k_cache, "k_cache", _BF16), _ptr(v_cache, "v_cache", _BF16),
+            _ptr(ctx_lens, "ctx_lens", (torch.int32,)), B, T, Hq, Hkv, D, S_max, float(scale),
+            _ptr(out, "out", (torch.float32,) + _BF16), _out_dtype(out),
+            _ptr(workspace, "workspace", (torch.uint8,)), workspace.numel(), int(chunk),
+            _stream(stream, q.device))
     _check("chunk_attn", st)
     return out
 
@@ -187,10 +224,11 @@ def prefill_attn(q, k_cache, v_cache, ctx_lens, scale: float, out, stream=None):
     if Dk != D or tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(out.shape) != (B, T, Hq, D) \
             or k_cache.shape[0] != B or tuple(ctx_lens.shape) != (B,):
         raise ValueError("shape mismatch between q, caches, ctx_lens and out")
-    st = load_library().prefill_attn(
-        _ptr(q, "q", _BF16), _ptr(k_cache, "k_cache", _BF16), _ptr(v_cache, "v_cache", _BF16),
-        _ptr(ctx_lens, "ctx_lens", (torch.int32,)), B, T, Hq, Hkv, D, S_max, float(scale),
-        _ptr(out, "out", (torch.float32,) + _BF16), _out_dtype(out), _stream(stream, q.device))
+    with _on_device(q, k_cache, v_cache, ctx_lens, out):
+        st = load_library().prefill_attn(
+            _ptr(q, "q", _BF16), _ptr(k_cache, "k_cache", _BF16), _ptr(v_cache, "v_cache", _BF16),
+            _ptr(ctx_lens, "ctx_lens", (torch.int32,)), B, T, Hq, Hkv, D, S_max, float(scale),
+            _ptr(out, "out", (torch.float32,) + _BF16), _out_dtype(out), _stream(stream, q.device))
     _check("prefill_attn", st)
     return out
 
@@ -202,8 +240,9 @@ def gemv_bf16(W, x, y, stream=None):
     B = x.shape[0]
     if tuple(x.shape) != (B, K) or tuple(y.shape) != (B, N):
         raise ValueError("shape mismatch between W, x and y")
-    st = load_library().gemv_bf16(_ptr(W, "W", _BF16), _ptr(x, "x", _BF16), B, N, K,
-                                  _ptr(y, "y", (torch.float32,) + _BF16), _out_dtype(y), _stream(stream, W.device))
+    with _on_device(W, x, y):
+        st = load_library().gemv_bf16(_ptr(W, "W", _BF16), _ptr(x, "x", _BF16), B, N, K,
+                                      _ptr(y, "y", (torch.float32,) + _BF16), _out_dtype(y), _stream(stream, W.device))
     _check("gemv_bf16", st)
     return y
 
@@ -214,9 +253,10 @@ def gemv_int8(Wq, scale, x, y, stream=None):
     B = x.shape[0]
     if tuple(x.shape) != (B, K) or tuple(y.shape) != (B, N) or tuple(scale.shape) != (N,):
         raise ValueError("shape mismatch between Wq, scale, x and y")
-    st = load_library().gemv_int8(_ptr(Wq, "Wq", (torch.int8,)), _ptr(scale, "scale", (torch.float32,)),
-                                  _ptr(x, "x", _BF16), B, N, K, _ptr(y, "y", (torch.float32,) + _BF16),
-                                  _out_dtype(y), _stream(stream, Wq.device))
+    with _on_device(Wq, scale, x, y):
+        st = load_library().gemv_int8(_ptr(Wq, "Wq", (torch.int8,)), _ptr(scale, "scale", (torch.float32,)),
+                                      _ptr(x, "x", _BF16), B, N, K, _ptr(y, "y", (torch.float32,) + _BF16),
+                                      _out_dtype(y), _stream(stream, Wq.device))
     _check("gemv_int8", st)
     return y
 
@@ -226,8 +266,9 @@ def quantize_rows_int8(W, Wq, scale, stream=None):
     N, K = W.shape
     if tuple(Wq.shape) != (N, K) or tuple(scale.shape) != (N,):
         raise ValueError("shape mismatch between W, Wq and scale")
-    st = load_library().quantize_rows_int8(_ptr(W, "W", _BF16), N, K, _ptr(Wq, "Wq", (torch.int8,)),
-                                           _ptr(scale, "scale", (torch.float32,)), _stream(stream, W.device))
+    with _on_device(W, Wq, scale):
+        st = load_library().quantize_rows_int8(_ptr(W, "W", _BF16), N, K, _ptr(Wq, "Wq", (torch.int8,)),
+                                               _ptr(scale, "scale", (torch.float32,)), _stream(stream, W.device))
     _check("quantize_rows_int8", st)
 
 
@@ -255,12 +296,13 @@ def spec_accept(logits, q, drafts, u, r, tau: float, lens, result, workspace, S_
     for name, t, shape in (("q", q, (B, G, V)), ("drafts", drafts, (B, G)), ("u", u, (B, G)), ("r", r, (B,))):
         if t is not None and tuple(t.shape) != shape:
             raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
-    st = load_library().spec_accept(
-        _ptr(logits, "logits", (torch.float32,)), _opt_ptr(q, "q", (torch.float32,)),
-        _opt_ptr(drafts, "drafts", (torch.int32,)), _opt_ptr(u, "u", (torch.float32,)),
-        _opt_ptr(r, "r", (torch.float32,)), float(tau), B, T, V, int(S_max),
-        _ptr(lens, "lens", (torch.int32,)), _ptr(result, "result", (torch.int32,)),
-        _ptr(workspace, "workspace", (torch.uint8,)), workspace.numel(), _stream(stream, logits.device))
+    with _on_device(logits, q, drafts, u, r, lens, result, workspace):
+        st = load_library().spec_accept(
+            _ptr(logits, "logits", (torch.float32,)), _opt_ptr(q, "q", (torch.float32,)),
+            _opt_ptr(drafts, "drafts", (torch.int32,)), _opt_ptr(u, "u", (torch.float32,)),
+            _opt_ptr(r, "r", (torch.float32,)), float(tau), B, T, V, int(S_max),
+            _ptr(lens, "lens", (torch.int32,)), _ptr(result, "result", (torch.int32,)),
+            _ptr(workspace, "workspace", (torch.uint8,)), workspace.numel(), _stream(stream, logits.device))
     _check("spec_accept", st)
     return result
 
@@ -274,11 +316,12 @@ def attn_partial(q, k_cache, v_cache, lens, scale: float, workspace, causal: boo
     else:
         B, T, Hq, D = q.shape
     _, Hkv, S_max, _ = k_cache.shape
-    st = load_library().attn_partial(
-        _ptr(q, "q", _BF16), _ptr(k_cache, "k_cache", _BF16), _ptr(v_cache, "v_cache", _BF16),
-        _ptr(lens, "lens", (torch.int32,)), B, T, Hq, Hkv, D, S_max, float(scale), int(bool(causal)),
-        _ptr(workspace, "workspace", (torch.uint8,)), workspace.numel(), int(chunk),
-        _stream(stream, q.device))
+    with _on_device(q, k_cache, v_cache, lens, workspace):
+        st = load_library().attn_partial(
+            _ptr(q, "q", _BF16), _ptr(k_cache, "k_cache", _BF16), _ptr(v_cache, "v_cache", _BF16),
+            _ptr(lens, "lens", (torch.int32,)), B, T, Hq, Hkv, D, S_max, float(scale), int(bool(causal)),
+            _ptr(workspace, "workspace", (torch.uint8,)), workspace.numel(), int(chunk),
+            _stream(stream, q.device))
     _check("attn_partial", st)
 
 
@@ -287,11 +330,12 @@ def attn_merge(lens, out, workspace, *, T: int, Hq: int, Hkv: int, S_max: int, c
     """Second phase only: log-sum-exp merge of ``workspace`` into ``out``."""
     B = lens.shape[0]
     D = out.shape[-1]
-    st = load_library().attn_merge(
-        _ptr(lens, "lens", (torch.int32,)), B, T, Hq, Hkv, D, S_max, int(bool(causal)),
-        _ptr(out, "out", (torch.float32,) + _BF16), _out_dtype(out),
-        _ptr(workspace, "workspace", (torch.uint8,)), workspace.numel(), int(chunk),
-        _stream(stream, out.device))
+    with _on_device(lens, out, workspace):
+        st = load_library().attn_merge(
+            _ptr(lens, "lens", (torch.int32,)), B, T, Hq, Hkv, D, S_max, int(bool(causal)),
+            _ptr(out, "out", (torch.float32,) + _BF16), _out_dtype(out),
+            _ptr(workspace, "workspace", (torch.uint8,)), workspace.numel(), int(chunk),
+            _stream(stream, out.device))
     _check("attn_merge", st)
 
 
@@ -328,23 +372,26 @@ def rope_kv_write(q_in, k_in, v_in, pos0, q_out, k_cache, v_cache, theta: float,
             or tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(pos0.shape) != (B,):
         raise ValueError("shape mismatch between q, k, v, pos0 and the caches")
     params = rope_params(theta, pairing, llama3)
-    st = load_library().rope_kv_write(
-        _ptr(q_in, "q_in", _BF16), _ptr(k_in, "k_in", _BF16), _ptr(v_in, "v_in", _BF16),
-        _ptr(pos0, "pos0", (torch.int32,)), B, T, Hq, Hkv, D, S_max, ctypes.byref(params),
-        _ptr(q_out, "q_out", _BF16), _ptr(k_cache, "k_cache", _BF16), _ptr(v_cache, "v_cache", _BF16),
-        _stream(stream, q_in.device))
+    with _on_device(q_in, k_in, v_in, pos0, q_out, k_cache, v_cache):
+        st = load_library().rope_kv_write(
+            _ptr(q_in, "q_in", _BF16), _ptr(k_in, "k_in", _BF16), _ptr(v_in, "v_in", _BF16),
+            _ptr(pos0, "pos0", (torch.int32,)), B, T, Hq, Hkv, D, S_max, ctypes.byref(params),
+            _ptr(q_out, "q_out", _BF16), _ptr(k_cache, "k_cache", _BF16), _ptr(v_cache, "v_cache", _BF16),
+            _stream(stream, q_in.device))
     _check("rope_kv_write", st)
     return q_out
 
 
 def probe_read(buf: torch.Tensor, sink: torch.Tensor, stream=None):
     """Stream-read every byte of ``buf`` (16-byte loads); writes at most 4 bytes of ``sink``."""
-    st = load_library().decattn_probe_read(buf.data_ptr(), buf.numel() * buf.element_size(),
-                                           sink.data_ptr(), _stream(stream, buf.device))
+    with _on_device(buf, sink):
+        st = load_library().decattn_probe_read(buf.data_ptr(), buf.numel() * buf.element_size(),
+                                               sink.data_ptr(), _stream(stream, buf.device))
     _check("decattn_probe_read", st)
 
 
 def probe_copy(dst: torch.Tensor, src: torch.Tensor, stream=None):
-    st = load_library().decattn_probe_copy(dst.data_ptr(), src.data_ptr(),
-                                           src.numel() * src.element_size(), _stream(stream, src.device))
+    with _on_device(dst, src):
+        st = load_library().decattn_probe_copy(dst.data_ptr(), src.data_ptr(),
+                                               src.numel() * src.element_size(), _stream(stream, src.device))
     _check("decattn_probe_copy", st)

@@ -247,3 +247,20 @@ def test_spec_workspace_bytes(lib):
 ])
 def test_spec_accept_rejects_bad_arguments(lib, kw, status):
     assert _spec(lib, **kw) == status
+
+
+def test_binding_rejects_host_tensors_before_calling_the_library():
+    """The ctypes layer refuses tensors that are not on a device (it would
+    otherwise hand host addresses to the kernels)."""
+    import torch
+    W = torch.zeros((16, 64), dtype=torch.bfloat16)
+    x = torch.zeros((1, 64), dtype=torch.bfloat16)
+    y = torch.zeros((1, 16), dtype=torch.float32)
+    with pytest.raises(ValueError, match="device tensor"):
+        sda.gemv_bf16(W, x, y)
+    q = torch.zeros((1, 4, 64), dtype=torch.bfloat16)
+    kv = torch.zeros((1, 2, 32, 64), dtype=torch.bfloat16)
+    lens = torch.zeros((1,), dtype=torch.int32)
+    ws = torch.zeros((4096,), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="device tensor"):
+        sda.decode_attn(q, kv, kv, lens, 0.125, q.clone(), ws)
