@@ -154,6 +154,10 @@ int resident_blocks(const void* kernel, int threads, size_t lds) {
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds) != hipSuccess) return 0;
     const int n = cus * (per_cu > 0 ? per_cu : 1);
     std::lock_guard<std::mutex> lock(mu);
+    // the key includes the dynamic LDS size, which some kernels size from the
+    // call's shapes: keep the linear search short for callers that cycle
+    // through many shapes (entries are recomputed on demand)
+    if (cache.size() >= 512) cache.clear();
     cache.push_back({Key{dev, kernel, threads, lds}, n});
     return n;
 }
