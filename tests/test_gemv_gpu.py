@@ -188,6 +188,44 @@ def test_gemv_at_the_largest_k(B):
     assert np.array_equal(y8.cpu().double().numpy(), oracle.gemv_int8(q, s, x))
 
 
+@pytest.mark.parametrize("N,K", [(6144, 4096), (4096, 4096), (28672, 4096), (4096, 14336)])
+def test_gemv_llama3_8b_matrices_sampled_rows(N, K):
+    """One Llama-3-8B layer's four products at full size, as the benchmark
+    times them (seeded N(0,1) weights drawn on the device, bf16 and INT8,
+    B = 1 and 8): the quantizer's codes and scales on 96 sampled rows (tile
+    edges, the last rows, random ones) equal the oracle's bit for bit, and
+    the products on those rows are within the fp32 bound of the oracle's."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(880 + N + K)
+    W = torch.randn((N, K), generator=g, device="cuda").to(torch.bfloat16)
+    Wq = torch.empty((N, K), dtype=torch.int8, device="cuda")
+    sc = torch.empty((N,), dtype=torch.float32, device="cuda")
+    sda.quantize_rows_int8(W, Wq, sc)
+    edges = [0, 1, 15, 16, 31, 32, 33, N - 33, N - 32, N - 17, N - 16, N - 1]
+    rows = sorted(set(edges) | set(np.random.default_rng(N + K).integers(0, N, 96 - len(edges)).tolist()))
+    ridx = torch.tensor(rows, dtype=torch.long, device="cuda")
+    W_rows = bits_of(W[ridx].contiguous())
+    q_ref, s_ref = oracle.quantize_rows_int8(W_rows)           # per row: the sampled rows stand alone
+    assert np.array_equal(Wq[ridx].cpu().numpy(), q_ref)
+    assert np.array_equal(sc[ridx].cpu().numpy(), s_ref)
+    for B in (1, 8):
+        x = torch.randn((B, K), generator=g, device="cuda").to(torch.bfloat16)
+        x_bits = bits_of(x)
+        y32 = torch.empty((B, N), dtype=torch.float32, device="cuda")
+        y16 = torch.empty((B, N), dtype=torch.bfloat16, device="cuda")
+        y8 = torch.empty((B, N), dtype=torch.float32, device="cuda")
+        sda.gemv_bf16(W, x, y32)
+        sda.gemv_bf16(W, x, y16)
+        sda.gemv_int8(Wq, sc, x, y8)
+        torch.cuda.synchronize()
+        ref = oracle.gemv(W_rows, x_bits)
+        bound = _bound(_f32(W_rows), _f32(x_bits))
+        _check_f32(y32[:, ridx], ref, bound)
+        _check_bf16(y16[:, ridx].contiguous(), ref, bound)
+        ref8 = oracle.gemv_int8(q_ref, s_ref, x_bits)
+        _check_f32(y8[:, ridx], ref8, _bound(q_ref.astype(np.float32) * s_ref[:, None], _f32(x_bits)))
+
+
 def test_gemv_graph_replay_with_new_activations():
     N, K, B = 512, 2048, 4
     W = workloads.bf16_randn((N, K), 750)
