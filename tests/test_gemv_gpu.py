@@ -79,6 +79,7 @@ SHAPES = [
     (8, 256, 14336),      # Llama-3-8B down-projection width (224 blocks of 64 k)
     (7, 1, 64),           # one row, one block: seven waves with no work
     (8, 33, 200),         # 4 blocks for 8 waves, the last holding 8 k
+    (8, 1600, 960),       # SmolLM2-360M q/k/v at B = 8: 15 blocks over 8 waves
 ]
 
 
@@ -132,7 +133,8 @@ def _codes(shape, seed):
 @pytest.mark.parametrize("B,N,K", [(1, 1600, 960), (1, 960, 2560), (1, 77, 1024), (1, 3, 16), (1, 77, 976),
                                    (2, 77, 976), (4, 960, 2560), (8, 77, 1024), (8, 64, 14336), (2, 3, 16),
                                    (3, 77, 976), (5, 3, 16), (8, 33, 208),
-                                   (3, 8200, 208), (8, 8193, 16)])   # two 16-row tiles per workgroup from N = 8192
+                                   (3, 8200, 208), (8, 8193, 16),    # two 16-row tiles per workgroup from N = 8192
+                                   (8, 1600, 960)])                  # 7.5 blocks of 128 k over 8 waves
 def test_gemv_int8_integer_data_is_exact(B, N, K):
     q = _codes((N, K), 730 + K)
     s = (2.0 ** np.random.default_rng(731).integers(-8, 1, size=N)).astype(np.float32)
