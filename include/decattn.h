@@ -144,9 +144,9 @@ int prefill_attn(const void* q, const void* k_cache, const void* v_cache,
  * Products accumulate in fp32. K must be a multiple of 8 (bf16) or 16 (int8);
  * B in 1..8, K up to 73728 (one staged vector fits 144 KB of LDS; larger K
  * gives DECATTN_ERR_UNSUPPORTED). One vector runs as dot products on the
- * vector units, with the vector in LDS; 2 to 8 run on the matrix cores in
- * one launch (16 x 16 x 32 bf16 products, INT8 codes widened to bf16
- * exactly). No host sync, capturable. W, Wq, x, y 16-byte aligned; scale
+ * vector units, with the vector in LDS (bf16 matrices of 16384 rows or more:
+ * on the matrix cores); 2 to 8 run on the matrix cores in one launch
+ * (16 x 16 x 32 bf16 products, INT8 codes widened to bf16 exactly). No host sync, capturable. W, Wq, x, y 16-byte aligned; scale
  * 4-byte aligned; (N + 64) * K weight bytes and B * K * 2 activation bytes
  * below 2^32. */
 int gemv_bf16(const void* W, const void* x, int B, int N, int K,

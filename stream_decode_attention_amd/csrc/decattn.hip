@@ -380,7 +380,8 @@ int gemv_common(const void* W, const float* scale, const void* x, int B, int N, 
     gp.out_bf16 = out_dtype == DECATTN_OUT_BF16;
     const size_t osz = gp.out_bf16 ? 2 : 4;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    if (B >= (int8 ? DECATTN_GEMV_MFMA_MIN_B_INT8 : DECATTN_GEMV_MFMA_MIN_B_BF16)) {
+    if (B >= (int8 ? DECATTN_GEMV_MFMA_MIN_B_INT8 : DECATTN_GEMV_MFMA_MIN_B_BF16) ||
+        (!int8 && N >= DECATTN_GEMV_MFMA_B1_MIN_N)) {
         // the matrix cores: every vector in one pass over the weights
         if ((size_t)B * K * 2 + 16 >= (1ull << 32)) return DECATTN_ERR_UNSUPPORTED;
         GemvMfmaParams mp{};

@@ -17,10 +17,11 @@
 // the group's first lane applies the row scale and stores y. The grid is
 // persistent: every wave walks row groups wave, wave + all waves, ...
 //
-// By default this dot-product kernel serves one vector and the matrix-core
-// kernel further down every B from 2; the kernel itself takes up to 8
-// vectors (raising DECATTN_GEMV_MFMA_MIN_B_* hands them to it, the setting
-// the rows-per-group rule below was measured in).
+// By default this dot-product kernel serves one vector (bf16 matrices of
+// 16384 rows or more excepted) and the matrix-core kernel further down every
+// B from 2; the kernel itself takes up to 8 vectors (raising
+// DECATTN_GEMV_MFMA_MIN_B_* hands them to it, the setting the rows-per-group
+// rule below was measured in).
 #pragma once
 
 #include "device_common.hpp"
@@ -234,10 +235,17 @@ typedef float gemv_f32x4_t __attribute__((ext_vector_type(4)));
 // Measured on MI355X over one Llama-3-8B layer (us per layer, dot-product
 // path / matrix cores): bf16 B = 2 80.6 / 75.4, B = 4 90.8 / 76.1, B = 8
 // 100.8 / 79.7; INT8 B = 2 54.8 / 53.8, B = 4 67.0 / 54.9. At B = 1 the
-// dot products win on most shapes (Llama-3-8B's 6144 x 4096: 10.8 / 13.0;
-// the matrix-core grid is N / 16 workgroups, 1.5 per CU there).
+// dot products win on matrices of fewer rows (Llama-3-8B's 6144 x 4096:
+// 10.8 / 13.0; the matrix-core grid is N / 16 workgroups, 1.5 per CU there).
 #ifndef DECATTN_GEMV_MFMA_MIN_B_BF16
 #define DECATTN_GEMV_MFMA_MIN_B_BF16 2
+#endif
+// bf16 matrices of this many rows take the matrix cores at B = 1 too: over
+// one Llama-3-8B layer (four products, the 28672-row gate/up the only one
+// this large) 80.0 -> 74.4 us; from 4096 or 6144 rows 76.1 / 76.8 us, the
+// 6144 x 4096 product alone 10.7 -> 13.0 us.
+#ifndef DECATTN_GEMV_MFMA_B1_MIN_N
+#define DECATTN_GEMV_MFMA_B1_MIN_N 16384
 #endif
 #ifndef DECATTN_GEMV_MFMA_MIN_B_INT8
 #define DECATTN_GEMV_MFMA_MIN_B_INT8 2

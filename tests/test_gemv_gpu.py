@@ -63,9 +63,9 @@ def _check_bf16(out, ref, bound):
 
 
 SHAPES = [
-    # B, N, K   (vector units, B = 1: lanes per row from K/8 chunks, >= 256 -> 64,
-    # >= 128 -> 32, else 16; matrix cores, B >= 2: 16-row tiles, 64-k blocks
-    # split over 8 waves)
+    # B, N, K   (vector units, B = 1 below 16384 rows: lanes per row from K/8
+    # chunks, >= 256 -> 64, >= 128 -> 32, else 16; matrix cores, B >= 2 and
+    # B = 1 from 16384 rows: 16-row tiles, 64-k blocks split over 8 waves)
     (1, 1600, 960),       # SmolLM2-360M fused q/k/v, 16 lanes per row
     (1, 960, 2560),       # SmolLM2 down projection, 64 lanes
     (1, 77, 1024),        # 32 lanes, ragged row count
@@ -80,6 +80,8 @@ SHAPES = [
     (7, 1, 64),           # one row, one block: seven waves with no work
     (8, 33, 200),         # 4 blocks for 8 waves, the last holding 8 k
     (8, 1600, 960),       # SmolLM2-360M q/k/v at B = 8: 15 blocks over 8 waves
+    (1, 16383, 256),      # one row short of the matrix cores at B = 1 (bf16)
+    (1, 16390, 200),      # the matrix cores at B = 1: ragged rows, a partial block
 ]
 
 
