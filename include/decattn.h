@@ -31,7 +31,13 @@
  *    [0, S_max], and a row with no keys outputs zeros.
  *  - Supported: D in {64, 128}; G = Hq / Hkv in 1..8; T in 1..16; chunk 0
  *    (library default) or a power of two in [16, 2^20] (a chunk >= S_max
- *    means one tile per row).
+ *    means one tile per row); B <= 4096; one kv head's cache, plus 512 keys
+ *    of slack, within a 32-bit byte range: (S_max + 512) * D * 2 < 2^32, i.e.
+ *    S_max <= 16776703 at D = 128 and <= 33553919 at D = 64. Shapes outside
+ *    this set give DECATTN_ERR_UNSUPPORTED, and decattn_workspace_bytes /
+ *    decattn_default_chunk return 0 for them.
+ *  - Lengths and the token offsets added to them (ctx + i + 1) are summed in
+ *    64 bits before the clamp, so any int32 length is safe.
  *  - Errors are returned, never thrown; no C++ exception crosses this ABI.
  */
 #ifndef DECATTN_H

@@ -40,6 +40,7 @@ constexpr size_t kMaxLdsBytes = 64 * 1024;
 constexpr int kMinChunk = 16;
 constexpr int kMaxChunk = 1 << 20;
 constexpr size_t kAlign = 256;
+constexpr int kKeyMargin = 512;            // keys a kernel may address past S_max (reading zeros)
 
 bool is_pow2(long long x) { return x > 0 && (x & (x - 1)) == 0; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -84,6 +85,10 @@ int make_plan(int B, int T, int Hq, int Hkv, int D, int S_max, int chunk, Plan* 
     if (chunk < kMinChunk || chunk > kMaxChunk || !is_pow2(chunk)) return DECATTN_ERR_UNSUPPORTED;
     const long long nc = ((long long)S_max + chunk - 1) / chunk;
     if ((long long)B * Hkv * S_max * (long long)D > (1LL << 46)) return DECATTN_ERR_UNSUPPORTED;
+    // the kernels address one kv head's cache through a buffer resource with a
+    // 32-bit byte range and 32-bit offsets; loads run up to a few sub-tiles
+    // (under kKeyMargin keys) past the last attended key
+    if (((long long)S_max + kKeyMargin) * D * 2 > 0xFFFFFFFFLL) return DECATTN_ERR_UNSUPPORTED;
     if (B > kMaxB || nc > 0x7FFFFFFF || (long long)B * T * Hq > 0x7FFFFFFF) return DECATTN_ERR_UNSUPPORTED;
 
     Plan p{};
@@ -248,13 +253,19 @@ int run_merge(const Plan& pl, const int32_t* lens, int causal, void* out, int ou
     return hipGetLastError() == hipSuccess ? DECATTN_OK : DECATTN_ERR_HIP;
 }
 
-int check_common(const void* q, const void* k, const void* v, const int32_t* lens, float scale,
-                 void* ws, size_t ws_bytes, const Plan& pl) {
-    if (!q || !k || !v || !lens || !ws) return DECATTN_ERR_INVALID_ARG;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(ws) ||
-        (reinterpret_cast<uintptr_t>(lens) & 3u))
+int check_inputs(const void* q, const void* k, const void* v, const int32_t* lens, float scale) {
+    if (!q || !k || !v || !lens) return DECATTN_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (reinterpret_cast<uintptr_t>(lens) & 3u))
         return DECATTN_ERR_INVALID_ARG;
     if (!std::isfinite(scale)) return DECATTN_ERR_INVALID_ARG;
+    return DECATTN_OK;
+}
+
+int check_common(const void* q, const void* k, const void* v, const int32_t* lens, float scale,
+                 void* ws, size_t ws_bytes, const Plan& pl) {
+    const int st = check_inputs(q, k, v, lens, scale);
+    if (st != DECATTN_OK) return st;
+    if (!ws || !aligned16(ws)) return DECATTN_ERR_INVALID_ARG;
     if (ws_bytes < pl.total_bytes) return DECATTN_ERR_WORKSPACE;
     return DECATTN_OK;
 }

@@ -174,4 +174,11 @@ __device__ __forceinline__ int clamp_len(int n, int s_max) {
     return n < 0 ? 0 : (n > s_max ? s_max : n);
 }
 
+// clamp(len + add, 0, s_max) with the sum taken in 64 bits: a device length
+// near INT_MAX plus a token offset must clamp to s_max, not wrap negative.
+__device__ __forceinline__ int clamp_len_add(int len, int add, int s_max) {
+    const long long n = (long long)len + add;
+    return n < 0 ? 0 : (n > s_max ? s_max : (int)n);
+}
+
 }  // namespace decattn

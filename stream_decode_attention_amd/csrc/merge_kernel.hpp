@@ -1,9 +1,9 @@
 // Log-sum-exp merge of the split-KV partial state: one workgroup per output row.
 //
 // For an output row with n attended keys, the first NA = ceil(n / chunk)
-// tiles hold its partial state (m_c in log2 units, l_c, acc_c). The merge
-// (llm-decode-cuda, attention section: "merges the chunks with the log-sum-exp
-// trick") is
+// tiles hold its partial state (m_c in log2 units, l_c, acc_c). The tiles are
+// combined by rescaling each to a common maximum (the log-sum-exp merge of
+// llm-decode-cuda's attention section):
 //     M = max_c m_c,  w_c = 2^(m_c - M),
 //     out = sum_c w_c acc_c / sum_c w_c l_c,
 // then stored as fp32 or rounded to bf16. Rows with n = 0 store zeros.
@@ -83,7 +83,7 @@ lse_merge(const MergeParams p) {
     fetch(cl, p.NC);
 
     const int len = p.lens[b];
-    const int n = clamp_len(p.causal ? len + i + 1 : len, p.S_max);
+    const int n = clamp_len_add(len, p.causal ? i + 1 : 0, p.S_max);
     int na = (n + p.chunk - 1) / p.chunk;
     na = na < p.NC ? na : p.NC;
 

@@ -183,7 +183,7 @@ split_kv_partial(const PartialParams p) {
     for (int i = tid; i < p.B; i += blockDim.x) {
         const int len = p.lens[i];
         s_len[i] = len;
-        const int lim = clamp_len(p.causal ? len + p.T : len, p.S_max);
+        const int lim = clamp_len_add(len, p.causal ? p.T : 0, p.S_max);
         my_tiles += (lim + p.chunk - 1) / p.chunk;
     }
     for (int o = 32; o > 0; o >>= 1) my_tiles += __shfl_xor(my_tiles, o);
@@ -201,7 +201,7 @@ split_kv_partial(const PartialParams p) {
     int b_cur = 0, pre_cur = 0;
     auto tiles_of = [&](int b) {
         const int len = s_len[b];
-        return (clamp_len(p.causal ? len + p.T : len, p.S_max) + p.chunk - 1) / p.chunk;
+        return (clamp_len_add(len, p.causal ? p.T : 0, p.S_max) + p.chunk - 1) / p.chunk;
     };
 
     struct Tile {
@@ -223,7 +223,7 @@ split_kv_partial(const PartialParams p) {
         tl.len = s_len[b_cur];
         tl.t0 = tl.c * p.chunk;
         tl.t1 = min(tl.t0 + p.chunk, p.S_max);
-        tl.lim_all = min(clamp_len(p.causal ? tl.len + p.T : tl.len, p.S_max), tl.t1);
+        tl.lim_all = min(clamp_len_add(tl.len, p.causal ? p.T : 0, p.S_max), tl.t1);
         return tl;
     };
 
@@ -243,7 +243,7 @@ split_kv_partial(const PartialParams p) {
             const int r = ok ? r0 : 0;
             const int i = r / p.G;
             const int h = tl.kvh * p.G + (r - i * p.G);
-            if (j == own && ok) my_lim = min(clamp_len(p.causal ? tl.len + i + 1 : tl.len, p.S_max), tl.t1);
+            if (j == own && ok) my_lim = min(clamp_len_add(tl.len, p.causal ? i + 1 : 0, p.S_max), tl.t1);
             qraw[j] = *reinterpret_cast<const uint4*>(p.q + ((size_t)(tl.b * p.T + i) * p.Hq + h) * D + db * 8);
         }
     };

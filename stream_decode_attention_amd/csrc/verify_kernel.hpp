@@ -126,9 +126,9 @@ verify_partial_mfma(const PartialParams p) {
     // empty state (m = -inf, l = 0, acc = 0) into the folded tile's slot, so
     // the merge still reads, for every row, slots that partition exactly the
     // keys that row attends.
-    auto tiles_raw = [&](int len) { return (clamp_len(len + p.T, p.S_max) + p.chunk - 1) / p.chunk; };
+    auto tiles_raw = [&](int len) { return (clamp_len_add(len, p.T, p.S_max) + p.chunk - 1) / p.chunk; };
     auto short_tail = [&](int len) {
-        const int lim = clamp_len(len + p.T, p.S_max);
+        const int lim = clamp_len_add(len, p.T, p.S_max);
         const int na = (lim + p.chunk - 1) / p.chunk;
         return na >= 2 && 4 * (lim - (na - 1) * p.chunk) <= p.chunk;
     };
@@ -175,7 +175,7 @@ verify_partial_mfma(const PartialParams p) {
         const int c = u % na;
         const int kvh = u / na;
         const int len = s_len[b];
-        const int lim_head = clamp_len(len + p.T, p.S_max);
+        const int lim_head = clamp_len_add(len, p.T, p.S_max);
         const bool folded = c == na - 1 && fold && short_tail(len);   // also takes the tile after it
         const int t0 = c * p.chunk;
         const int t1 = folded ? lim_head : min(t0 + p.chunk, p.S_max);
@@ -187,8 +187,8 @@ verify_partial_mfma(const PartialParams p) {
         const bool row_ok = n < p.RT;
         const int nr = row_ok ? n : 0;
         const int i = nr / p.G;
-        const int lim_n = row_ok ? min(clamp_len(len + i + 1, p.S_max), t1) : 0;
-        const int lim_min = min(clamp_len(len + 1, p.S_max), t1);   // row i = 0 attends the fewest keys
+        const int lim_n = row_ok ? min(clamp_len_add(len, i + 1, p.S_max), t1) : 0;
+        const int lim_min = min(clamp_len_add(len, 1, p.S_max), t1);   // row i = 0 attends the fewest keys
         const uint16_t* qrow = p.q + ((size_t)(b * p.T + i) * p.Hq + kvh * p.G + (nr - i * p.G)) * D + h * 8;
         uint4 qv[KS];
 #pragma unroll

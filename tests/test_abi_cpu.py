@@ -107,6 +107,35 @@ def test_decode_rejects_bad_arguments(lib, kw, status):
     assert _decode(lib, **kw) == status
 
 
+@pytest.mark.parametrize("D,refused", [(128, 1 << 24), (64, 1 << 25)])
+def test_one_kv_head_must_fit_a_32bit_byte_range(lib, D, refused):
+    """The kernels address one kv head's cache with 32-bit byte offsets, so
+    (S_max + 512) * D * 2 must stay below 2^32; past it every entry point that
+    plans split-KV tiles refuses instead of reading wrapped offsets."""
+    largest = (0xFFFFFFFF // (D * 2)) - 512
+    for T, Hq, Hkv in ((1, 8, 8), (6, 24, 8)):
+        assert sda.workspace_bytes(1, T, Hq, Hkv, D, refused, 0) == 0
+        assert sda.default_chunk(1, T, Hq, Hkv, D, refused) == 0
+        assert sda.workspace_bytes(1, T, Hq, Hkv, D, largest + 1, 0) == 0
+        assert sda.workspace_bytes(1, T, Hq, Hkv, D, largest, 0) > 0
+        assert sda.default_chunk(1, T, Hq, Hkv, D, largest) > 0
+    assert _decode(lib, B=1, Hq=8, Hkv=8, D=D, S=refused, wsb=1 << 40) == 2
+    assert _decode(lib, B=1, Hq=8, Hkv=8, D=D, S=largest + 1, wsb=1 << 40) == 2
+    chunk = lambda S: lib.chunk_attn(FAKE, FAKE, FAKE, FAKE, 1, 6, 24, 8, D, S, 0.088, FAKE, 1, FAKE,
+                                     1 << 40, 0, None)
+    assert chunk(refused) == 2
+    part = lambda S: lib.attn_partial(FAKE, FAKE, FAKE, FAKE, 1, 1, 8, 8, D, S, 0.1, 0, FAKE, 1 << 40, 0, None)
+    assert part(refused) == 2
+    merge = lambda S: lib.attn_merge(FAKE, 1, 1, 8, 8, D, S, 0, FAKE, 1, FAKE, 1 << 40, 0, None)
+    assert merge(refused) == 2
+    # the largest accepted S_max gets past the shape checks (it then fails on
+    # the deliberately tiny workspace, status 3, before anything is launched)
+    assert _decode(lib, B=1, Hq=8, Hkv=8, D=D, S=largest, wsb=16) == 3
+    assert lib.attn_merge(FAKE, 1, 1, 8, 8, D, largest, 0, FAKE, 1, FAKE, 16, 0, None) == 3
+    assert lib.chunk_attn(FAKE, FAKE, FAKE, FAKE, 1, 6, 24, 8, D, largest, 0.088, FAKE, 1, FAKE,
+                          16, 0, None) == 3
+
+
 def test_chunk_rejects_bad_arguments(lib):
     args = lambda T, wsb=1 << 24: (FAKE, FAKE, FAKE, FAKE, 1, T, 24, 8, 128, 16384, 0.088, FAKE, 1,
                                    FAKE, wsb, 0, None)
