@@ -100,6 +100,29 @@ int decode_attn(const void* q, const void* k_cache, const void* v_cache,
                 void* workspace, size_t workspace_bytes, int chunk,
                 void* stream);
 
+/* decode_attn for callers that cannot allocate device memory: code under
+ * hipGraph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, kernels and results as decode_attn (bit for bit, same
+ * chunk), with no workspace argument: the partial state goes to a static
+ * device array of DECATTN_NOALLOC_SCRATCH_BYTES inside the library, one per
+ * GPU, held until the process ends. The call allocates nothing and calls no
+ * allocating routine. Limits and behaviour:
+ *  - shapes whose workspace (decattn_workspace_bytes with T = 1) exceeds
+ *    DECATTN_NOALLOC_SCRATCH_BYTES are refused with DECATTN_ERR_WORKSPACE
+ *    before anything is launched (pass a larger chunk, or use decode_attn);
+ *  - every call on one GPU shares that GPU's array: calls that may overlap in
+ *    time on one GPU (two streams, two threads) race and must be ordered by
+ *    the caller, e.g. kept on one stream; the partial kernel writes every slot
+ *    the merge reads, so no clearing is needed between calls;
+ *  - the first call on each device looks up the array's device address
+ *    (hipGetSymbolAddress, host side only) and keeps it; make that first call
+ *    outside graph capture. A failed lookup returns DECATTN_ERR_HIP. */
+#define DECATTN_NOALLOC_SCRATCH_BYTES (8u << 20)
+int decode_attn_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* seq_lens,
+                        int B, int Hq, int Hkv, int D, int S_max, float scale,
+                        void* out, int out_dtype, int chunk, void* stream);
+
 /* Causal multi-query "chunk" attention for verifying T speculative tokens
  * (tinydecode README, "speculative decoding": the verify pass runs k+1 tokens
  * on top of the existing context, reading the cache once for all of them).

@@ -15,7 +15,7 @@ import torch
 
 __all__ = [
     "DecattnError", "load_library", "abi_version", "status_str", "default_chunk",
-    "workspace_bytes", "decode_attn", "chunk_attn", "attn_partial", "attn_merge",
+    "workspace_bytes", "decode_attn", "decode_attn_noalloc", "NOALLOC_SCRATCH_BYTES", "chunk_attn", "attn_partial", "attn_merge",
     "probe_read", "probe_copy", "rope_kv_write", "RopeParams", "prefill_attn",
     "gemv_bf16", "gemv_int8", "quantize_rows_int8", "spec_accept", "spec_accept_workspace_bytes",
     "OUT_BF16", "OUT_F32", "LIB_PATH",
@@ -23,6 +23,7 @@ __all__ = [
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdecattn.so")
 OUT_BF16, OUT_F32 = 0, 1
+NOALLOC_SCRATCH_BYTES = 8 << 20     # DECATTN_NOALLOC_SCRATCH_BYTES of include/decattn.h
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small", 4: "HIP error"}
 
 _lib: Optional[ctypes.CDLL] = None
@@ -43,6 +44,7 @@ _SIGNATURES = {
     "decattn_default_chunk": ([_i] * 6, _i),
     "decattn_workspace_bytes": ([_i] * 7, _sz),
     "decode_attn": ([_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _i, _vp, _sz, _i, _vp], _i),
+    "decode_attn_noalloc": ([_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _i, _i, _vp], _i),
     "chunk_attn": ([_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp, _i, _vp, _sz, _i, _vp], _i),
     "attn_partial": ([_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _i, _vp], _i),
     "prefill_attn": ([_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp, _i, _vp], _i),
@@ -193,6 +195,26 @@ def decode_attn(q, k_cache, v_cache, seq_lens, scale: float, out, workspace, chu
             _ptr(workspace, "workspace", (torch.uint8,)), workspace.numel(), int(chunk),
             _stream(stream, q.device))
     _check("decode_attn", st)
+    return out
+
+
+def decode_attn_noalloc(q, k_cache, v_cache, seq_lens, scale: float, out, chunk: int = 0, stream=None):
+    """decode_attn without a workspace argument: the library keeps the partial
+    state in its own static device array (NOALLOC_SCRATCH_BYTES per GPU) and
+    allocates nothing. Calls that may overlap on one GPU race; see
+    include/decattn.h."""
+    B, Hq, D = q.shape
+    _, Hkv, S_max, Dk = k_cache.shape
+    if Dk != D or tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(out.shape) != (B, Hq, D) \
+            or k_cache.shape[0] != B or tuple(seq_lens.shape) != (B,):
+        raise ValueError("shape mismatch between q, caches, seq_lens and out")
+    with _on_device(q, k_cache, v_cache, seq_lens, out):
+        st = load_library().decode_attn_noalloc(
+            _ptr(q, "q", _BF16), _ptr(k_cache, "k_cache", _BF16), _ptr(v_cache, "v_cache", _BF16),
+            _ptr(seq_lens, "seq_lens", (torch.int32,)), B, Hq, Hkv, D, S_max, float(scale),
+            _ptr(out, "out", (torch.float32,) + _BF16), _out_dtype(out), int(chunk),
+            _stream(stream, q.device))
+    _check("decode_attn_noalloc", st)
     return out
 
 

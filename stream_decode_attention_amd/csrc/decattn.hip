@@ -24,6 +24,9 @@
 #include "spec_kernel.hpp"
 #include "verify_kernel.hpp"
 
+// The scratch of decode_attn_noalloc (its use is described there).
+static __device__ __align__(256) unsigned char scratch[DECATTN_NOALLOC_SCRATCH_BYTES];
+
 namespace decattn {
 namespace {
 
@@ -207,6 +210,32 @@ hipError_t launch_partial_d(const Plan& pl, const PartialParams& pp, hipStream_t
         case 8: return launch_partial_dr<D, 8>(pl, pp, s);
         default: return hipErrorInvalidValue;
     }
+}
+
+// ---- the allocation-free decode entry point's scratch ----------------------
+//
+// decode_attn_noalloc keeps its partial state in this file-scope device array
+// instead of a caller's workspace. Every GPU the library runs on holds its own
+// copy, at its own address, until the process ends. In host code the array's
+// name is only a host-side stand-in: kernels must be handed the device address
+// that hipGetSymbolAddress returns for the current device, never `scratch`.
+constexpr int kMaxDevices = 64;
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per device
+// (with that device current) and kept; nullptr when the lookup fails.
+void* scratch_for_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
 }
 
 // Scores are taken in log2 units (softmax on exp2): the kernels multiply q.k
@@ -540,6 +569,22 @@ int decode_attn(const void* q, const void* k_cache, const void* v_cache, const i
                 size_t workspace_bytes, int chunk, void* stream) {
     return attention(q, k_cache, v_cache, seq_lens, B, 1, Hq, Hkv, D, S_max, scale, 0, out, out_dtype,
                      workspace, workspace_bytes, chunk, stream);
+}
+
+int decode_attn_noalloc(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens,
+                        int B, int Hq, int Hkv, int D, int S_max, float scale, void* out, int out_dtype,
+                        int chunk, void* stream) {
+    Plan pl;
+    int st = make_plan(B, 1, Hq, Hkv, D, S_max, chunk, &pl);
+    if (st != DECATTN_OK) return st;
+    if ((st = check_inputs(q, k_cache, v_cache, seq_lens, scale)) != DECATTN_OK) return st;
+    if ((st = check_out(out, out_dtype)) != DECATTN_OK) return st;
+    if (pl.total_bytes > DECATTN_NOALLOC_SCRATCH_BYTES) return DECATTN_ERR_WORKSPACE;
+    void* ws = scratch_for_current_device();    // the device address, never `scratch` itself
+    if (!ws) return DECATTN_ERR_HIP;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = run_partial(pl, q, k_cache, v_cache, seq_lens, scale, 0, ws, s)) != DECATTN_OK) return st;
+    return run_merge(pl, seq_lens, 0, out, out_dtype, ws, s);
 }
 
 int chunk_attn(const void* q, const void* k_cache, const void* v_cache, const int32_t* ctx_lens, int B,

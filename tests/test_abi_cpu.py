@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = set(declared_functions())
-    assert {"decode_attn", "chunk_attn", "attn_partial", "attn_merge", "decattn_workspace_bytes",
+    assert {"decode_attn", "decode_attn_noalloc", "chunk_attn", "attn_partial", "attn_merge", "decattn_workspace_bytes",
             "decattn_default_chunk", "decattn_status_str", "decattn_abi_version",
             "decattn_probe_read", "decattn_probe_copy", "rope_kv_write", "prefill_attn",
             "gemv_bf16", "gemv_int8", "quantize_rows_int8", "spec_accept",
@@ -134,6 +134,23 @@ def test_one_kv_head_must_fit_a_32bit_byte_range(lib, D, refused):
     assert lib.attn_merge(FAKE, 1, 1, 8, 8, D, largest, 0, FAKE, 1, FAKE, 16, 0, None) == 3
     assert lib.chunk_attn(FAKE, FAKE, FAKE, FAKE, 1, 6, 24, 8, D, largest, 0.088, FAKE, 1, FAKE,
                           16, 0, None) == 3
+
+
+def test_noalloc_decode_rejects_before_touching_the_device(lib):
+    """decode_attn_noalloc checks everything on the host first: bad shapes and
+    pointers, and a partial state larger than its static scratch array, return a
+    status before the device array is looked up or anything is launched."""
+    def call(B=1, Hq=8, Hkv=2, D=64, S=64, q=FAKE, lens=FAKE, out=FAKE, od=1, chunk=0, scale=0.125):
+        return lib.decode_attn_noalloc(q, FAKE, FAKE, lens, B, Hq, Hkv, D, S, scale, out, od, chunk, None)
+    assert call(Hq=9) == 1 and call(D=96) == 2 and call(q=None) == 1 and call(lens=FAKE + 2) == 1
+    assert call(out=FAKE + 4) == 1 and call(od=5) == 1 and call(scale=float("nan")) == 1
+    assert call(chunk=48) == 2 and call(S=1 << 24, D=128) == 2
+    # B = 8, Hq = 32, S_max = 32768 at 128-key tiles: ~35 MB of partial state
+    need = sda.workspace_bytes(8, 1, 32, 8, 128, 32768, 128)
+    assert need > sda.NOALLOC_SCRATCH_BYTES
+    assert call(B=8, Hq=32, Hkv=8, D=128, S=32768, chunk=128) == 3
+    # the headline shape at its default tiles fits
+    assert sda.workspace_bytes(8, 1, 32, 8, 128, 32768, 0) <= sda.NOALLOC_SCRATCH_BYTES
 
 
 def test_chunk_rejects_bad_arguments(lib):
