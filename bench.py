@@ -11,19 +11,25 @@ Every timed call runs inside a captured graph (the form a decode loop runs
 in, all of a step's layer calls in one graph). value = algorithmic KV bytes
 per call / µs per call, from one graph of the K timed calls on the two cache
 copies in turn, timed with HIP events on the replay stream (a long read keeps
-the GPU busy while the host launches it), median of 5 rounds;
-each call's K/V was last read two calls earlier, with 487 MB of other K/V read
-since (more than the 256 MB Infinity Cache holds). "launch_floor_us" replays
-the same launches with every length 0. "one_call_per_graph" reports a graph
-of a single call, warm and after a 1 GiB read that evicts the Infinity Cache,
-with its own floor (each graph launch costs several µs on its own). The
-partial kernel alone is replayed the same way for the roofline entry. The
-other four workloads are timed the same way and reported under "workloads";
-the steps around attention (rope_kv_write, prefill_attn, the GEMV weight
-products, the speculative accept/reject step spec_accept) under their own
-keys.
-The fp64 CPU oracle is timed on the headline workload on this host as
-"cpu_baseline".
+the GPU busy while the host launches it), median of 9 rounds (p10 and p90
+reported beside it); each call's K/V was last read two calls earlier, with
+487 MB of other K/V read since (more than the 256 MB Infinity Cache holds).
+"launch_floor_us" replays the same launches with every length 0;
+"one_tile_ablation" the same call with one tile per row (chunk = S_max), the
+pages' baseline for split-KV. "one_call_per_graph" reports a graph of a
+single call, warm and after a 1 GiB read that evicts the Infinity Cache, with
+its own floor (each graph launch costs several µs on its own). The partial
+kernel alone is replayed the same way for the roofline entry. The other four
+workloads are timed per graph replay (median, p10, p90 of at least 50) and
+reported under "workloads"; the steps around attention (rope_kv_write,
+prefill_attn, the GEMV weight products, the speculative accept/reject step
+spec_accept) under their own keys.
+
+The fp64 CPU oracle runs first, before the GPU is touched, on every workload
+(whole calls, or whole steps of layer calls): one BLAS thread in one process,
+then the same independent slices over a pool of worker processes. The
+headline's figure is "cpu_baseline"; the others sit in each workload's
+"cpu_oracle".
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--headline-only]
 """
@@ -97,6 +103,33 @@ def back_to_back_us(torch, stream, graphs, steps, warmup, busy=None):
     return e0.elapsed_time(e1) * 1e3 / steps
 
 
+def replay_dist_us(torch, stream, graphs, steps, warmup, busy=None):
+    """µs of each of ``steps`` back-to-back replays of graphs[i % len], from an
+    event recorded after every replay on the replay stream (``busy`` as in
+    back_to_back_us). Returns the list of per-replay times."""
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            graphs[i % len(graphs)].replay()
+        stream.synchronize()
+        if busy is not None:
+            busy()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record(stream)
+        for i in range(steps):
+            graphs[i % len(graphs)].replay()
+            ev[i + 1].record(stream)
+        ev[-1].synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(steps)]
+
+
+def dist(xs, scale=1.0, nd=2):
+    """median / p10 / p90 of xs (times scale), rounded."""
+    import numpy as np
+    a = np.asarray(xs, dtype=np.float64) * scale
+    return {"median": round(float(np.median(a)), nd), "p10": round(float(np.percentile(a, 10)), nd),
+            "p90": round(float(np.percentile(a, 90)), nd)}
+
+
 def cold_us(torch, stream, graphs, n, flush):
     """Median µs of single replays, each preceded by ``flush`` (a 1 GiB read that
     evicts the 256 MB Infinity Cache and keeps the GPU busy while the host
@@ -135,6 +168,16 @@ def main():
     import stream_decode_attention_amd as sda
     import workloads
     from stream_decode_attention_amd import roofline as rf
+
+    # ---------------------------------------------- inputs, then the CPU oracle
+    # (before anything touches the GPU: the oracle's worker processes fork)
+    t = time.time()
+    inputs = {cfg: [workloads.make_config(cfg, layer=l) for l in range(workloads.CONFIGS[cfg].layers)]
+              for cfg in ((4,) if args.headline_only else (1, 2, 3, 4, 5))}
+    c4 = inputs[4][0]
+    w4 = c4["workload"]
+    log(f"inputs generated in {time.time() - t:.1f}s, workload 4 lens {c4['lens'].tolist()}")
+    cpu = None if args.no_cpu_baseline else cpu_oracle_runs(inputs, rf)
 
     sda.load_library()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
@@ -175,10 +218,6 @@ def main():
         sda.probe_read(flush_buf, sink, stream=stream)
 
     # ------------------------------------------------------ headline: workload 4
-    t = time.time()
-    c4 = workloads.make_config(4)
-    w4 = c4["workload"]
-    log(f"workload 4 generated in {time.time() - t:.1f}s, lens {c4['lens'].tolist()}")
     q = up(c4["q"])
     ks = [up(c4["k"])]
     vs = [up(c4["v"])]
@@ -207,7 +246,7 @@ def main():
     # turn: each call's K/V was last read two calls earlier, with 487 MB of other
     # K/V read since, more than the 256 MB Infinity Cache holds.
     K, W = args.steps, max(1, args.warmup)
-    ROUNDS = 5
+    ROUNDS = 9
 
     def graphs_for(make):
         return (graph_of(torch, stream, [make(i % 2) for i in range(W)]),
@@ -228,6 +267,19 @@ def main():
             per_round[name].append(back_to_back_us(torch, stream, [timed], 1, 0, busy=flush) / K)
     us_call, us_part, us_floor = (float(np.median(per_round[n])) for n in ("call", "partial", "floor"))
     del kinds
+    # the pages' baseline for split-KV: one tile per row (llm-decode-cuda's one
+    # block per head), the same call with chunk = S_max
+    ws_one = torch.empty(sda.workspace_bytes(w4.B, 1, w4.Hq, w4.Hkv, w4.D, w4.S_max, w4.S_max),
+                         dtype=torch.uint8, device=dev)
+    g_one_tile = graphs_for(lambda i: (lambda: sda.decode_attn(q, ks[i], vs[i], lens, c4["scale"], out, ws_one,
+                                                               w4.S_max, stream=stream)))
+    one_tile_rounds = []
+    for _ in range(3):
+        with torch.cuda.stream(stream):
+            g_one_tile[0].replay()
+        one_tile_rounds.append(back_to_back_us(torch, stream, [g_one_tile[1]], 1, 0, busy=flush) / K)
+    us_one_tile = float(np.median(one_tile_rounds))
+    del g_one_tile
     # one call per graph: what a lone replay costs, warm and after an Infinity Cache flush
     g_one = [graph_of(torch, stream, [call(i)]) for i in range(2)]
     g_one_floor = [graph_of(torch, stream, [call(i, zero_lens)]) for i in range(2)]
@@ -273,7 +325,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
+        "accum_dtype": "f32",
         "data": "synthetic",
         "config": {
             "workload": w4.name, "B": w4.B, "Hq": w4.Hq, "Hkv": w4.Hkv, "D": w4.D, "S_max": w4.S_max,
@@ -284,6 +337,16 @@ def main():
         "calls_per_graph": K,
         "rounds": ROUNDS,
         "us_per_call_rounds": [round(x, 2) for x in per_round["call"]],
+        "us_per_call_dist": dist(per_round["call"]),
+        "partial_us_dist": dist(per_round["partial"]),
+        "launch_floor_us_dist": dist(per_round["floor"]),
+        "one_tile_ablation": {
+            "what": "the same call with chunk = S_max: one tile (one workgroup) per (sequence, kv head), the "
+                    "pages' one-block-per-head baseline for split-KV",
+            "chunk": w4.S_max, "us_per_call": round(us_one_tile, 2),
+            "us_per_call_rounds": [round(x, 2) for x in one_tile_rounds],
+            "GBps": round(kv_bytes / (us_one_tile / 1e6) / 1e9, 1),
+            "split_kv_speedup": round(us_one_tile / us_call, 2)},
         "frac_of_hbm_peak": round(value / rf.HBM_PEAK_GBPS, 4),
         "launch_floor_us": round(us_floor, 2),
         "one_call_per_graph": {
@@ -331,12 +394,27 @@ def main():
 
     # ------------------------------------------------------- other workloads
     if not args.headline_only:
-        result["workloads"] = other_workloads(args, dev, up, sda, workloads, rf, np, torch, stream, flush)
+        result["workloads"] = other_workloads(args, dev, up, sda, workloads, rf, np, torch, stream, flush,
+                                             inputs)
         result["rope_kv_write"].append(result["workloads"][-1].pop("rope_kv_write"))
 
     # ------------------------------------------------------ CPU oracle baseline
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(c4, rf, np)
+    if cpu is not None:
+        h = cpu[w4.name]
+        result["cpu_baseline"] = {
+            "value": h["all_cores"]["GBps"], "unit": "GB/s", "cores": h["all_cores"]["cores"], "kind": "oracle",
+            "sample": f"the whole headline call (all {w4.B * w4.Hq} query rows, {kv_bytes} KV bytes), fp64 NumPy "
+                      f"oracle, {h['sample'][len('the whole call, '):]} over {h['all_cores']['cores']} worker "
+                      f"processes with one BLAS thread each; median of {h['all_cores']['runs']} runs of "
+                      f"{h['all_cores']['s_per_unit']['median']:.3f} s",
+            "s_per_call": h["all_cores"]["s_per_unit"],
+            "single_core": {"value": h["GBps"], "unit": "GB/s", "cores": 1, "runs": h["runs"],
+                            "s_per_call": h["s_per_unit"]}}
+        for e in result.get("workloads", []):
+            key = e["workload"] + (f"@{e['n']}" if e["workload"].startswith(("smollm2", "tinyllama")) and
+                                   "calls_per_step" in e else "")
+            if key in cpu:
+                e["cpu_oracle"] = cpu[key]
 
     print(json.dumps(result), flush=True)
 
@@ -361,11 +439,13 @@ def rope_timings(args, sda, torch, np, stream, flush, rope_call, attn_call, floo
               "step": graph_of(torch, stream, [f for _ in range(K // 2) for f in (rope_call, attn_call)]),
               "attn": graph_of(torch, stream, [attn_call] * (K // 2))}
     per = {n: [] for n in graphs}
-    for _ in range(5):
+    for _ in range(7):
         for n, g in graphs.items():
             calls = K if n in ("rope", "floor") else K // 2
             per[n].append(back_to_back_us(torch, stream, [g], 1, 1, busy=flush) / calls)
-    return {n: float(np.median(v)) for n, v in per.items()}
+    res = {n: float(np.median(v)) for n, v in per.items()}
+    res["dist"] = {n: dist(v) for n, v in per.items()}
+    return res
 
 
 def rope_step_headline(args, up, sda, workloads, rf, np, torch, stream, flush, c4, q, ks, vs, lens):
@@ -405,7 +485,7 @@ def rope_step_headline(args, up, sda, workloads, rf, np, torch, stream, flush, c
             "theta": ROPE_THETA, "pairing": "half", "llama3_scaling": False, "calls_per_graph": 50,
             "us_per_call": round(t["rope"], 2), "launch_floor_us": round(t["floor"], 2),
             "bytes_per_call": nb, "GBps": round(nb / (t["rope"] / 1e6) / 1e9, 1),
-            "step_us": round(t["step"], 2), "attention_alone_us": round(t["attn"], 2)}
+            "step_us": round(t["step"], 2), "attention_alone_us": round(t["attn"], 2), "rounds_dist": t["dist"]}
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
@@ -444,9 +524,10 @@ def prefill_runs(up, sda, workloads, np, torch, stream, flush):
                 sda.prefill_attn(q, k, v, lens, scale, out, stream=stream)
                 stream.synchronize()
             g = graph_of(torch, stream, [lambda: sda.prefill_attn(q, k, v, lens, scale, out, stream=stream)] * 5)
-            us = float(np.median([back_to_back_us(torch, stream, [g], 1, 1, busy=flush) / 5 for _ in range(5)]))
+            rounds = [back_to_back_us(torch, stream, [g], 1, 1, busy=flush) / 5 for _ in range(7)]
+            us = float(np.median(rounds))
             tf = entry["flops_per_call"] / us / 1e6
-            entry[tag] = {"us_per_call": round(us, 2), "TFLOPs": round(tf, 1),
+            entry[tag] = {"us_per_call": round(us, 2), "us_per_call_dist": dist(rounds), "TFLOPs": round(tf, 1),
                           "frac_of_bf16_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
             del g
         log(f"prefill_attn {name}: bf16 out {entry['bf16_out']['us_per_call']:.1f} us "
@@ -501,11 +582,13 @@ def gemv_runs(sda, np, torch, stream, flush):
                     step(0)
                     stream.synchronize()
                 gr = graph_of(torch, stream, [lambda l=l: step(l) for l in range(nl)])
-                us = float(np.median([back_to_back_us(torch, stream, [gr], 1, 1, busy=flush) for _ in range(5)]))
+                rounds = [back_to_back_us(torch, stream, [gr], 1, 1, busy=flush) for _ in range(7)]
+                us = float(np.median(rounds))
                 wbytes = nl * sum(N * K * (1 if int8 else 2) + (4 * N if int8 else 0) for N, K in mats)
                 gbps = wbytes / us / 1e3
                 entry[f"{'int8' if int8 else 'bf16'}_B{B}"] = {
-                    "us_per_graph": round(us, 1), "launches": 4 * nl, "weight_bytes": wbytes,
+                    "us_per_graph": round(us, 1), "us_per_graph_dist": dist(rounds, nd=1), "launches": 4 * nl,
+                    "weight_bytes": wbytes,
                     "GBps": round(gbps, 1), "frac_of_hbm_peak": round(gbps / 8000.0, 4)}
                 log(f"gemv {name} {'int8' if int8 else 'bf16'} B={B}: {us:.1f} us for {4 * nl} products, "
                     f"{gbps:.0f} GB/s of weights")
@@ -551,10 +634,12 @@ def spec_runs(sda, workloads, np, torch, stream, flush):
                 stream.synchronize()
             n_kept = copies[0]["res"][:, 0].float().mean().item()
             g = graph_of(torch, stream, [lambda d=d: call(d) for d in copies * 2])
-            us = float(np.median([back_to_back_us(torch, stream, [g], 1, 1, busy=flush) / 4 for _ in range(5)]))
+            rounds = [back_to_back_us(torch, stream, [g], 1, 1, busy=flush) / 4 for _ in range(7)]
+            us = float(np.median(rounds))
             alg = B * T * V * 4 + (B * V * 4 if tau else 0)
             gbps = alg / us / 1e3
-            entry[tag] = {"us_per_call": round(us, 2), "algorithmic_bytes": alg, "GBps": round(gbps, 1),
+            entry[tag] = {"us_per_call": round(us, 2), "us_per_call_dist": dist(rounds), "algorithmic_bytes": alg,
+                          "GBps": round(gbps, 1),
                           "frac_of_hbm_peak": round(gbps / 8000.0, 4), "mean_drafts_kept": round(n_kept, 2),
                           "launches": 2 if tau == 0 else 3}
             log(f"spec_accept {name} {tag}: {us:.1f} us per call, {gbps:.0f} GB/s, "
@@ -564,12 +649,14 @@ def spec_runs(sda, workloads, np, torch, stream, flush):
     return res
 
 
-def other_workloads(args, dev, up, sda, workloads, rf, np, torch, stream, flush):
+def other_workloads(args, dev, up, sda, workloads, rf, np, torch, stream, flush, inputs):
+    """Workloads 1, 2, 3 and 5, each timed per graph replay over at least 50
+    back-to-back replays: median, p10 and p90 of the per-replay times."""
     res = []
-    steps = max(20, args.steps)
+    steps = max(50, args.steps)
 
-    # workload 1: one small call per graph, latency only
-    c = workloads.make_config(1)
+    # workload 1: one small call, 16 calls per graph, latency only
+    c = inputs[1][0]
     w = c["workload"]
     q, k, v = up(c["q"]), up(c["k"]), up(c["v"])
     lens = torch.from_numpy(c["lens"]).to(dev)
@@ -577,66 +664,88 @@ def other_workloads(args, dev, up, sda, workloads, rf, np, torch, stream, flush)
     out = torch.empty((1, w.Hq, w.D), dtype=torch.float32, device=dev)
     g1 = [graph_of(torch, stream, [lambda: sda.decode_attn(q, k, v, lens, c["scale"], out, ws, w.chunk,
                                                               stream=stream)] * 16)]
-    us = back_to_back_us(torch, stream, g1, steps, args.warmup, busy=flush) / 16
-    res.append({"workload": w.name, "n": 64, "chunk": w.chunk, "calls_per_graph": 16, "us_per_call": round(us, 2),
-                "kv_bytes_per_call": rf.kv_bytes_decode([64], w.Hkv, w.D, w.S_max)})
-    log(f"workload 1: {us:.2f} us/call")
+    d = dist(replay_dist_us(torch, stream, g1, steps, args.warmup, busy=flush), 1 / 16)
+    res.append({"workload": w.name, "n": 64, "chunk": w.chunk, "calls_per_graph": 16, "us_per_call": d["median"],
+                "us_per_call_dist": d, "kv_bytes_per_call": rf.kv_bytes_decode([64], w.Hkv, w.D, w.S_max)})
+    log(f"workload 1: {d['median']:.2f} us/call (p10 {d['p10']:.2f}, p90 {d['p90']:.2f})")
     del g1
 
     # workloads 2 and 3: a graph of L independent layer calls per step, replayed
-    # with the device-resident length rewritten; three cache sets rotate
+    # with the device-resident length rewritten; three cache sets rotate.
+    # Workload 2 at its longest length also runs with one tile per row (chunk =
+    # S_max), the pages' baseline for split-KV.
     for cfg in (2, 3):
         w = workloads.CONFIGS[cfg]
-        layers = [workloads.make_config(cfg, layer=l) for l in range(w.layers)]
-        chunk = sda.default_chunk(1, 1, w.Hq, w.Hkv, w.D, w.S_max)
+        layers = inputs[cfg]
         lens = torch.zeros(1, dtype=torch.int32, device=dev)
         sets = []
-        for s in range(3):
+        for si in range(3):
             tens = []
             for l, cl in enumerate(layers):
                 kq = up(cl["q"])
-                kk = up(cl["k"]) if s == 0 else sets[0][l][1].clone()
-                vv = up(cl["v"]) if s == 0 else sets[0][l][2].clone()
-                wsl = torch.empty(sda.workspace_bytes(1, 1, w.Hq, w.Hkv, w.D, w.S_max, chunk),
-                                  dtype=torch.uint8, device=dev)
+                kk = up(cl["k"]) if si == 0 else sets[0][l][1].clone()
+                vv = up(cl["v"]) if si == 0 else sets[0][l][2].clone()
                 o = torch.empty((1, w.Hq, w.D), dtype=torch.bfloat16, device=dev)
-                tens.append((kq, kk, vv, wsl, o))
+                tens.append((kq, kk, vv, o))
             sets.append(tens)
         scale = layers[0]["scale"]
+        chunk = sda.default_chunk(1, 1, w.Hq, w.Hkv, w.D, w.S_max)
 
-        def step_fns(tens):
-            return [lambda t=t: sda.decode_attn(t[0], t[1], t[2], lens, scale, t[4], t[3], chunk, stream=stream)
-                    for t in tens]
+        def make_graphs(ch):
+            wsl = [torch.empty(sda.workspace_bytes(1, 1, w.Hq, w.Hkv, w.D, w.S_max, ch), dtype=torch.uint8,
+                               device=dev) for _ in layers]
 
-        lens.fill_(max(w.lens))
-        torch.cuda.synchronize()
-        with torch.cuda.stream(stream):
-            for tens in sets:
-                for fn in step_fns(tens):
-                    fn()
-            stream.synchronize()
-        graphs = [graph_of(torch, stream, step_fns(tens)) for tens in sets]
+            def step_fns(tens):
+                return [lambda t=t, wl=wl: sda.decode_attn(t[0], t[1], t[2], lens, scale, t[3], wl, ch,
+                                                           stream=stream)
+                        for t, wl in zip(tens, wsl)]
+            lens.fill_(max(w.lens))
+            torch.cuda.synchronize()
+            with torch.cuda.stream(stream):
+                for tens in sets:
+                    for fn in step_fns(tens):
+                        fn()
+                stream.synchronize()
+            return [graph_of(torch, stream, step_fns(tens)) for tens in sets], wsl
+
+        graphs, _wsl = make_graphs(chunk)
         lens.fill_(0)
         torch.cuda.synchronize()
-        floor = back_to_back_us(torch, stream, graphs, steps, args.warmup, busy=flush)
+        floor = dist(replay_dist_us(torch, stream, graphs, steps, args.warmup, busy=flush))
         for n in w.lens:
             lens.fill_(n)
             torch.cuda.synchronize()
-            us = back_to_back_us(torch, stream, graphs, steps, args.warmup, busy=flush)
+            d = dist(replay_dist_us(torch, stream, graphs, steps, args.warmup, busy=flush))
+            us = d["median"]
             kvb = rf.kv_bytes_decode([n], w.Hkv, w.D, w.S_max) * w.layers
             res.append({"workload": w.name, "n": n, "chunk": chunk, "calls_per_step": w.layers,
-                        "us_per_step": round(us, 2), "us_per_call": round(us / w.layers, 3),
-                        "launch_floor_us_per_step": round(floor, 2),
+                        "us_per_step": us, "us_per_step_dist": d, "us_per_call": round(us / w.layers, 3),
+                        "launch_floor_us_per_step": floor["median"], "launch_floor_us_per_step_dist": floor,
                         "kv_bytes_per_step": kvb, "GBps": round(kvb / (us / 1e6) / 1e9, 1),
                         "frac_of_hbm_peak": round(kvb / (us / 1e6) / 1e9 / rf.HBM_PEAK_GBPS, 4)})
-            log(f"workload {cfg} n={n}: {us:.1f} us/step ({us / w.layers:.2f} us/call), "
-                f"{res[-1]['GBps']:.0f} GB/s (floor {floor:.1f} us/step)")
-        del graphs
+            log(f"workload {cfg} n={n}: {us:.1f} us/step ({us / w.layers:.2f} us/call, p10 {d['p10']:.1f}, "
+                f"p90 {d['p90']:.1f}), {res[-1]['GBps']:.0f} GB/s (floor {floor['median']:.1f} us/step)")
+        del graphs, _wsl
+        if cfg == 2:
+            n = max(w.lens)
+            graphs, _wsl = make_graphs(w.S_max)
+            lens.fill_(n)
+            torch.cuda.synchronize()
+            d = dist(replay_dist_us(torch, stream, graphs, steps, args.warmup, busy=flush))
+            kvb = rf.kv_bytes_decode([n], w.Hkv, w.D, w.S_max) * w.layers
+            res[-1]["one_tile_ablation"] = {
+                "what": "the same step with chunk = S_max: one tile (one workgroup) per kv head",
+                "chunk": w.S_max, "us_per_step": d["median"], "us_per_step_dist": d,
+                "us_per_call": round(d["median"] / w.layers, 3), "GBps": round(kvb / (d["median"] / 1e6) / 1e9, 1),
+                "split_kv_speedup": round(d["median"] / res[-1]["us_per_step"], 2)}
+            log(f"workload 2 n={n}, one tile per row: {d['median'] / w.layers:.2f} us/call "
+                f"({res[-1]['one_tile_ablation']['split_kv_speedup']:.2f}x the split-KV time)")
+            del graphs, _wsl
         torch.cuda.synchronize()
-        del sets, layers
+        del sets
 
-    # workload 5: verify chunk, one call per graph, eight cache copies rotate
-    c = workloads.make_config(5)
+    # workload 5: verify chunk, eight calls per graph on eight cache copies
+    c = inputs[5][0]
     w = c["workload"]
     chunk = sda.default_chunk(w.B, w.T, w.Hq, w.Hkv, w.D, w.S_max)
     q = up(c["q"])
@@ -650,13 +759,14 @@ def other_workloads(args, dev, up, sda, workloads, rf, np, torch, stream, flush)
         stream.synchronize()
     g5 = [graph_of(torch, stream, [lambda kv=kv: sda.chunk_attn(q, kv[0], kv[1], lens, c["scale"], out, ws, chunk,
                                                                    stream=stream) for kv in kvs])]
-    us = back_to_back_us(torch, stream, g5, steps, args.warmup, busy=flush) / len(kvs)
+    d = dist(replay_dist_us(torch, stream, g5, steps, args.warmup, busy=flush), 1 / len(kvs))
+    us = d["median"]
     kvb = rf.kv_bytes_chunk(c["lens"], w.T, w.Hkv, w.D, w.S_max)
     res.append({"workload": w.name, "ctx": int(c["lens"][0]), "T": w.T, "chunk": chunk,
-                "calls_per_graph": len(kvs), "us_per_call": round(us, 2),
+                "calls_per_graph": len(kvs), "us_per_call": us, "us_per_call_dist": d,
                 "kv_bytes_per_call": kvb, "GBps": round(kvb / (us / 1e6) / 1e9, 1),
                 "frac_of_hbm_peak": round(kvb / (us / 1e6) / 1e9 / rf.HBM_PEAK_GBPS, 4)})
-    log(f"workload 5: {us:.1f} us/call, {res[-1]['GBps']:.0f} GB/s")
+    log(f"workload 5: {us:.1f} us/call (p10 {d['p10']:.1f}, p90 {d['p90']:.1f}), {res[-1]['GBps']:.0f} GB/s")
     del g5
 
     # the verify step before attention: rotate and write the T draft tokens
@@ -689,38 +799,111 @@ def other_workloads(args, dev, up, sda, workloads, rf, np, torch, stream, flush)
         "S_max": w.S_max, "theta": ROPE_THETA, "pairing": "half", "llama3_scaling": ROPE_LLAMA3,
         "calls_per_graph": 50, "us_per_call": round(t["rope"], 2), "launch_floor_us": round(t["floor"], 2),
         "bytes_per_call": nb, "GBps": round(nb / (t["rope"] / 1e6) / 1e9, 1),
-        "step_us": round(t["step"], 2), "attention_alone_us": round(t["attn"], 2)}
+        "step_us": round(t["step"], 2), "attention_alone_us": round(t["attn"], 2), "rounds_dist": t["dist"]}
     return res
 
 
-def cpu_baseline(c4, rf, np, budget_s=10.0):
-    """The fp64 oracle, as it stands, on the whole headline call, repeated for
-    about ``budget_s`` seconds (at least 3 runs); one thread, then every core."""
+# ------------------------------------------------------------ CPU oracle baseline
+#
+# The fp64 oracle, as it stands, timed on this host's cores in the same run as
+# the GPU figures. It runs before the GPU is touched: the all-cores leg is a
+# pool of forked worker processes, and a process that has initialised the GPU
+# is not forked. Every workload's call (or step of layer calls) is split into
+# independent slices -- one sequence and a range of kv heads with their query
+# heads -- and each slice is the unchanged oracle on that part of the inputs
+# (heads do not interact, so the slices' outputs are the call's output).
+
+_ORACLE_INPUTS = {}     # name -> list of per-call inputs; forked workers inherit it
+
+
+def _oracle_slice(task):
+    """Oracle output of one slice: (name, call, b, kv0, kv1, n) -> array. A
+    length n overrides the call's own (workloads 2 and 3 replay one cache at
+    several lengths)."""
+    import numpy as np
     import oracle
+    name, call, b, kv0, kv1, n = task
+    c = _ORACLE_INPUTS[name][call]
+    k, v = c["k"][b:b + 1, kv0:kv1], c["v"][b:b + 1, kv0:kv1]
+    G = c["q"].shape[-2] // c["k"].shape[1]
+    lens = c["lens"][b:b + 1] if n is None else np.array([n], np.int32)
+    if c["q"].ndim == 4:        # a verify chunk [B, T, Hq, D]
+        return oracle.chunk_attention(c["q"][b:b + 1, :, kv0 * G:kv1 * G], k, v, lens, c["scale"])
+    return oracle.decode_attention(c["q"][b:b + 1, kv0 * G:kv1 * G], k, v, lens, c["scale"])
+
+
+def _limit_blas_threads():
     from threadpoolctl import threadpool_limits
-    w = c4["workload"]
-    kvb = rf.kv_bytes_decode(c4["lens"], w.Hkv, w.D, w.S_max)
+    threadpool_limits(1)
 
-    def timed(threads):
-        times = []
-        with threadpool_limits(threads):
-            while len(times) < 3 or (sum(times) < budget_s and len(times) < 200):
-                t = time.perf_counter()
-                oracle.decode_attention(c4["q"], c4["k"], c4["v"], c4["lens"], c4["scale"])
-                times.append(time.perf_counter() - t)
-        return float(np.median(times)), len(times), sum(times)
 
-    med, runs, total = timed(1)
-    log(f"cpu oracle: {med:.2f} s per call ({kvb / med / 1e9:.3f} GB/s), {runs} runs")
-    ncores = len(os.sched_getaffinity(0))
-    med_all, runs_all, total_all = timed(ncores)
-    log(f"cpu oracle, {ncores} cores: {med_all:.2f} s per call ({kvb / med_all / 1e9:.3f} GB/s), {runs_all} runs")
-    return {"value": round(kvb / med / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"the whole headline call (all {w.B * w.Hq} query rows, {kvb} KV bytes), fp64 NumPy, "
-                      f"BLAS limited to 1 thread; median of {runs} runs ({total:.1f} s of CPU work) of {med:.3f} s",
-            "all_cores": {"value": round(kvb / med_all / 1e9, 4), "unit": "GB/s", "cores": ncores,
-                          "sample": f"the same call with BLAS allowed {ncores} threads; median of {runs_all} runs "
-                                    f"({total_all:.1f} s) of {med_all:.3f} s"}}
+def _timed_runs(fn, budget_s, min_runs=3, max_runs=200):
+    """Median, p10, p90 seconds of fn() over at least min_runs runs and about
+    budget_s seconds, and the number of runs."""
+    import numpy as np
+    times = []
+    while len(times) < min_runs or (sum(times) < budget_s and len(times) < max_runs):
+        t = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t)
+    return (float(np.median(times)), float(np.percentile(times, 10)), float(np.percentile(times, 90)),
+            len(times))
+
+
+def cpu_oracle_runs(inputs, rf, budget_s=1.5):
+    """The oracle on every workload, one BLAS thread in one process, then the
+    same slices over a pool of worker processes (one BLAS thread each). Returns
+    {key: entry}; the keys name the workload (and length)."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    plans = []      # (key, tasks, unit calls, kv bytes per unit, description)
+    for cfg, cs in inputs.items():
+        w = cs[0]["workload"]
+        _ORACLE_INPUTS[w.name] = cs
+        if cfg in (2, 3):
+            for n in w.lens:
+                tasks = [(w.name, l, 0, 0, w.Hkv, n) for l in range(len(cs))]
+                kvb = rf.kv_bytes_decode([n], w.Hkv, w.D, w.S_max) * len(cs)
+                plans.append((f"{w.name}@{n}", tasks, len(cs), kvb,
+                              f"a whole step: {len(cs)} layer calls at n = {n}, one task per layer"))
+        elif cfg == 5:
+            tasks = [(w.name, 0, 0, h, h + 1, None) for h in range(w.Hkv)]
+            kvb = rf.kv_bytes_chunk(cs[0]["lens"], w.T, w.Hkv, w.D, w.S_max)
+            plans.append((w.name, tasks, 1, kvb, f"the whole call, one task per kv head ({w.Hkv})"))
+        else:
+            tasks = [(w.name, 0, b, h, h + 1, None) for b in range(w.B) for h in range(w.Hkv)]
+            kvb = rf.kv_bytes_decode(cs[0]["lens"], w.Hkv, w.D, w.S_max)
+            plans.append((w.name, tasks, 1, kvb, f"the whole call, one task per (sequence, kv head) "
+                                                  f"({len(tasks)})"))
+    res = {}
+    with threadpool_limits(1):
+        for key, tasks, calls, kvb, desc in plans:
+            budget = budget_s * (3 if key.startswith("llama3-8b") else 1)
+            med, p10, p90, runs = _timed_runs(lambda: [_oracle_slice(t) for t in tasks], budget)
+            res[key] = {"kind": "oracle", "cores": 1, "sample": desc, "runs": runs,
+                        "s_per_unit": {"median": med, "p10": p10, "p90": p90},
+                        "us_per_call": round(med / calls * 1e6, 1), "GBps": round(kvb / med / 1e9, 4)}
+            log(f"cpu oracle {key}, 1 core: {med * 1e3:.1f} ms ({kvb / med / 1e9:.3f} GB/s), {runs} runs")
+    workers = min(16, len(os.sched_getaffinity(0)))
+    with ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("fork"),
+                             initializer=_limit_blas_threads) as pool:
+        list(pool.map(abs, range(4 * workers)))          # fork every worker before timing
+        for key, tasks, calls, kvb, desc in plans:
+            budget = budget_s * (3 if key.startswith("llama3-8b") else 1)
+            med, p10, p90, runs = _timed_runs(lambda: list(pool.map(_oracle_slice, tasks)), budget)
+            res[key]["all_cores"] = {"cores": workers, "runs": runs,
+                                     "s_per_unit": {"median": med, "p10": p10, "p90": p90},
+                                     "us_per_call": round(med / calls * 1e6, 1),
+                                     "GBps": round(kvb / med / 1e9, 4),
+                                     "sample": f"the same tasks over {workers} worker processes, "
+                                               f"one BLAS thread each"}
+            log(f"cpu oracle {key}, {workers} processes: {med * 1e3:.1f} ms ({kvb / med / 1e9:.3f} GB/s)")
+    _ORACLE_INPUTS.clear()
+    return res
 
 
 if __name__ == "__main__":

@@ -9,9 +9,9 @@ the INT8 section):
   * a decode step multiplies each activation vector by every weight matrix;
     weights are row-major [out][in], each read once per step, so the product
     is bound by the bytes read;
-  * INT8 weight-only: each weight row is stored as INT8 with one fp32 scale,
-    symmetric, per output channel, quantized when the weights are loaded; the
-    product dequantizes in registers;
+  * INT8 weight-only: the codes are symmetric and scaled per output row (one
+    fp32 factor per row), computed once at load time, and widened back to
+    real values inside the product;
   * a batch of sequences reads the weights once per step.
 
 Readings taken where the pages are silent (restated where used):

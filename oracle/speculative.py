@@ -5,11 +5,11 @@ TEST INFRASTRUCTURE ONLY (see the package docstring): plain NumPy, sharing
 nothing with the HIP library.
 
 What the pages fix:
-  * a draft token is kept with probability min(1, p_t / p_d); the extra token
-    of the step comes from the residual (p_t - p_d)+ at the first rejection,
-    or from the target's bonus row when every draft was kept; at temperature
-    0 the rule becomes "keep drafts while they equal the target's argmax"
-    (tinydecode README, "speculative decoding");
+  * each draft survives with probability min(1, p_t / p_d); at the first
+    one that does not, the step's extra token is drawn from the positive part
+    of p_t - p_d, and when all survive, from the target's last (bonus) row;
+    with temperature 0 the survivors are the leading drafts that match the
+    target's argmax (tinydecode README, "speculative decoding");
   * the test is u_i < min(1, p(x_i) / q(x_i)), evaluated in log space, and a
     rejected position draws its token from max(0, p - q) normalised to sum 1
     (Leviathan et al. 2023, Algorithm 1, as the FlashSpec page restates it in

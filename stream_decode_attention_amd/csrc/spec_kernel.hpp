@@ -1,10 +1,12 @@
 // Speculative decoding's accept/reject step with the rollback of the cache
-// lengths, on the device (tinydecode README, "speculative decoding": keep a
-// draft with probability min(1, p_t / p_d), take the extra token from the
-// residual (p_t - p_d)+ at the first rejection or from the bonus row, greedy
-// keeps drafts while they equal the argmax, rollback only moves the length;
-// FlashSpec page, correctness paragraph: Leviathan et al. 2023, Algorithm 1,
-// the test taken in log space).
+// lengths, on the device. The rule (tinydecode README, "speculative
+// decoding"; FlashSpec page, correctness paragraph, after Leviathan et al.
+// 2023, Algorithm 1): a draft survives when a uniform falls under the ratio of
+// target to draft probability (compared here as logarithms); at the first
+// draft that fails, the step's extra token is sampled from the positive part
+// of target minus draft, and when all survive, from the target's last row; at
+// temperature 0 the survivors are the drafts that match the target's argmax;
+// rolling back is only a change of the length.
 //
 // Launches (no host sync):
 //   spec_stats_kernel   one workgroup per (row b, position i, vocabulary
