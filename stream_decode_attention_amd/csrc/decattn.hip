@@ -172,14 +172,25 @@ int resident_blocks(const void* kernel, int threads, size_t lds) {
 
 template <int D, int R>
 hipError_t launch_partial_dr(const Plan& pl, const PartialParams& pp, hipStream_t s) {
-    // persistent: one wave of resident workgroups walks all attended tiles
     const int threads = 64 * pl.nwk * pl.rg_per_block;
-    const void* fn = reinterpret_cast<const void*>(&split_kv_partial<D, R>);
+    const long long items = (long long)pl.B * pl.Hkv * pl.n_row_blocks * pl.NC;   // every possible tile
+    // one workgroup per possible work item when they all fit on the device at
+    // once: each knows its tile from its index and requests its K/V before the
+    // length arrives (tiles past the length exit); measured 0.6-0.7 us faster
+    // per call than the persistent walk on the single-sequence decode layers
+    const void* fn1 = reinterpret_cast<const void*>(&split_kv_partial<D, R, true>);
+    const long long res1 = resident_blocks(fn1, threads, pl.lds_bytes);
+    if (res1 <= 0) return hipErrorInvalidDeviceFunction;
+    if (items <= res1) {
+        hipLaunchKernelGGL((split_kv_partial<D, R, true>), dim3((unsigned)items), dim3(threads), pl.lds_bytes, s, pp);
+        return hipGetLastError();
+    }
+    // persistent: one wave of resident workgroups walks all attended tiles
+    const void* fn = reinterpret_cast<const void*>(&split_kv_partial<D, R, false>);
     long long grid = resident_blocks(fn, threads, pl.lds_bytes);
     if (grid <= 0) return hipErrorInvalidDeviceFunction;
-    const long long items = (long long)pl.B * pl.Hkv * pl.n_row_blocks * pl.NC;   // upper bound
     if (grid > items) grid = items;
-    hipLaunchKernelGGL((split_kv_partial<D, R>), dim3((unsigned)grid), dim3(threads), pl.lds_bytes, s, pp);
+    hipLaunchKernelGGL((split_kv_partial<D, R, false>), dim3((unsigned)grid), dim3(threads), pl.lds_bytes, s, pp);
     return hipGetLastError();
 }
 

@@ -32,6 +32,13 @@
 //    t0 + (s*NWK + w)*KPW ...); their states are combined once through LDS.
 //  * Waves of the same workgroup may hold different row groups (the verify
 //    chunk has T*G rows per kv head); all row groups share the tile's K/V.
+//  * Work distribution, two modes. Persistent: a grid of the resident
+//    workgroups stages the lengths, counts the attended tiles and walks them
+//    (tiles past a length are never scheduled; a workgroup may take several,
+//    with the next item's loads in flight while one is finished). One round
+//    (ONE_ROUND, when every possible tile up to S_max fits on the device at
+//    once): one workgroup per possible tile, which issues its query and K/V
+//    loads before its length arrives and exits if the tile lies past it.
 //
 // Every row is computed with the same sequence of floating-point operations
 // whatever R is and whatever other rows share its wave (the butterfly pairs
@@ -149,7 +156,13 @@ __device__ __forceinline__ void gather_all_i(int x, int (&out)[8]) {
     }
 }
 
-template <int D, int R>
+// ONE_ROUND: every possible work item has a workgroup of its own (the host
+// launches one per (b, kv head, row block, tile) when they all fit on the
+// device at once), so a workgroup knows its tile from its index alone and
+// issues its query and first K/V loads before the length arrives; keys past
+// the length are then masked by select (scores to -inf, V to 0), never by a
+// multiply, since stale slots may hold any bits.
+template <int D, int R, bool ONE_ROUND>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(DECATTN_WAVES_PER_EU)))
 split_kv_partial(const PartialParams p) {
     constexpr int LPK = D / 8;              // lanes per key row
@@ -179,20 +192,23 @@ split_kv_partial(const PartialParams p) {
     float* s_acc = smem;                                    // [rgb][nwk][R][D]
     float* s_ml = smem + (size_t)p.rg_per_block * p.nwk * R * D;   // [rgb][nwk][R][2]
     int* s_len = reinterpret_cast<int*>(s_ml + (size_t)p.rg_per_block * p.nwk * R * 2);   // [B]
-    int my_tiles = 0;
-    for (int i = tid; i < p.B; i += blockDim.x) {
-        const int len = p.lens[i];
-        s_len[i] = len;
-        const int lim = clamp_len_add(len, p.causal ? p.T : 0, p.S_max);
-        my_tiles += (lim + p.chunk - 1) / p.chunk;
-    }
-    for (int o = 32; o > 0; o >>= 1) my_tiles += __shfl_xor(my_tiles, o);
-    if (lane == 0) s_count[wave] = my_tiles;
-    __syncthreads();
-    int n_tiles = 0;
-    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) n_tiles += s_count[w];
     const int per_tile = p.Hkv * p.n_row_blocks;            // work items per (b, tile)
-    const int n_items = n_tiles * per_tile;
+    int n_items = 0;
+    if constexpr (!ONE_ROUND) {
+        int my_tiles = 0;
+        for (int i = tid; i < p.B; i += blockDim.x) {
+            const int len = p.lens[i];
+            s_len[i] = len;
+            const int lim = clamp_len_add(len, p.causal ? p.T : 0, p.S_max);
+            my_tiles += (lim + p.chunk - 1) / p.chunk;
+        }
+        for (int o = 32; o > 0; o >>= 1) my_tiles += __shfl_xor(my_tiles, o);
+        if (lane == 0) s_count[wave] = my_tiles;
+        __syncthreads();
+        int n_tiles = 0;
+        for (int w = 0; w < (int)(blockDim.x >> 6); ++w) n_tiles += s_count[w];
+        n_items = n_tiles * per_tile;
+    }
 
     // Work item t enumerates (b, kvh, row block, tile c) over attended tiles
     // only, b-major; workgroup w takes items w, w + P, w + 2P, ... (P = grid),
@@ -278,7 +294,7 @@ split_kv_partial(const PartialParams p) {
     float acc[RP][8];                       // slot k, this lane's 8 dims
 
     auto compute = [&](const uint4 (&qraw)[RP], int my_lim, const uint4 (&kb)[NSTEP],
-                       const uint4 (&vb)[NSTEP], int base) {
+                       const uint4 (&vb)[NSTEP], int base, int v_lim) {
         // own-row scores in log2 units, -inf past the row's limit
         float dm[NSTEP];
 #pragma unroll
@@ -322,6 +338,11 @@ split_kv_partial(const PartialParams p) {
             gather_all<LPK, RP>(pj, ps);
             float vf[8];
             bf16x8_to_f32(vb[st], vf);
+            if (base + kKeysPerWave > v_lim) {     // wave-uniform: keys past v_lim were loaded
+                const bool in = base + st * KPL + kk < v_lim;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) vf[e] = in ? vf[e] : 0.f;
+            }
 #pragma unroll
             for (int k = 0; k < RP; ++k)
 #pragma unroll
@@ -421,6 +442,62 @@ split_kv_partial(const PartialParams p) {
     // has at least kNumBuf slots, the load pointer is at most one item ahead
     // (one spare set of query registers), and every item ends at the end of a
     // ring cycle, where it is combined.
+    if constexpr (ONE_ROUND) {
+        // Work item blockIdx.x = (((b * Hkv + kvh) * n_row_blocks + rblk) * NC + c).
+        Tile tl;
+        {
+            int t = blockIdx.x;
+            tl.c = t % p.NC;
+            t /= p.NC;
+            tl.rblk = t % p.n_row_blocks;
+            t /= p.n_row_blocks;
+            tl.kvh = t % p.Hkv;
+            tl.b = t / p.Hkv;
+        }
+        tl.t0 = tl.c * p.chunk;
+        tl.t1 = min(tl.t0 + p.chunk, p.S_max);
+        const int len = p.lens[tl.b];       // issued first; waited for only below
+        const int spt_real = (p.chunk + sub_stride - 1) / sub_stride;
+        const int spt = (spt_real + kNumBuf - 1) / kNumBuf * kNumBuf;
+        uint4 qc[RP];
+        int limc;
+        tl.len = 0;
+        tl.lim_all = tl.t1;
+        load_q(tl, qc, limc);               // the limit is recomputed once the length is known
+        // the first kNumBuf sub-tiles are requested over the whole tile (keys
+        // up to t1 all lie inside the cache); later ones only up to the
+        // attended keys
+        Rsrc rs = make_tile_rsrc(tl);
+        uint4 kb[kNumBuf][NSTEP], vb[kNumBuf][NSTEP];
+        auto slot_base = [&](int s, int lim) {
+            return min(s < spt_real ? tl.t0 + kw * kKeysPerWave + s * sub_stride : lim, lim);
+        };
+#pragma unroll
+        for (int u = 0; u < kNumBuf; ++u) load(rs, kb[u], vb[u], slot_base(u, tl.t1));
+
+        tl.len = len;
+        tl.lim_all = min(clamp_len_add(len, p.causal ? p.T : 0, p.S_max), tl.t1);
+        if (tl.t0 >= tl.lim_all) return;    // workgroup-uniform: a tile past the length
+        {
+            const int rg = tl.rblk * p.rg_per_block + rgl;
+            const int r0 = rg * R + own;
+            const int i = (r0 < p.RT ? r0 : 0) / p.G;
+            limc = (own < R && r0 < p.RT) ? min(clamp_len_add(len, p.causal ? i + 1 : 0, p.S_max), tl.t1) : 0;
+        }
+        rs = make_tile_rsrc(tl);
+        reset_state();
+        for (int s0 = 0; s0 < spt; s0 += kNumBuf) {
+#pragma unroll
+            for (int u = 0; u < kNumBuf; ++u) {
+                const int base = tl.t0 + kw * kKeysPerWave + (s0 + u) * sub_stride;
+                if (s0 + u < spt_real && base < tl.lim_all) compute(qc, limc, kb[u], vb[u], base, tl.lim_all);
+                if (s0 + u + kNumBuf < spt) load(rs, kb[u], vb[u], slot_base(s0 + u + kNumBuf, tl.lim_all));
+            }
+        }
+        finish(tl);
+        return;
+    }
+
     int c_item = blockIdx.x;
     if (c_item >= n_items) return;          // workgroup-uniform
     const int P = (int)gridDim.x;
@@ -467,7 +544,7 @@ split_kv_partial(const PartialParams p) {
                 issue(kb[nu], vb[nu]);
                 if (DECATTN_PREFETCH_FENCE) __builtin_amdgcn_sched_barrier(0);
                 const int base = ct.t0 + kw * kKeysPerWave + (s0 + u) * sub_stride;
-                if (s0 + u < spt_real && base < ct.lim_all) compute(qc, limc, kb[u], vb[u], base);
+                if (s0 + u < spt_real && base < ct.lim_all) compute(qc, limc, kb[u], vb[u], base, 0x7FFFFFFF);
             }
         }
         finish(ct);
