@@ -124,6 +124,75 @@ def test_matrix_core_context_just_past_a_tile_boundary(chunk):
     assert_bf16_close(run_chunk(c, chunk=chunk, out_dtype=torch.bfloat16), ref)
 
 
+# ------------------------------------- batched decode on the persistent walk
+
+# Shapes with more possible tiles than the device holds at once (the
+# persistent tile walk): rows far shorter than a tile next to full ones, many
+# sequences of random lengths, rows ending off tile boundaries.
+
+@pytest.mark.parametrize("B,Hkv,G,D,S,lens", [
+    # short rows (0, 1, 15, 17 keys) next to long ones
+    (8, 8, 4, 128, 8192, [0, 1, 15, 17, 300, 8192, 5000, 2]),
+    # 64 sequences of random lengths, every fifth under 40 keys
+    (64, 2, 3, 64, 4096, None),
+    # long rows ending off tile boundaries
+    (4, 8, 4, 128, 32768, [30001, 29999, 32768, 31000]),
+])
+def test_persistent_walk_ragged_batches_vs_oracle(B, Hkv, G, D, S, lens):
+    if lens is None:
+        lens = np.random.default_rng(71).integers(0, S + 1, size=B)
+        lens[::5] = np.random.default_rng(72).integers(0, 40, size=len(lens[::5]))
+    c = workloads.make_case(B, G * Hkv, Hkv, D, S, lens, seed=70 + B)
+    ref = oracle.decode_attention(c["q"], c["k"], c["v"], c["lens"], c["scale"])
+    tensors = (dev_bits(c["q"]), dev_bits(c["k"]), dev_bits(c["v"]))
+    assert_f32_close(run_decode(c, tensors=tensors), ref)
+    assert_bf16_close(run_decode(c, tensors=tensors, out_dtype=torch.bfloat16), ref)
+
+
+def test_persistent_walk_nan_poison_past_length_is_never_read():
+    lens = [1, 4095, 20, 2048, 0, 4096, 333, 17]
+    c = workloads.make_case(8, 32, 8, 128, 4096, lens, seed=73)
+    poisoned = dict(c, k=c["k"].copy(), v=c["v"].copy())
+    for b, n in enumerate(lens):
+        poisoned["k"][b, :, n:] = BF16_NAN
+        poisoned["v"][b, :, n:] = BF16_NAN
+    for dt in (torch.float32, torch.bfloat16):
+        a = run_decode(c, out_dtype=dt)
+        p = run_decode(poisoned, out_dtype=dt)
+        assert torch.equal(a.view(torch.int16), p.view(torch.int16))
+        assert not torch.isnan(p.float()).any()
+
+
+def test_persistent_walk_graph_replay_follows_device_lengths():
+    """The attended-tile list depends on the lengths, which change on the
+    device between replays of one captured call."""
+    c = workloads.make_case(8, 32, 8, 128, 8192, [8192] * 8, seed=74)
+    q, k, v = dev_bits(c["q"]), dev_bits(c["k"]), dev_bits(c["v"])
+    lens = dev_lens([8192] * 8)
+    ws = workspace(8, 1, 32, 8, 128, 8192, 0, poison=True)
+    out = torch.zeros((8, 32, 128), device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        sda.decode_attn(q, k, v, lens, c["scale"], out, ws)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sda.decode_attn(q, k, v, lens, c["scale"], out, ws)
+    rng = np.random.default_rng(75)
+    for trial in range(4):
+        n = rng.integers(0, 8193, size=8).astype(np.int32)
+        if trial == 3:
+            n[:] = 0
+        lens.copy_(torch.from_numpy(n))
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        ref = oracle.decode_attention(c["q"], c["k"], c["v"], n, c["scale"])
+        assert_f32_close(got, ref)
+        assert torch.equal(got, run_decode(c, lens=n, tensors=(q, k, v))), f"replay {trial} differs from eager"
+
+
 # ------------------------------------------------------------- size extremes
 
 def test_row_with_more_tiles_than_one_merge_batch():
