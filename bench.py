@@ -156,6 +156,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true")
     ap.add_argument("--chunk", type=int, default=0, help="override the library's default tile size")
+    ap.add_argument("--only", type=int, default=0, choices=[0, 1, 2, 3, 5],
+                    help="profiling: run only this workload's timing (no headline line)")
+    ap.add_argument("--lengths", type=str, default="",
+                    help="profiling: comma-separated lengths for workloads 2 and 3 instead of the listed ones")
+    ap.add_argument("--no-floor", action="store_true",
+                    help="profiling: skip the every-length-0 graphs, so every launch has the chosen lengths")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the decode-attention kernels run on a single device and "
@@ -172,11 +178,10 @@ def main():
     # ---------------------------------------------- inputs, then the CPU oracle
     # (before anything touches the GPU: the oracle's worker processes fork)
     t = time.time()
+    cfgs = (args.only,) if args.only else (4,) if args.headline_only else (1, 2, 3, 4, 5)
     inputs = {cfg: [workloads.make_config(cfg, layer=l) for l in range(workloads.CONFIGS[cfg].layers)]
-              for cfg in ((4,) if args.headline_only else (1, 2, 3, 4, 5))}
-    c4 = inputs[4][0]
-    w4 = c4["workload"]
-    log(f"inputs generated in {time.time() - t:.1f}s, workload 4 lens {c4['lens'].tolist()}")
+              for cfg in cfgs}
+    log(f"inputs generated in {time.time() - t:.1f}s")
     cpu = None if args.no_cpu_baseline else cpu_oracle_runs(inputs, rf)
 
     sda.load_library()
@@ -217,7 +222,16 @@ def main():
     def flush():
         sda.probe_read(flush_buf, sink, stream=stream)
 
+    if args.only:
+        # profiling run: one workload's graphs, printed as a JSON list
+        res = other_workloads(args, dev, up, sda, workloads, rf, np, torch, stream, flush, inputs)
+        print(json.dumps(res), flush=True)
+        return
+
     # ------------------------------------------------------ headline: workload 4
+    c4 = inputs[4][0]
+    w4 = c4["workload"]
+    log(f"workload 4 lens {c4['lens'].tolist()}")
     q = up(c4["q"])
     ks = [up(c4["k"])]
     vs = [up(c4["v"])]
@@ -654,8 +668,29 @@ def other_workloads(args, dev, up, sda, workloads, rf, np, torch, stream, flush,
     back-to-back replays: median, p10 and p90 of the per-replay times."""
     res = []
     steps = max(50, args.steps)
+    run = lambda cfg: not args.only or args.only == cfg
 
     # workload 1: one small call, 16 calls per graph, latency only
+    if run(1):
+        res.append(workload1(args, dev, up, sda, rf, torch, stream, flush, inputs, steps))
+
+    # workloads 2 and 3: a graph of L independent layer calls per step, replayed
+    # with the device-resident length rewritten; three cache sets rotate.
+    # Workload 2 at its longest length also runs with one tile per row (chunk =
+    # S_max), the pages' baseline for split-KV.
+    for cfg in (2, 3):
+        if run(cfg):
+            res.extend(decode_layers(args, cfg, dev, up, sda, workloads, rf, np, torch, stream, flush, inputs, steps))
+
+    # workload 5: verify chunk, eight calls per graph on eight cache copies
+    if run(5):
+        res.append(verify_chunk(args, dev, up, sda, workloads, rf, np, torch, stream, flush, inputs, steps))
+    return res
+
+
+def workload1(args, dev, up, sda, rf, torch, stream, flush, inputs, steps):
+    """Workload 1: the single small call, 16 per graph."""
+    res = []
     c = inputs[1][0]
     w = c["workload"]
     q, k, v = up(c["q"]), up(c["k"]), up(c["v"])
@@ -669,82 +704,90 @@ def other_workloads(args, dev, up, sda, workloads, rf, np, torch, stream, flush,
                 "us_per_call_dist": d, "kv_bytes_per_call": rf.kv_bytes_decode([64], w.Hkv, w.D, w.S_max)})
     log(f"workload 1: {d['median']:.2f} us/call (p10 {d['p10']:.2f}, p90 {d['p90']:.2f})")
     del g1
+    return res[0]
 
-    # workloads 2 and 3: a graph of L independent layer calls per step, replayed
-    # with the device-resident length rewritten; three cache sets rotate.
-    # Workload 2 at its longest length also runs with one tile per row (chunk =
-    # S_max), the pages' baseline for split-KV.
-    for cfg in (2, 3):
-        w = workloads.CONFIGS[cfg]
-        layers = inputs[cfg]
-        lens = torch.zeros(1, dtype=torch.int32, device=dev)
-        sets = []
-        for si in range(3):
-            tens = []
-            for l, cl in enumerate(layers):
-                kq = up(cl["q"])
-                kk = up(cl["k"]) if si == 0 else sets[0][l][1].clone()
-                vv = up(cl["v"]) if si == 0 else sets[0][l][2].clone()
-                o = torch.empty((1, w.Hq, w.D), dtype=torch.bfloat16, device=dev)
-                tens.append((kq, kk, vv, o))
-            sets.append(tens)
-        scale = layers[0]["scale"]
-        chunk = sda.default_chunk(1, 1, w.Hq, w.Hkv, w.D, w.S_max)
 
-        def make_graphs(ch):
-            wsl = [torch.empty(sda.workspace_bytes(1, 1, w.Hq, w.Hkv, w.D, w.S_max, ch), dtype=torch.uint8,
-                               device=dev) for _ in layers]
+def decode_layers(args, cfg, dev, up, sda, workloads, rf, np, torch, stream, flush, inputs, steps):
+    """Workloads 2 and 3: graphs of a step's layer calls at each length."""
+    res = []
+    w = workloads.CONFIGS[cfg]
+    lengths = [int(x) for x in args.lengths.split(",")] if args.lengths else list(w.lens)
+    layers = inputs[cfg]
+    lens = torch.zeros(1, dtype=torch.int32, device=dev)
+    sets = []
+    for si in range(3):
+        tens = []
+        for l, cl in enumerate(layers):
+            kq = up(cl["q"])
+            kk = up(cl["k"]) if si == 0 else sets[0][l][1].clone()
+            vv = up(cl["v"]) if si == 0 else sets[0][l][2].clone()
+            o = torch.empty((1, w.Hq, w.D), dtype=torch.bfloat16, device=dev)
+            tens.append((kq, kk, vv, o))
+        sets.append(tens)
+    scale = layers[0]["scale"]
+    chunk = sda.default_chunk(1, 1, w.Hq, w.Hkv, w.D, w.S_max)
 
-            def step_fns(tens):
-                return [lambda t=t, wl=wl: sda.decode_attn(t[0], t[1], t[2], lens, scale, t[3], wl, ch,
-                                                           stream=stream)
-                        for t, wl in zip(tens, wsl)]
-            lens.fill_(max(w.lens))
-            torch.cuda.synchronize()
-            with torch.cuda.stream(stream):
-                for tens in sets:
-                    for fn in step_fns(tens):
-                        fn()
-                stream.synchronize()
-            return [graph_of(torch, stream, step_fns(tens)) for tens in sets], wsl
+    def make_graphs(ch):
+        wsl = [torch.empty(sda.workspace_bytes(1, 1, w.Hq, w.Hkv, w.D, w.S_max, ch), dtype=torch.uint8,
+                           device=dev) for _ in layers]
 
-        graphs, _wsl = make_graphs(chunk)
+        def step_fns(tens):
+            return [lambda t=t, wl=wl: sda.decode_attn(t[0], t[1], t[2], lens, scale, t[3], wl, ch,
+                                                       stream=stream)
+                    for t, wl in zip(tens, wsl)]
+        lens.fill_(max(lengths))
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            for tens in sets:
+                for fn in step_fns(tens):
+                    fn()
+            stream.synchronize()
+        return [graph_of(torch, stream, step_fns(tens)) for tens in sets], wsl
+
+    graphs, _wsl = make_graphs(chunk)
+    floor = {"median": None, "p10": None, "p90": None}
+    if not args.no_floor:
         lens.fill_(0)
         torch.cuda.synchronize()
         floor = dist(replay_dist_us(torch, stream, graphs, steps, args.warmup, busy=flush))
-        for n in w.lens:
-            lens.fill_(n)
-            torch.cuda.synchronize()
-            d = dist(replay_dist_us(torch, stream, graphs, steps, args.warmup, busy=flush))
-            us = d["median"]
-            kvb = rf.kv_bytes_decode([n], w.Hkv, w.D, w.S_max) * w.layers
-            res.append({"workload": w.name, "n": n, "chunk": chunk, "calls_per_step": w.layers,
-                        "us_per_step": us, "us_per_step_dist": d, "us_per_call": round(us / w.layers, 3),
-                        "launch_floor_us_per_step": floor["median"], "launch_floor_us_per_step_dist": floor,
-                        "kv_bytes_per_step": kvb, "GBps": round(kvb / (us / 1e6) / 1e9, 1),
-                        "frac_of_hbm_peak": round(kvb / (us / 1e6) / 1e9 / rf.HBM_PEAK_GBPS, 4)})
-            log(f"workload {cfg} n={n}: {us:.1f} us/step ({us / w.layers:.2f} us/call, p10 {d['p10']:.1f}, "
-                f"p90 {d['p90']:.1f}), {res[-1]['GBps']:.0f} GB/s (floor {floor['median']:.1f} us/step)")
-        del graphs, _wsl
-        if cfg == 2:
-            n = max(w.lens)
-            graphs, _wsl = make_graphs(w.S_max)
-            lens.fill_(n)
-            torch.cuda.synchronize()
-            d = dist(replay_dist_us(torch, stream, graphs, steps, args.warmup, busy=flush))
-            kvb = rf.kv_bytes_decode([n], w.Hkv, w.D, w.S_max) * w.layers
-            res[-1]["one_tile_ablation"] = {
-                "what": "the same step with chunk = S_max: one tile (one workgroup) per kv head",
-                "chunk": w.S_max, "us_per_step": d["median"], "us_per_step_dist": d,
-                "us_per_call": round(d["median"] / w.layers, 3), "GBps": round(kvb / (d["median"] / 1e6) / 1e9, 1),
-                "split_kv_speedup": round(d["median"] / res[-1]["us_per_step"], 2)}
-            log(f"workload 2 n={n}, one tile per row: {d['median'] / w.layers:.2f} us/call "
-                f"({res[-1]['one_tile_ablation']['split_kv_speedup']:.2f}x the split-KV time)")
-            del graphs, _wsl
+    for n in lengths:
+        lens.fill_(n)
         torch.cuda.synchronize()
-        del sets
+        d = dist(replay_dist_us(torch, stream, graphs, steps, args.warmup, busy=flush))
+        us = d["median"]
+        kvb = rf.kv_bytes_decode([n], w.Hkv, w.D, w.S_max) * w.layers
+        res.append({"workload": w.name, "n": n, "chunk": chunk, "calls_per_step": w.layers,
+                    "us_per_step": us, "us_per_step_dist": d, "us_per_call": round(us / w.layers, 3),
+                    "launch_floor_us_per_step": floor["median"], "launch_floor_us_per_step_dist": floor,
+                    "kv_bytes_per_step": kvb, "GBps": round(kvb / (us / 1e6) / 1e9, 1),
+                    "frac_of_hbm_peak": round(kvb / (us / 1e6) / 1e9 / rf.HBM_PEAK_GBPS, 4)})
+        log(f"workload {cfg} n={n}: {us:.1f} us/step ({us / w.layers:.2f} us/call, p10 {d['p10']:.1f}, "
+            f"p90 {d['p90']:.1f}), {res[-1]['GBps']:.0f} GB/s (floor {floor['median']} us/step)")
+    del graphs, _wsl
+    if cfg == 2 and not args.lengths:
+        n = max(w.lens)
+        graphs, _wsl = make_graphs(w.S_max)
+        lens.fill_(n)
+        torch.cuda.synchronize()
+        d = dist(replay_dist_us(torch, stream, graphs, steps, args.warmup, busy=flush))
+        kvb = rf.kv_bytes_decode([n], w.Hkv, w.D, w.S_max) * w.layers
+        res[-1]["one_tile_ablation"] = {
+            "what": "the same step with chunk = S_max: one tile (one workgroup) per kv head",
+            "chunk": w.S_max, "us_per_step": d["median"], "us_per_step_dist": d,
+            "us_per_call": round(d["median"] / w.layers, 3), "GBps": round(kvb / (d["median"] / 1e6) / 1e9, 1),
+            "split_kv_speedup": round(d["median"] / res[-1]["us_per_step"], 2)}
+        log(f"workload 2 n={n}, one tile per row: {d['median'] / w.layers:.2f} us/call "
+            f"({res[-1]['one_tile_ablation']['split_kv_speedup']:.2f}x the split-KV time)")
+        del graphs, _wsl
+    torch.cuda.synchronize()
+    del sets
+    return res
 
-    # workload 5: verify chunk, eight calls per graph on eight cache copies
+
+def verify_chunk(args, dev, up, sda, workloads, rf, np, torch, stream, flush, inputs, steps):
+    """Workload 5: the verify chunk, eight calls per graph on eight cache
+    copies, then the rotary/K-V write of the verify step beside it."""
+    res = []
     c = inputs[5][0]
     w = c["workload"]
     chunk = sda.default_chunk(w.B, w.T, w.Hq, w.Hkv, w.D, w.S_max)
@@ -800,7 +843,7 @@ def other_workloads(args, dev, up, sda, workloads, rf, np, torch, stream, flush,
         "calls_per_graph": 50, "us_per_call": round(t["rope"], 2), "launch_floor_us": round(t["floor"], 2),
         "bytes_per_call": nb, "GBps": round(nb / (t["rope"] / 1e6) / 1e9, 1),
         "step_us": round(t["step"], 2), "attention_alone_us": round(t["attn"], 2), "rounds_dist": t["dist"]}
-    return res
+    return res[0]
 
 
 # ------------------------------------------------------------ CPU oracle baseline

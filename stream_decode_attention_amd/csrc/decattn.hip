@@ -175,13 +175,17 @@ hipError_t launch_partial_dr(const Plan& pl, const PartialParams& pp, hipStream_
     const int threads = 64 * pl.nwk * pl.rg_per_block;
     const long long items = (long long)pl.B * pl.Hkv * pl.n_row_blocks * pl.NC;   // every possible tile
     // one workgroup per possible work item when they all fit on the device at
-    // once: each knows its tile from its index and requests its K/V before the
-    // length arrives (tiles past the length exit); measured 0.6-0.7 us faster
-    // per call than the persistent walk on the single-sequence decode layers
+    // once: each knows its tile from its index and reads only its own row's
+    // length (no staging, counting or barrier; tiles past the length exit);
+    // measured 0.6-0.7 us faster per call than the persistent walk on the
+    // single-sequence decode layers
     const void* fn1 = reinterpret_cast<const void*>(&split_kv_partial<D, R, true>);
     const long long res1 = resident_blocks(fn1, threads, pl.lds_bytes);
     if (res1 <= 0) return hipErrorInvalidDeviceFunction;
-    if (items <= res1) {
+    // (only for tiles of at most kNumBuf sub-tiles per wave, the shape it was
+    // measured on: a one-tile-per-row call on this loop ran 1.7x slower than
+    // on the persistent walk)
+    if (items <= res1 && pl.chunk <= kNumBuf * pl.nwk * kKeysPerWave) {
         hipLaunchKernelGGL((split_kv_partial<D, R, true>), dim3((unsigned)items), dim3(threads), pl.lds_bytes, s, pp);
         return hipGetLastError();
     }
