@@ -156,8 +156,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true")
     ap.add_argument("--chunk", type=int, default=0, help="override the library's default tile size")
-    ap.add_argument("--only", type=int, default=0, choices=[0, 1, 2, 3, 5],
-                    help="profiling: run only this workload's timing (no headline line)")
+    ap.add_argument("--only", type=str, default="", choices=["", "1", "2", "3", "5", "gemv", "prefill", "spec"],
+                    help="profiling: run only this workload's (or step's) timing (no headline line)")
     ap.add_argument("--lengths", type=str, default="",
                     help="profiling: comma-separated lengths for workloads 2 and 3 instead of the listed ones")
     ap.add_argument("--no-floor", action="store_true",
@@ -178,7 +178,8 @@ def main():
     # ---------------------------------------------- inputs, then the CPU oracle
     # (before anything touches the GPU: the oracle's worker processes fork)
     t = time.time()
-    cfgs = (args.only,) if args.only else (4,) if args.headline_only else (1, 2, 3, 4, 5)
+    wl = int(args.only) if args.only.isdigit() else 0
+    cfgs = (wl,) if wl else () if args.only else (4,) if args.headline_only else (1, 2, 3, 4, 5)
     inputs = {cfg: [workloads.make_config(cfg, layer=l) for l in range(workloads.CONFIGS[cfg].layers)]
               for cfg in cfgs}
     log(f"inputs generated in {time.time() - t:.1f}s")
@@ -223,8 +224,15 @@ def main():
         sda.probe_read(flush_buf, sink, stream=stream)
 
     if args.only:
-        # profiling run: one workload's graphs, printed as a JSON list
-        res = other_workloads(args, dev, up, sda, workloads, rf, np, torch, stream, flush, inputs)
+        # profiling run: one workload's (or step's) graphs, printed as JSON
+        if wl:
+            res = other_workloads(args, dev, up, sda, workloads, rf, np, torch, stream, flush, inputs)
+        elif args.only == "gemv":
+            res = gemv_runs(sda, np, torch, stream, flush)
+        elif args.only == "prefill":
+            res = prefill_runs(up, sda, workloads, np, torch, stream, flush)
+        else:
+            res = spec_runs(sda, workloads, np, torch, stream, flush)
         print(json.dumps(res), flush=True)
         return
 
@@ -668,7 +676,7 @@ def other_workloads(args, dev, up, sda, workloads, rf, np, torch, stream, flush,
     back-to-back replays: median, p10 and p90 of the per-replay times."""
     res = []
     steps = max(50, args.steps)
-    run = lambda cfg: not args.only or args.only == cfg
+    run = lambda cfg: not args.only or args.only == str(cfg)
 
     # workload 1: one small call, 16 calls per graph, latency only
     if run(1):

@@ -58,11 +58,14 @@ __device__ __forceinline__ float gemv_group_sum(float v) {
     return v;
 }
 
-// INT8 weights: 16 codes in a uint4 -> eight packed bf16 pairs (exact)
+// INT8 weights: 16 codes in a uint4 -> eight packed bf16 pairs (exact:
+// |q| <= 127 has at most 7 significant bits). Each code is one conversion
+// reading its byte sign-extended in place (SDWA); one byte permute then keeps
+// the upper halves of the two floats, the pair's bf16 bits.
 __device__ __forceinline__ uint32_t int8x2_to_bf16x2(uint32_t w, int shift) {
     const float lo = (float)(int)(int8_t)(w >> shift);
     const float hi = (float)(int)(int8_t)(w >> (shift + 8));
-    return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);   // exact: |q| <= 127
+    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
 }
 
 // Rows each lane group works on at once, so that every activation piece read
@@ -89,6 +92,10 @@ template <int LPR, int B, bool INT8>
 __global__ void __launch_bounds__(kGemvThreads)
 gemv_kernel(const GemvParams p) {
     constexpr int RB = gemv_rows_per_group<B, INT8>();
+    // one vector: four independent accumulation chains per row (the dot
+    // products of a chunk alternate between them), so a lane's products do
+    // not wait on each other; several vectors already give several chains
+    constexpr int NCH = B == 1 ? 4 : 1;
     constexpr int U = kGemvUnroll / RB;             // chunk rounds in flight per row
     constexpr int RPW = 64 / LPR;                   // lane groups per wave
     constexpr int EPC = INT8 ? 16 : 8;              // weights per chunk
@@ -120,11 +127,13 @@ gemv_kernel(const GemvParams p) {
     for (int g = wave_id; g < groups; g += waves_total) {
         // lane group grp owns rows base + grp + RPW * r, r < RB
         const int base = g * rows_per_wave;
-        float acc[RB][B];
+        float acc[RB][B][NCH];
 #pragma unroll
         for (int r = 0; r < RB; ++r)
 #pragma unroll
-            for (int b = 0; b < B; ++b) acc[r][b] = 0.f;
+            for (int b = 0; b < B; ++b)
+#pragma unroll
+                for (int h = 0; h < NCH; ++h) acc[r][b][h] = 0.f;
 
         for (int c0 = 0; c0 < p.KCP; c0 += LPR * U) {
             uint4 w[RB][U];
@@ -152,20 +161,22 @@ gemv_kernel(const GemvParams p) {
                         const uint4 xv = *reinterpret_cast<const uint4*>(xs + b * p.xrow + c * 8);
 #pragma unroll
                         for (int r = 0; r < RB; ++r) {
+                            // the padded tail holds the next row's bf16 weights, which
+                            // may be non-finite: zeroed, not multiplied by x = 0
                             const uint4 wv = in_row ? w[r][u] : make_uint4(0, 0, 0, 0);
-                            float a = acc[r][b];
-                            a = dot2_bf16(wv.x, xv.x, a);
-                            a = dot2_bf16(wv.y, xv.y, a);
-                            a = dot2_bf16(wv.z, xv.z, a);
-                            a = dot2_bf16(wv.w, xv.w, a);
-                            acc[r][b] = a;
+                            float* a = acc[r][b];
+                            a[0] = dot2_bf16(wv.x, xv.x, a[0]);
+                            a[1 % NCH] = dot2_bf16(wv.y, xv.y, a[1 % NCH]);
+                            a[2 % NCH] = dot2_bf16(wv.z, xv.z, a[2 % NCH]);
+                            a[3 % NCH] = dot2_bf16(wv.w, xv.w, a[3 % NCH]);
                         }
                     }
                 } else {
                     uint32_t wb[RB][8];
+                    (void)in_row;   // the padded tail's codes are finite and meet x = 0 (staged as zeros)
 #pragma unroll
                     for (int r = 0; r < RB; ++r) {
-                        const uint4 wv = in_row ? w[r][u] : make_uint4(0, 0, 0, 0);
+                        const uint4 wv = w[r][u];
                         const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
@@ -179,16 +190,15 @@ gemv_kernel(const GemvParams p) {
                         const uint4 x1 = *reinterpret_cast<const uint4*>(xs + b * p.xrow + c * 16 + 8);
 #pragma unroll
                         for (int r = 0; r < RB; ++r) {
-                            float a = acc[r][b];
-                            a = dot2_bf16(wb[r][0], x0.x, a);
-                            a = dot2_bf16(wb[r][1], x0.y, a);
-                            a = dot2_bf16(wb[r][2], x0.z, a);
-                            a = dot2_bf16(wb[r][3], x0.w, a);
-                            a = dot2_bf16(wb[r][4], x1.x, a);
-                            a = dot2_bf16(wb[r][5], x1.y, a);
-                            a = dot2_bf16(wb[r][6], x1.z, a);
-                            a = dot2_bf16(wb[r][7], x1.w, a);
-                            acc[r][b] = a;
+                            float* a = acc[r][b];
+                            a[0] = dot2_bf16(wb[r][0], x0.x, a[0]);
+                            a[1 % NCH] = dot2_bf16(wb[r][1], x0.y, a[1 % NCH]);
+                            a[2 % NCH] = dot2_bf16(wb[r][2], x0.z, a[2 % NCH]);
+                            a[3 % NCH] = dot2_bf16(wb[r][3], x0.w, a[3 % NCH]);
+                            a[0] = dot2_bf16(wb[r][4], x1.x, a[0]);
+                            a[1 % NCH] = dot2_bf16(wb[r][5], x1.y, a[1 % NCH]);
+                            a[2 % NCH] = dot2_bf16(wb[r][6], x1.z, a[2 % NCH]);
+                            a[3 % NCH] = dot2_bf16(wb[r][7], x1.w, a[3 % NCH]);
                         }
                     }
                 }
@@ -197,13 +207,17 @@ gemv_kernel(const GemvParams p) {
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
 #pragma unroll
-            for (int b = 0; b < B; ++b) acc[r][b] = gemv_group_sum<LPR>(acc[r][b]);
+            for (int b = 0; b < B; ++b) {
+                float t = acc[r][b][0];
+                if constexpr (NCH == 4) t = (acc[r][b][0] + acc[r][b][1]) + (acc[r][b][2] + acc[r][b][3]);
+                acc[r][b][0] = gemv_group_sum<LPR>(t);
+            }
             const int row = base + grp + RPW * r;
             if (sub == 0 && row < p.N) {
                 const float sc = INT8 ? p.scale[row] : 1.f;
 #pragma unroll
                 for (int b = 0; b < B; ++b) {
-                    const float v = INT8 ? acc[r][b] * sc : acc[r][b];
+                    const float v = INT8 ? acc[r][b][0] * sc : acc[r][b][0];
                     const size_t o = (size_t)b * p.N + row;
                     if (p.out_bf16) reinterpret_cast<uint16_t*>(p.y)[o] = f32_to_bf16_rne(v);
                     else reinterpret_cast<float*>(p.y)[o] = v;

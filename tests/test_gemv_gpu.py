@@ -8,7 +8,8 @@ Two checks for each product:
     oracle bit for bit -- a dropped, repeated or misplaced term cannot hide;
   * N(0,1) data: |y_gpu - y| <= a worst-case fp32 bound derived from the
     kernels' summation (vector units: per lane at most 8 * ceil(K / 8 / 16)
-    roundings in its chain of dot2 steps, the 16/32/64-lane tree, the row
+    roundings in its chains of dot2 steps -- at B = 1 four chains, each a
+    quarter of that, then two more additions --, the 16/32/64-lane tree, the row
     scale; matrix cores: per wave a chain of at most ceil(K / 256) + 4
     products of 32 terms, each a few roundings, then 8 waves and the row
     scale -- fewer): (8 * ceil(K / 128) + 8) * 2^-24 * sum_k |W x|, and for bf16
