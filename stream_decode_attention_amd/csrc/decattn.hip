@@ -284,16 +284,19 @@ int run_partial(const Plan& pl, const void* q, const void* k, const void* v, con
 int run_merge(const Plan& pl, const int32_t* lens, int causal, void* out, int out_dtype, void* ws,
               hipStream_t s) {
     MergeParams mp{};
-    mp.ws_ml = static_cast<const float*>(ws);
-    mp.ws_acc = reinterpret_cast<const float*>(static_cast<const char*>(ws) + pl.ml_bytes);
-    mp.lens = lens;
+    const float* ws_ml = static_cast<const float*>(ws);
+    const float* ws_acc = reinterpret_cast<const float*>(static_cast<const char*>(ws) + pl.ml_bytes);
     mp.out = out;
     mp.out_bf16 = out_dtype == DECATTN_OUT_BF16;
-    mp.T = pl.T; mp.Hq = pl.Hq; mp.Hkv = pl.Hkv; mp.G = pl.G; mp.S_max = pl.S_max;
-    mp.chunk = pl.chunk; mp.NC = pl.NC; mp.RT = pl.RT; mp.causal = causal;
+    mp.T = pl.T; mp.S_max = pl.S_max; mp.chunk = pl.chunk; mp.causal = causal;
     const dim3 grid(pl.B * pl.T * pl.Hq);
-    if (pl.D == 64) hipLaunchKernelGGL(lse_merge<64>, grid, dim3(kMergeThreads), 0, s, mp);
-    else hipLaunchKernelGGL(lse_merge<128>, grid, dim3(kMergeThreads), 0, s, mp);
+    const int thq = pl.T * pl.Hq;
+    if (pl.D == 64)
+        hipLaunchKernelGGL(lse_merge<64>, grid, dim3(kMergeThreads), 0, s, ws_ml, ws_acc, lens, thq, pl.Hq, pl.G,
+                           pl.Hkv, pl.NC, pl.RT, mp);
+    else
+        hipLaunchKernelGGL(lse_merge<128>, grid, dim3(kMergeThreads), 0, s, ws_ml, ws_acc, lens, thq, pl.Hq, pl.G,
+                           pl.Hkv, pl.NC, pl.RT, mp);
     return hipGetLastError() == hipSuccess ? DECATTN_OK : DECATTN_ERR_HIP;
 }
 

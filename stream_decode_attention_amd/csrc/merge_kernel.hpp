@@ -22,21 +22,23 @@
 
 namespace decattn {
 
+// Arguments the first loads depend on come first, as scalars, so that they
+// can be preloaded into SGPRs at wave launch; the rest arrive by a scalar load
+// from the kernel-argument segment while the first loads are in flight.
 struct MergeParams {
-    const float* ws_ml;     // [B][Hkv][NC][RT][2]
-    const float* ws_acc;    // [B][Hkv][NC][RT][D]
-    const int32_t* lens;    // [B]
     void* out;              // [B][T][Hq][D]
     int out_bf16;
-    int T, Hq, Hkv, G, S_max, chunk, NC, RT, causal;
+    int T, S_max, chunk, causal;
 };
 
 constexpr int kMergeThreads = 512;
 constexpr int kMergeUnroll = 16;
 
+// ws_ml [B][Hkv][NC][RT][2], ws_acc [B][Hkv][NC][RT][D], lens [B]; THq = T*Hq.
 template <int D>
 __global__ void __launch_bounds__(kMergeThreads)
-lse_merge(const MergeParams p) {
+lse_merge(const float* ws_ml_, const float* ws_acc_, const int32_t* lens, int THq, int Hq, int G, int Hkv, int NC,
+          int RT, const MergeParams p) {
     constexpr int QPR = D / 4;                    // float4 quads per row
     constexpr int NCL = kMergeThreads / QPR;      // tile lanes working in parallel
     __shared__ float4 s_acc[NCL][QPR];
@@ -44,16 +46,16 @@ lse_merge(const MergeParams p) {
     __shared__ float s_l[NCL];
 
     const int row = blockIdx.x;                   // (b, i, h) flattened
-    const int b = row / (p.T * p.Hq);
-    const int rem = row - b * p.T * p.Hq;
-    const int i = rem / p.Hq;
-    const int h = rem - i * p.Hq;
-    const int kvh = h / p.G;
-    const int r = i * p.G + (h - kvh * p.G);
+    const int b = row / THq;
+    const int rem = row - b * THq;
+    const int i = rem / Hq;
+    const int h = rem - i * Hq;
+    const int kvh = h / G;
+    const int r = i * G + (h - kvh * G);
 
-    const size_t head0 = (size_t)(b * p.Hkv + kvh) * p.NC * p.RT;   // tile 0, row 0
-    const float* ml = p.ws_ml + head0 * 2;
-    const float* accp = p.ws_acc + head0 * D;
+    const size_t head0 = (size_t)(b * Hkv + kvh) * NC * RT;   // tile 0, row 0
+    const float* ml = ws_ml_ + head0 * 2;
+    const float* accp = ws_acc_ + head0 * D;
     const int tid = threadIdx.x;
     const int q4 = tid % QPR;
     const int cl = tid / QPR;
@@ -68,7 +70,7 @@ lse_merge(const MergeParams p) {
         for (int u = 0; u < kMergeUnroll; ++u) {
             const int c = c0 + u * NCL;
             if (c < bound) {
-                const size_t tr = (size_t)c * p.RT + r;
+                const size_t tr = (size_t)c * RT + r;
                 const float2 x = *reinterpret_cast<const float2*>(ml + tr * 2);
                 mv[u] = x.x;
                 lv[u] = x.y;
@@ -80,12 +82,12 @@ lse_merge(const MergeParams p) {
             }
         }
     };
-    fetch(cl, p.NC);
+    fetch(cl, NC);
 
-    const int len = p.lens[b];
+    const int len = lens[b];
     const int n = clamp_len_add(len, p.causal ? i + 1 : 0, p.S_max);
     int na = (n + p.chunk - 1) / p.chunk;
-    na = na < p.NC ? na : p.NC;
+    na = na < NC ? na : NC;
 
     if (na == 0) {
         if (tid < D) {
