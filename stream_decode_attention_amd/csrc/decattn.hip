@@ -39,6 +39,7 @@ constexpr int kMaxWavesPerBlock = 8;       // matches __launch_bounds__(512)
 #define DECATTN_MAX_KEY_WAVES 4
 #endif
 constexpr int kMaxKeyWaves = DECATTN_MAX_KEY_WAVES;   // waves splitting one tile's keys
+static_assert((kMaxKeyWaves & (kMaxKeyWaves - 1)) == 0, "the partial kernel splits its waves by shifts");
 constexpr size_t kMaxLdsBytes = 64 * 1024;
 constexpr int kMinChunk = 16;
 constexpr int kMaxChunk = 1 << 20;
@@ -174,19 +175,22 @@ template <int D, int R>
 hipError_t launch_partial_dr(const Plan& pl, const PartialParams& pp, hipStream_t s) {
     const int threads = 64 * pl.nwk * pl.rg_per_block;
     const long long items = (long long)pl.B * pl.Hkv * pl.n_row_blocks * pl.NC;   // every possible tile
+    const int g_magic = (65536 + pl.G - 1) / pl.G;     // r / G = (r * g_magic) >> 16 for r < 8192
     // one workgroup per possible work item when they all fit on the device at
-    // once: each knows its tile from its index and reads only its own row's
-    // length (no staging, counting or barrier; tiles past the length exit);
-    // measured 0.6-0.7 us faster per call than the persistent walk on the
-    // single-sequence decode layers
+    // once: each knows its tile from its index (grid NC x Hkv x B, one row
+    // block) and reads only its own row's length (no staging, counting or
+    // barrier; tiles past the length exit); measured 0.6-0.7 us faster per
+    // call than the persistent walk on the single-sequence decode layers
     const void* fn1 = reinterpret_cast<const void*>(&split_kv_partial<D, R, true>);
     const long long res1 = resident_blocks(fn1, threads, pl.lds_bytes);
     if (res1 <= 0) return hipErrorInvalidDeviceFunction;
     // (only for tiles of at most kNumBuf sub-tiles per wave, the shape it was
     // measured on: a one-tile-per-row call on this loop ran 1.7x slower than
     // on the persistent walk)
-    if (items <= res1 && pl.chunk <= kNumBuf * pl.nwk * kKeysPerWave) {
-        hipLaunchKernelGGL((split_kv_partial<D, R, true>), dim3((unsigned)items), dim3(threads), pl.lds_bytes, s, pp);
+    if (items <= res1 && pl.n_row_blocks == 1 && pl.chunk <= kNumBuf * pl.nwk * kKeysPerWave) {
+        hipLaunchKernelGGL((split_kv_partial<D, R, true>), dim3((unsigned)pl.NC, (unsigned)pl.Hkv, (unsigned)pl.B),
+                           dim3(threads), pl.lds_bytes, s, pp.lens, pp.k, pp.v, pp.q, pl.S_max, pl.chunk, pl.Hkv,
+                           g_magic, pp);
         return hipGetLastError();
     }
     // persistent: one wave of resident workgroups walks all attended tiles
@@ -194,7 +198,8 @@ hipError_t launch_partial_dr(const Plan& pl, const PartialParams& pp, hipStream_
     long long grid = resident_blocks(fn, threads, pl.lds_bytes);
     if (grid <= 0) return hipErrorInvalidDeviceFunction;
     if (grid > items) grid = items;
-    hipLaunchKernelGGL((split_kv_partial<D, R, false>), dim3((unsigned)grid), dim3(threads), pl.lds_bytes, s, pp);
+    hipLaunchKernelGGL((split_kv_partial<D, R, false>), dim3((unsigned)grid), dim3(threads), pl.lds_bytes, s, pp.lens,
+                       pp.k, pp.v, pp.q, pl.S_max, pl.chunk, pl.Hkv, g_magic, pp);
     return hipGetLastError();
 }
 
@@ -289,14 +294,13 @@ int run_merge(const Plan& pl, const int32_t* lens, int causal, void* out, int ou
     mp.out = out;
     mp.out_bf16 = out_dtype == DECATTN_OUT_BF16;
     mp.T = pl.T; mp.S_max = pl.S_max; mp.chunk = pl.chunk; mp.causal = causal;
-    const dim3 grid(pl.B * pl.T * pl.Hq);
-    const int thq = pl.T * pl.Hq;
+    const dim3 grid(pl.Hq, pl.T, pl.B);
     if (pl.D == 64)
-        hipLaunchKernelGGL(lse_merge<64>, grid, dim3(kMergeThreads), 0, s, ws_ml, ws_acc, lens, thq, pl.Hq, pl.G,
-                           pl.Hkv, pl.NC, pl.RT, mp);
+        hipLaunchKernelGGL(lse_merge<64>, grid, dim3(kMergeThreads), 0, s, ws_ml, ws_acc, lens, pl.G, pl.Hkv, pl.NC,
+                           pl.RT, mp);
     else
-        hipLaunchKernelGGL(lse_merge<128>, grid, dim3(kMergeThreads), 0, s, ws_ml, ws_acc, lens, thq, pl.Hq, pl.G,
-                           pl.Hkv, pl.NC, pl.RT, mp);
+        hipLaunchKernelGGL(lse_merge<128>, grid, dim3(kMergeThreads), 0, s, ws_ml, ws_acc, lens, pl.G, pl.Hkv, pl.NC,
+                           pl.RT, mp);
     return hipGetLastError() == hipSuccess ? DECATTN_OK : DECATTN_ERR_HIP;
 }
 

@@ -8,10 +8,12 @@
 //     out = sum_c w_c acc_c / sum_c w_c l_c,
 // then stored as fp32 or rounded to bf16. Rows with n = 0 store zeros.
 //
-// The partial state was written by another kernel, so every read misses the
-// reading compute unit's L2; the loads are therefore issued in batches (each
-// thread fetches up to kMergeUnroll tiles at once: 256 tiles of a 128-dim row
-// in one round trip) instead of one dependent round trip per tile.
+// The partial state was written by another kernel; the loads of a batch of
+// tiles are issued together (one round trip per batch), and the first batch
+// before the row's length arrives. The code stays short and free of branches
+// up to the first wait (a tile index past the workspace is clamped into it
+// and its values dropped by a select), so the waves start their loads after
+// few instruction fetches.
 // 512 threads: thread (cl, q4) owns 4 dims (one 16-byte load) of the tiles
 // c = cl, cl + NCL, ...; it folds them into a running (m, l, acc) with the
 // same rule, and the NCL tile lanes are combined once in LDS in a fixed order,
@@ -32,24 +34,21 @@ struct MergeParams {
 };
 
 constexpr int kMergeThreads = 512;
-constexpr int kMergeUnroll = 16;
+constexpr int kMergeUnroll = 4;        // tiles per thread per batch: 64 (D = 128) or 128 (D = 64) per row
 
-// ws_ml [B][Hkv][NC][RT][2], ws_acc [B][Hkv][NC][RT][D], lens [B]; THq = T*Hq.
+// ws_ml [B][Hkv][NC][RT][2], ws_acc [B][Hkv][NC][RT][D], lens [B]; one
+// workgroup per output row, grid (Hq, T, B).
 template <int D>
 __global__ void __launch_bounds__(kMergeThreads)
-lse_merge(const float* ws_ml_, const float* ws_acc_, const int32_t* lens, int THq, int Hq, int G, int Hkv, int NC,
-          int RT, const MergeParams p) {
+lse_merge(const float* ws_ml_, const float* ws_acc_, const int32_t* lens, int G, int Hkv, int NC, int RT,
+          const MergeParams p) {
     constexpr int QPR = D / 4;                    // float4 quads per row
     constexpr int NCL = kMergeThreads / QPR;      // tile lanes working in parallel
     __shared__ float4 s_acc[NCL][QPR];
     __shared__ float s_m[NCL];
     __shared__ float s_l[NCL];
 
-    const int row = blockIdx.x;                   // (b, i, h) flattened
-    const int b = row / THq;
-    const int rem = row - b * THq;
-    const int i = rem / Hq;
-    const int h = rem - i * Hq;
+    const int h = blockIdx.x, i = blockIdx.y, b = blockIdx.z;
     const int kvh = h / G;
     const int r = i * G + (h - kvh * G);
 
@@ -60,39 +59,34 @@ lse_merge(const float* ws_ml_, const float* ws_acc_, const int32_t* lens, int TH
     const int q4 = tid % QPR;
     const int cl = tid / QPR;
 
-    // The first batch of tile loads does not wait for the row's length: tiles
-    // c < NC always lie inside the workspace, and those at or past the row's
-    // tile count (stale data from earlier calls) are dropped by a select.
+    // tiles c0, c0 + NCL, ...: every load lands inside the workspace (tile
+    // index clamped to NC - 1); which of them count is decided by a select
+    // once the row's tile count is known
     float mv[kMergeUnroll], lv[kMergeUnroll];
     float4 av[kMergeUnroll];
-    auto fetch = [&](int c0, int bound) {
+    auto fetch = [&](int c0) {
 #pragma unroll
         for (int u = 0; u < kMergeUnroll; ++u) {
-            const int c = c0 + u * NCL;
-            if (c < bound) {
-                const size_t tr = (size_t)c * RT + r;
-                const float2 x = *reinterpret_cast<const float2*>(ml + tr * 2);
-                mv[u] = x.x;
-                lv[u] = x.y;
-                av[u] = *reinterpret_cast<const float4*>(accp + tr * D + q4 * 4);
-            } else {
-                mv[u] = kNegInf;
-                lv[u] = 0.f;
-                av[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-            }
+            const int c = min(c0 + u * NCL, NC - 1);
+            const size_t tr = (size_t)c * RT + r;
+            const float2 x = *reinterpret_cast<const float2*>(ml + tr * 2);
+            mv[u] = x.x;
+            lv[u] = x.y;
+            av[u] = *reinterpret_cast<const float4*>(accp + tr * D + q4 * 4);
         }
     };
-    fetch(cl, NC);
+    fetch(cl);
 
     const int len = lens[b];
     const int n = clamp_len_add(len, p.causal ? i + 1 : 0, p.S_max);
     int na = (n + p.chunk - 1) / p.chunk;
     na = na < NC ? na : NC;
+    const size_t row = ((size_t)b * p.T + i) * (size_t)gridDim.x + h;   // (b, i, h) flattened
 
     if (na == 0) {
         if (tid < D) {
-            if (p.out_bf16) reinterpret_cast<uint16_t*>(p.out)[(size_t)row * D + tid] = 0;
-            else reinterpret_cast<float*>(p.out)[(size_t)row * D + tid] = 0.f;
+            if (p.out_bf16) reinterpret_cast<uint16_t*>(p.out)[row * D + tid] = 0;
+            else reinterpret_cast<float*>(p.out)[row * D + tid] = 0.f;
         }
         return;
     }
@@ -100,7 +94,7 @@ lse_merge(const float* ws_ml_, const float* ws_acc_, const int32_t* lens, int TH
     float m_t = kNegInf, l_t = 0.f;
     float4 a_t = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int c0 = cl; c0 < na; c0 += NCL * kMergeUnroll) {
-        if (c0 != cl) fetch(c0, na);
+        if (c0 != cl) fetch(c0);
 #pragma unroll
         for (int u = 0; u < kMergeUnroll; ++u) {
             if (c0 + u * NCL >= na) {       // not this row's tile: drop (select, no arithmetic)
@@ -155,7 +149,7 @@ lse_merge(const float* ws_ml_, const float* ws_acc_, const int32_t* lens, int TH
             t.w = __builtin_fmaf(wt, u.w, t.w);
         }
         const float o0 = t.x / L, o1 = t.y / L, o2 = t.z / L, o3 = t.w / L;
-        const size_t o = (size_t)row * D + q4 * 4;
+        const size_t o = row * D + q4 * 4;
         if (p.out_bf16) {
             uint16_t* ob = reinterpret_cast<uint16_t*>(p.out) + o;
             const uint2 packed = make_uint2(

@@ -159,8 +159,9 @@ __device__ __forceinline__ void gather_all_i(int x, int (&out)[8]) {
 }
 
 // ONE_ROUND: every possible work item has a workgroup of its own (the host
-// launches one per (b, kv head, row block, tile) when they all fit on the
-// device at once), so a workgroup knows its tile from its index alone. Its
+// launches a grid of (tile, kv head, sequence) when they all fit on the
+// device at once and one row block holds every row), so a workgroup knows its
+// tile from its index alone, with no division. Its
 // first K/V loads are written over the whole tile (keys up to t1 lie inside
 // the cache) so that they need no length; keys past the length are masked by
 // select (scores to -inf, V to 0), never by a multiply, since stale slots may
@@ -168,9 +169,13 @@ __device__ __forceinline__ void gather_all_i(int x, int (&out)[8]) {
 // them. Forcing them ahead of it saved about 0.1 us per call at full length
 // and cost more when most tiles lie past the length, whose loads then fetch
 // data for nothing.)
+// The pointers and shapes the first loads depend on are leading scalar
+// arguments (preloaded into SGPRs at wave launch); g_magic = ceil(2^16 / G)
+// gives r / G = (r * g_magic) >> 16 exactly for every row index r < 8192.
 template <int D, int R, bool ONE_ROUND>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(DECATTN_WAVES_PER_EU)))
-split_kv_partial(const PartialParams p) {
+split_kv_partial(const int32_t* lens, const uint16_t* kc, const uint16_t* vc, const uint16_t* qp, int S_max,
+                 int chunk, int Hkv, int g_magic, const PartialParams p) {
     constexpr int LPK = D / 8;              // lanes per key row
     constexpr int KPL = 64 / LPK;           // keys per wave-wide load
     constexpr int NSTEP = kKeysPerWave / KPL;
@@ -186,8 +191,8 @@ split_kv_partial(const PartialParams p) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int kw = wave % p.nwk;
-    const int rgl = wave / p.nwk;
+    const int kw = wave & (p.nwk - 1);      // nwk is a power of two
+    const int rgl = wave >> __builtin_ctz(p.nwk);
     const int kk = lane / LPK;              // key slot inside one load
     const int db = lane % LPK;              // 8-dim block of this lane
     const int own = db >> SET_BITS;         // the row this lane completes
@@ -198,15 +203,15 @@ split_kv_partial(const PartialParams p) {
     float* s_acc = smem;                                    // [rgb][nwk][R][D]
     float* s_ml = smem + (size_t)p.rg_per_block * p.nwk * R * D;   // [rgb][nwk][R][2]
     int* s_len = reinterpret_cast<int*>(s_ml + (size_t)p.rg_per_block * p.nwk * R * 2);   // [B]
-    const int per_tile = p.Hkv * p.n_row_blocks;            // work items per (b, tile)
+    const int per_tile = Hkv * p.n_row_blocks;              // work items per (b, tile)
     int n_items = 0;
     if constexpr (!ONE_ROUND) {
         int my_tiles = 0;
         for (int i = tid; i < p.B; i += blockDim.x) {
-            const int len = p.lens[i];
+            const int len = lens[i];
             s_len[i] = len;
-            const int lim = clamp_len_add(len, p.causal ? p.T : 0, p.S_max);
-            my_tiles += (lim + p.chunk - 1) / p.chunk;
+            const int lim = clamp_len_add(len, p.causal ? p.T : 0, S_max);
+            my_tiles += (lim + chunk - 1) / chunk;
         }
         for (int o = 32; o > 0; o >>= 1) my_tiles += __shfl_xor(my_tiles, o);
         if (lane == 0) s_count[wave] = my_tiles;
@@ -223,7 +228,7 @@ split_kv_partial(const PartialParams p) {
     int b_cur = 0, pre_cur = 0;
     auto tiles_of = [&](int b) {
         const int len = s_len[b];
-        return (clamp_len_add(len, p.causal ? p.T : 0, p.S_max) + p.chunk - 1) / p.chunk;
+        return (clamp_len_add(len, p.causal ? p.T : 0, S_max) + chunk - 1) / chunk;
     };
 
     struct Tile {
@@ -243,9 +248,9 @@ split_kv_partial(const PartialParams p) {
         tl.rblk = rest % p.n_row_blocks;
         tl.kvh = rest / p.n_row_blocks;
         tl.len = s_len[b_cur];
-        tl.t0 = tl.c * p.chunk;
-        tl.t1 = min(tl.t0 + p.chunk, p.S_max);
-        tl.lim_all = min(clamp_len_add(tl.len, p.causal ? p.T : 0, p.S_max), tl.t1);
+        tl.t0 = tl.c * chunk;
+        tl.t1 = min(tl.t0 + chunk, S_max);
+        tl.lim_all = min(clamp_len_add(tl.len, p.causal ? p.T : 0, S_max), tl.t1);
         return tl;
     };
 
@@ -263,10 +268,10 @@ split_kv_partial(const PartialParams p) {
             const int r0 = rg * R + j;
             const bool ok = j < R && r0 < p.RT;
             const int r = ok ? r0 : 0;
-            const int i = r / p.G;
+            const int i = (r * g_magic) >> 16;      // r / G
             const int h = tl.kvh * p.G + (r - i * p.G);
-            if (j == own && ok) my_lim = min(clamp_len_add(tl.len, p.causal ? i + 1 : 0, p.S_max), tl.t1);
-            qraw[j] = *reinterpret_cast<const uint4*>(p.q + ((size_t)(tl.b * p.T + i) * p.Hq + h) * D + db * 8);
+            if (j == own && ok) my_lim = min(clamp_len_add(tl.len, p.causal ? i + 1 : 0, S_max), tl.t1);
+            qraw[j] = *reinterpret_cast<const uint4*>(qp + ((size_t)(tl.b * p.T + i) * p.Hq + h) * D + db * 8);
         }
     };
 
@@ -279,9 +284,9 @@ split_kv_partial(const PartialParams p) {
         __amdgpu_buffer_rsrc_t k, v;
     };
     auto make_tile_rsrc = [&](const Tile& tl) {
-        const size_t head_base = (size_t)(tl.b * p.Hkv + tl.kvh) * p.S_max * D;
+        const size_t head_base = (size_t)(tl.b * Hkv + tl.kvh) * S_max * D;
         const uint32_t range = (uint32_t)tl.lim_all * D * 2;
-        return Rsrc{make_rsrc(p.k + head_base, range), make_rsrc(p.v + head_base, range)};
+        return Rsrc{make_rsrc(kc + head_base, range), make_rsrc(vc + head_base, range)};
     };
 
     auto load = [&](const Rsrc& rs, uint4 (&kb)[NSTEP], uint4 (&vb)[NSTEP], int base) {
@@ -403,7 +408,7 @@ split_kv_partial(const PartialParams p) {
         // four dims per thread, the key waves folded in a fixed order
         constexpr int Q4 = D / 4;
         const int total = p.rg_per_block * R * Q4;
-        const size_t tile_row0 = ((size_t)(tl.b * p.Hkv + tl.kvh) * p.NC + tl.c) * p.RT;
+        const size_t tile_row0 = ((size_t)(tl.b * Hkv + tl.kvh) * p.NC + tl.c) * p.RT;
         for (int idx = tid; idx < total; idx += blockDim.x) {
             const int rg2 = idx / (R * Q4);
             const int rem = idx - rg2 * (R * Q4);
@@ -449,21 +454,16 @@ split_kv_partial(const PartialParams p) {
     // (one spare set of query registers), and every item ends at the end of a
     // ring cycle, where it is combined.
     if constexpr (ONE_ROUND) {
-        // Work item blockIdx.x = (((b * Hkv + kvh) * n_row_blocks + rblk) * NC + c).
+        // grid (NC, Hkv, B), one row block: the work item is the block index
         Tile tl;
-        {
-            int t = blockIdx.x;
-            tl.c = t % p.NC;
-            t /= p.NC;
-            tl.rblk = t % p.n_row_blocks;
-            t /= p.n_row_blocks;
-            tl.kvh = t % p.Hkv;
-            tl.b = t / p.Hkv;
-        }
-        tl.t0 = tl.c * p.chunk;
-        tl.t1 = min(tl.t0 + p.chunk, p.S_max);
-        const int len = p.lens[tl.b];
-        const int spt_real = (p.chunk + sub_stride - 1) / sub_stride;
+        tl.c = blockIdx.x;
+        tl.kvh = blockIdx.y;
+        tl.b = blockIdx.z;
+        tl.rblk = 0;
+        tl.t0 = tl.c * chunk;
+        tl.t1 = min(tl.t0 + chunk, S_max);
+        const int len = lens[tl.b];
+        const int spt_real = (chunk + sub_stride - 1) / sub_stride;
         const int spt = (spt_real + kNumBuf - 1) / kNumBuf * kNumBuf;
         uint4 qc[RP];
         int limc;
@@ -482,13 +482,13 @@ split_kv_partial(const PartialParams p) {
         for (int u = 0; u < kNumBuf; ++u) load(rs, kb[u], vb[u], slot_base(u, tl.t1));
 
         tl.len = len;
-        tl.lim_all = min(clamp_len_add(len, p.causal ? p.T : 0, p.S_max), tl.t1);
+        tl.lim_all = min(clamp_len_add(len, p.causal ? p.T : 0, S_max), tl.t1);
         if (tl.t0 >= tl.lim_all) return;    // workgroup-uniform: a tile past the length
         {
             const int rg = tl.rblk * p.rg_per_block + rgl;
             const int r0 = rg * R + own;
-            const int i = (r0 < p.RT ? r0 : 0) / p.G;
-            limc = (own < R && r0 < p.RT) ? min(clamp_len_add(len, p.causal ? i + 1 : 0, p.S_max), tl.t1) : 0;
+            const int i = ((r0 < p.RT ? r0 : 0) * g_magic) >> 16;   // r0 / G
+            limc = (own < R && r0 < p.RT) ? min(clamp_len_add(len, p.causal ? i + 1 : 0, S_max), tl.t1) : 0;
         }
         rs = make_tile_rsrc(tl);
         reset_state();
@@ -509,7 +509,7 @@ split_kv_partial(const PartialParams p) {
     int c_item = blockIdx.x;
     if (c_item >= n_items) return;          // workgroup-uniform
     const int P = (int)gridDim.x;
-    const int spt_real = (p.chunk + sub_stride - 1) / sub_stride;
+    const int spt_real = (chunk + sub_stride - 1) / sub_stride;
     const int spt = (spt_real + kNumBuf - 1) / kNumBuf * kNumBuf;
 
     uint4 kb[kNumBuf][NSTEP], vb[kNumBuf][NSTEP];
