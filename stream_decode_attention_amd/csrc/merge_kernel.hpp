@@ -16,8 +16,9 @@
 // few instruction fetches.
 // 512 threads: thread (cl, q4) owns 4 dims (one 16-byte load) of the tiles
 // c = cl, cl + NCL, ...; it folds them into a running (m, l, acc) with the
-// same rule, and the NCL tile lanes are combined once in LDS in a fixed order,
-// so the result does not depend on scheduling.
+// same rule; the tile lanes of a wave are joined by lane swaps and the eight
+// waves through LDS, each in a fixed order, so the result does not depend on
+// scheduling.
 #pragma once
 
 #include "device_common.hpp"
@@ -44,9 +45,9 @@ lse_merge(const float* ws_ml_, const float* ws_acc_, const int32_t* lens, int G,
           const MergeParams p) {
     constexpr int QPR = D / 4;                    // float4 quads per row
     constexpr int NCL = kMergeThreads / QPR;      // tile lanes working in parallel
-    __shared__ float4 s_acc[NCL][QPR];
-    __shared__ float s_m[NCL];
-    __shared__ float s_l[NCL];
+    __shared__ float4 s_acc[kMergeThreads / 64][QPR];
+    __shared__ float s_m[kMergeThreads / 64];
+    __shared__ float s_l[kMergeThreads / 64];
 
     const int h = blockIdx.x, i = blockIdx.y, b = blockIdx.z;
     const int kvh = h / G;
@@ -125,23 +126,51 @@ lse_merge(const float* ws_ml_, const float* ws_acc_, const int32_t* lens, int G,
         }
         m_t = m_new;
     }
-    s_acc[cl][q4] = a_t;
-    if (q4 == 0) {
-        s_m[cl] = m_t;
-        s_l[cl] = l_t;
+    // Tile lanes of one wave (4 at D = 64 in its 16-lane rows, 2 at D = 128 in
+    // its halves) are joined with lane swaps, in the same order for every
+    // lane; then the 8 waves' states are joined through LDS in wave order.
+    auto join = [&](const f32x2& mm, const f32x2& ll, const f32x2& ax, const f32x2& ay, const f32x2& az,
+                    const f32x2& aw) {
+        // the two states (m, l, acc) in .x and .y; an empty state (m = -inf)
+        // adds nothing, and two empty states stay empty
+        const float M = fmaxf(mm.x, mm.y);
+        const float mu = (M == kNegInf) ? 0.f : M;
+        const float w0 = fast_exp2(mm.x - mu), w1 = fast_exp2(mm.y - mu);
+        m_t = M;
+        l_t = __builtin_fmaf(w1, ll.y, w0 * ll.x);
+        a_t.x = __builtin_fmaf(w1, ax.y, w0 * ax.x);
+        a_t.y = __builtin_fmaf(w1, ay.y, w0 * ay.x);
+        a_t.z = __builtin_fmaf(w1, az.y, w0 * az.x);
+        a_t.w = __builtin_fmaf(w1, aw.y, w0 * aw.x);
+    };
+    if constexpr (QPR == 16) {              // rows r and r ^ 1 of the wave
+        join(swap16(m_t, m_t), swap16(l_t, l_t), swap16(a_t.x, a_t.x), swap16(a_t.y, a_t.y),
+             swap16(a_t.z, a_t.z), swap16(a_t.w, a_t.w));
+    }
+    join(swap32(m_t, m_t), swap32(l_t, l_t), swap32(a_t.x, a_t.x), swap32(a_t.y, a_t.y), swap32(a_t.z, a_t.z),
+         swap32(a_t.w, a_t.w));
+    constexpr int NW = kMergeThreads / 64;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    if (lane < QPR) {
+        s_acc[wave][lane] = a_t;
+        if (lane == 0) {
+            s_m[wave] = m_t;
+            s_l[wave] = l_t;
+        }
     }
     __syncthreads();
 
-    if (cl == 0) {
+    if (tid < QPR) {
         float M = s_m[0];
 #pragma unroll
-        for (int k = 1; k < NCL; ++k) M = fmaxf(M, s_m[k]);
+        for (int k = 1; k < NW; ++k) M = fmaxf(M, s_m[k]);
         float L = 0.f;
         float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-        for (int k = 0; k < NCL; ++k) {
-            const float wt = fast_exp2(s_m[k] - M);    // lanes with no tile: 2^-inf = 0
-            const float4 u = s_acc[k][q4];
+        for (int k = 0; k < NW; ++k) {
+            const float wt = fast_exp2(s_m[k] - M);    // waves with no tile: 2^-inf = 0
+            const float4 u = s_acc[k][tid];
             L = __builtin_fmaf(wt, s_l[k], L);
             t.x = __builtin_fmaf(wt, u.x, t.x);
             t.y = __builtin_fmaf(wt, u.y, t.y);
@@ -149,7 +178,7 @@ lse_merge(const float* ws_ml_, const float* ws_acc_, const int32_t* lens, int G,
             t.w = __builtin_fmaf(wt, u.w, t.w);
         }
         const float o0 = t.x / L, o1 = t.y / L, o2 = t.z / L, o3 = t.w / L;
-        const size_t o = row * D + q4 * 4;
+        const size_t o = row * D + tid * 4;
         if (p.out_bf16) {
             uint16_t* ob = reinterpret_cast<uint16_t*>(p.out) + o;
             const uint2 packed = make_uint2(
