@@ -155,7 +155,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true")
-    ap.add_argument("--chunk", type=int, default=0, help="override the library's default tile size")
+    ap.add_argument("--chunk", type=int, default=0,
+                    help="override the library's default tile size (workloads 2-5)")
     ap.add_argument("--only", type=str, default="", choices=["", "1", "2", "3", "5", "gemv", "prefill", "spec"],
                     help="profiling: run only this workload's (or step's) timing (no headline line)")
     ap.add_argument("--lengths", type=str, default="",
@@ -733,7 +734,7 @@ def decode_layers(args, cfg, dev, up, sda, workloads, rf, np, torch, stream, flu
             tens.append((kq, kk, vv, o))
         sets.append(tens)
     scale = layers[0]["scale"]
-    chunk = sda.default_chunk(1, 1, w.Hq, w.Hkv, w.D, w.S_max)
+    chunk = args.chunk or sda.default_chunk(1, 1, w.Hq, w.Hkv, w.D, w.S_max)
 
     def make_graphs(ch):
         wsl = [torch.empty(sda.workspace_bytes(1, 1, w.Hq, w.Hkv, w.D, w.S_max, ch), dtype=torch.uint8,
@@ -798,7 +799,7 @@ def verify_chunk(args, dev, up, sda, workloads, rf, np, torch, stream, flush, in
     res = []
     c = inputs[5][0]
     w = c["workload"]
-    chunk = sda.default_chunk(w.B, w.T, w.Hq, w.Hkv, w.D, w.S_max)
+    chunk = args.chunk or sda.default_chunk(w.B, w.T, w.Hq, w.Hkv, w.D, w.S_max)
     q = up(c["q"])
     k0, v0 = up(c["k"]), up(c["v"])
     kvs = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(7)]
