@@ -65,22 +65,35 @@ lse_merge(const float* ws_ml_, const float* ws_acc_, const int32_t* lens, int G,
     // once the row's tile count is known
     float mv[kMergeUnroll], lv[kMergeUnroll];
     float4 av[kMergeUnroll];
-    auto fetch = [&](int c0) {
+    // slots u < nu are loaded (nu is uniform); the others stay empty
+    auto fetch = [&](int c0, int nu) {
 #pragma unroll
         for (int u = 0; u < kMergeUnroll; ++u) {
-            const int c = min(c0 + u * NCL, NC - 1);
-            const size_t tr = (size_t)c * RT + r;
-            const float2 x = *reinterpret_cast<const float2*>(ml + tr * 2);
-            mv[u] = x.x;
-            lv[u] = x.y;
-            av[u] = *reinterpret_cast<const float4*>(accp + tr * D + q4 * 4);
+            if (u < nu) {
+                const int c = min(c0 + u * NCL, NC - 1);
+                const size_t tr = (size_t)c * RT + r;
+                const float2 x = *reinterpret_cast<const float2*>(ml + tr * 2);
+                mv[u] = x.x;
+                lv[u] = x.y;
+                av[u] = *reinterpret_cast<const float4*>(accp + tr * D + q4 * 4);
+            } else {
+                mv[u] = kNegInf;
+                lv[u] = 0.f;
+                av[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
         }
     };
-    fetch(cl);
+    // the first batch: only slots that can hold a tile of the workspace (a
+    // slot u past ceil(NC / NCL) lies past every row's tiles)
+    fetch(cl, min(kMergeUnroll, (NC + NCL - 1) / NCL));
+    // keep those loads ahead of the length's: without this the compiler
+    // moves the exit test for an empty row (and the length's round trip)
+    // above them
+    asm volatile("" ::: "memory");
 
     const int len = lens[b];
     const int n = clamp_len_add(len, p.causal ? i + 1 : 0, p.S_max);
-    int na = (n + p.chunk - 1) / p.chunk;
+    int na = (n + p.chunk - 1) >> __builtin_ctz(p.chunk);   // chunk is a power of two
     na = na < NC ? na : NC;
     const size_t row = ((size_t)b * p.T + i) * (size_t)gridDim.x + h;   // (b, i, h) flattened
 
@@ -95,7 +108,7 @@ lse_merge(const float* ws_ml_, const float* ws_acc_, const int32_t* lens, int G,
     float m_t = kNegInf, l_t = 0.f;
     float4 a_t = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int c0 = cl; c0 < na; c0 += NCL * kMergeUnroll) {
-        if (c0 != cl) fetch(c0);
+        if (c0 != cl) fetch(c0, kMergeUnroll);
 #pragma unroll
         for (int u = 0; u < kMergeUnroll; ++u) {
             if (c0 + u * NCL >= na) {       // not this row's tile: drop (select, no arithmetic)
