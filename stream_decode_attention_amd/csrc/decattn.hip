@@ -210,8 +210,9 @@ hipError_t launch_verify_dk(const Plan& pl, const PartialParams& pp, hipStream_t
     if (grid <= 0) return hipErrorInvalidDeviceFunction;
     const long long items = (long long)pl.B * pl.Hkv * pl.NC;   // upper bound
     if (grid > items) grid = items;
+    const int g_magic = (65536 + pl.G - 1) / pl.G;     // r / G = (r * g_magic) >> 16 for r < 8192
     hipLaunchKernelGGL((verify_partial_mfma<D, KB>), dim3((unsigned)grid), dim3(64 * kVerifyWaves),
-                       pl.mfma_lds_bytes, s, pp);
+                       pl.mfma_lds_bytes, s, pp.lens, pp.k, pp.v, pp.q, pl.S_max, pl.chunk, pl.Hkv, g_magic, pp);
     return hipGetLastError();
 }
 

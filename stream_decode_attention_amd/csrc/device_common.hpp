@@ -139,6 +139,20 @@ __device__ __forceinline__ void across_groups_sum_scatter(float (&v)[M], float (
     }
 }
 
+// Sum of an int over the 64 lanes of a wave, in every lane: DPP moves inside
+// each 16-lane row, then the row swaps (no LDS round trips, unlike a
+// shuffle-based reduction).
+__device__ __forceinline__ int wave_sum_i(int x) {
+    x += dpp_copy_i<kDppXor1>(x);
+    x += dpp_copy_i<kDppXor2>(x);
+    x += dpp_copy_i<kDppHalfMirror>(x);
+    x += dpp_copy_i<kDppMirror>(x);
+    const auto a = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
+    x = (int)(a[0] + a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+    return (int)(b[0] + b[1]);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));

@@ -211,9 +211,9 @@ split_kv_partial(const int32_t* lens, const uint16_t* kc, const uint16_t* vc, co
             const int len = lens[i];
             s_len[i] = len;
             const int lim = clamp_len_add(len, p.causal ? p.T : 0, S_max);
-            my_tiles += (lim + chunk - 1) / chunk;
+            my_tiles += (lim + chunk - 1) >> __builtin_ctz(chunk);   // chunk is a power of two
         }
-        for (int o = 32; o > 0; o >>= 1) my_tiles += __shfl_xor(my_tiles, o);
+        my_tiles = wave_sum_i(my_tiles);
         if (lane == 0) s_count[wave] = my_tiles;
         __syncthreads();
         int n_tiles = 0;
@@ -228,7 +228,7 @@ split_kv_partial(const int32_t* lens, const uint16_t* kc, const uint16_t* vc, co
     int b_cur = 0, pre_cur = 0;
     auto tiles_of = [&](int b) {
         const int len = s_len[b];
-        return (clamp_len_add(len, p.causal ? p.T : 0, S_max) + chunk - 1) / chunk;
+        return (clamp_len_add(len, p.causal ? p.T : 0, S_max) + chunk - 1) >> __builtin_ctz(chunk);
     };
 
     struct Tile {

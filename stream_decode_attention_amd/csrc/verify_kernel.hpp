@@ -83,9 +83,12 @@ __device__ __forceinline__ uint2 lds_read_tr16_b64(const char* p) {
     return __builtin_bit_cast(uint2, r);
 }
 
+// Leading scalar arguments as for split_kv_partial (preloaded into SGPRs;
+// r / G = (r * g_magic) >> 16).
 template <int D, int KB>
 __global__ void __launch_bounds__(256)
-verify_partial_mfma(const PartialParams p) {
+verify_partial_mfma(const int32_t* lens, const uint16_t* kc, const uint16_t* vc, const uint16_t* qp, int S_max,
+                    int chunk, int Hkv, int g_magic, const PartialParams p) {
     constexpr int KS = D / 16;              // 16-dim steps of the score product
     constexpr int DB = D / 32;              // 32-dim blocks of the output
     constexpr int WK = 32 * KB;             // keys per wave per sub-tile
@@ -126,25 +129,24 @@ verify_partial_mfma(const PartialParams p) {
     // empty state (m = -inf, l = 0, acc = 0) into the folded tile's slot, so
     // the merge still reads, for every row, slots that partition exactly the
     // keys that row attends.
-    auto tiles_raw = [&](int len) { return (clamp_len_add(len, p.T, p.S_max) + p.chunk - 1) / p.chunk; };
+    const int csh = __builtin_ctz(chunk);     // chunk is a power of two
+    auto tiles_raw = [&](int len) { return (clamp_len_add(len, p.T, S_max) + chunk - 1) >> csh; };
     auto short_tail = [&](int len) {
-        const int lim = clamp_len_add(len, p.T, p.S_max);
-        const int na = (lim + p.chunk - 1) / p.chunk;
-        return na >= 2 && 4 * (lim - (na - 1) * p.chunk) <= p.chunk;
+        const int lim = clamp_len_add(len, p.T, S_max);
+        const int na = (lim + chunk - 1) >> csh;
+        return na >= 2 && 4 * (lim - ((na - 1) << csh)) <= chunk;
     };
 
     // ---- lengths into LDS; count attended tiles, with and without folding
     int my_raw = 0, my_short = 0;
     for (int i = tid; i < p.B; i += blockDim.x) {
-        const int len = p.lens[i];
+        const int len = lens[i];
         s_len[i] = len;
         my_raw += tiles_raw(len);
         my_short += short_tail(len) ? 1 : 0;
     }
-    for (int o = 32; o > 0; o >>= 1) {
-        my_raw += __shfl_xor(my_raw, o);
-        my_short += __shfl_xor(my_short, o);
-    }
+    my_raw = wave_sum_i(my_raw);
+    my_short = wave_sum_i(my_short);
     if (lane == 0) {
         s_count[wave] = my_raw;
         s_count[kVerifyWaves + wave] = my_short;
@@ -157,16 +159,16 @@ verify_partial_mfma(const PartialParams p) {
         n_short += s_count[kVerifyWaves + w];
     }
     const int P = (int)gridDim.x;
-    const bool fold = (n_raw * p.Hkv + P - 1) / P > ((n_raw - n_short) * p.Hkv + P - 1) / P;
-    const int n_items = (fold ? n_raw - n_short : n_raw) * p.Hkv;
+    const bool fold = (n_raw * Hkv + P - 1) / P > ((n_raw - n_short) * Hkv + P - 1) / P;
+    const int n_items = (fold ? n_raw - n_short : n_raw) * Hkv;
     auto tiles_of = [&](int b) { return tiles_raw(s_len[b]) - (fold && short_tail(s_len[b]) ? 1 : 0); };
     int b_cur = 0, pre_cur = 0;
 
     const float qs = p.qscale;
     for (int item = blockIdx.x; item < n_items; item += P) {
         // locate (b, kvh, tile); items are b-major, the walk only moves forward
-        while (item >= pre_cur + tiles_of(b_cur) * p.Hkv) {
-            pre_cur += tiles_of(b_cur) * p.Hkv;
+        while (item >= pre_cur + tiles_of(b_cur) * Hkv) {
+            pre_cur += tiles_of(b_cur) * Hkv;
             ++b_cur;
         }
         const int b = b_cur;
@@ -175,10 +177,10 @@ verify_partial_mfma(const PartialParams p) {
         const int c = u % na;
         const int kvh = u / na;
         const int len = s_len[b];
-        const int lim_head = clamp_len_add(len, p.T, p.S_max);
+        const int lim_head = clamp_len_add(len, p.T, S_max);
         const bool folded = c == na - 1 && fold && short_tail(len);   // also takes the tile after it
-        const int t0 = c * p.chunk;
-        const int t1 = folded ? lim_head : min(t0 + p.chunk, p.S_max);
+        const int t0 = c << csh;
+        const int t1 = folded ? lim_head : min(t0 + chunk, S_max);
         const int lim_all = min(lim_head, t1);
 
         // this lane's row (n) and its key limit; query slice for the B operand.
@@ -186,18 +188,18 @@ verify_partial_mfma(const PartialParams p) {
         // no branch) and are masked by a key limit of 0.
         const bool row_ok = n < p.RT;
         const int nr = row_ok ? n : 0;
-        const int i = nr / p.G;
-        const int lim_n = row_ok ? min(clamp_len_add(len, i + 1, p.S_max), t1) : 0;
-        const int lim_min = min(clamp_len_add(len, 1, p.S_max), t1);   // row i = 0 attends the fewest keys
-        const uint16_t* qrow = p.q + ((size_t)(b * p.T + i) * p.Hq + kvh * p.G + (nr - i * p.G)) * D + h * 8;
+        const int i = (nr * g_magic) >> 16;   // nr / G
+        const int lim_n = row_ok ? min(clamp_len_add(len, i + 1, S_max), t1) : 0;
+        const int lim_min = min(clamp_len_add(len, 1, S_max), t1);   // row i = 0 attends the fewest keys
+        const uint16_t* qrow = qp + ((size_t)(b * p.T + i) * p.Hq + kvh * p.G + (nr - i * p.G)) * D + h * 8;
         uint4 qv[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) qv[ks] = *reinterpret_cast<const uint4*>(qrow + ks * 16);
 
-        const size_t head_base = (size_t)(b * p.Hkv + kvh) * p.S_max * D;
+        const size_t head_base = (size_t)(b * Hkv + kvh) * S_max * D;
         const uint32_t range = (uint32_t)lim_all * D * 2;
-        const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + head_base, range);
-        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + head_base, range);
+        const __amdgpu_buffer_rsrc_t krs = make_rsrc(kc + head_base, range);
+        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vc + head_base, range);
 
         float m_run = kNegInf, l_run = 0.f;
         f32x16_t acc[DB];
@@ -354,7 +356,7 @@ verify_partial_mfma(const PartialParams p) {
             }
         }
         __syncthreads();
-        const size_t tile_row0 = ((size_t)(b * p.Hkv + kvh) * p.NC + c) * p.RT;
+        const size_t tile_row0 = ((size_t)(b * Hkv + kvh) * p.NC + c) * p.RT;
         // per row: the waves' common maximum, their weights and the summed l
         if (tid < p.RT) {
             float M = kNegInf;
