@@ -42,6 +42,14 @@ constexpr int kMaxKeyWaves = DECATTN_MAX_KEY_WAVES;   // waves splitting one til
 static_assert((kMaxKeyWaves & (kMaxKeyWaves - 1)) == 0, "the partial kernel splits its waves by shifts");
 constexpr size_t kMaxLdsBytes = 64 * 1024;
 constexpr int kMinChunk = 16;
+// Decode calls (T = 1) with at least this many query heads per kv head run on
+// the matrix-core kernel when the tile is a multiple of 128 keys. Measured per
+// call on MI355X: TinyLlama layers (G = 8, D = 64, one sequence of 1k-8k keys)
+// 8.2-9.0 us against 8.8-9.9 on the dot-product kernel; eight sequences with
+// G = 8, D = 128 at the headline lengths 83.7 against 91.9 us. With G = 3 or 4
+// (SmolLM2-360M layers, the Llama-3-8B batch) the matrix cores were slower:
+// 8.1 against 8.0 us and 83.0 against 79.1 us.
+constexpr int kMfmaDecodeMinG = 8;
 constexpr int kMaxChunk = 1 << 20;
 constexpr size_t kAlign = 256;
 constexpr int kKeyMargin = 512;            // keys a kernel may address past S_max (reading zeros)
@@ -114,9 +122,10 @@ int make_plan(int B, int T, int Hq, int Hkv, int D, int S_max, int chunk, Plan* 
     if ((long long)B * Hkv * p.n_row_blocks * nc > 0x7FFFFFFF) return DECATTN_ERR_UNSUPPORTED;
     p.lds_bytes = (size_t)rgb * lds_per_rg + lds_lens;
 
-    // verify chunks of at most 32 rows per kv head on tiles of a multiple of
-    // 128 keys run on the matrix cores (scores and p.V are dense products there)
-    p.mfma = T > 1 && p.RT <= kVerifyMaxRows && chunk % 128 == 0;
+    // verify chunks (and decode calls with kMfmaDecodeMinG or more query heads
+    // per kv head) of at most 32 rows per kv head on tiles of a multiple of 128
+    // keys run on the matrix cores (scores and p.V are dense products there)
+    p.mfma = (T > 1 || G >= kMfmaDecodeMinG) && p.RT <= kVerifyMaxRows && chunk % 128 == 0;
     // one 32-key block per wave: a 128-key sub-tile per workgroup, and room
     // in registers for the next sub-tile's loads while one is computed
     p.mfma_kb = 1;
@@ -218,7 +227,7 @@ hipError_t launch_verify_dk(const Plan& pl, const PartialParams& pp, hipStream_t
 
 template <int D>
 hipError_t launch_partial_d(const Plan& pl, const PartialParams& pp, hipStream_t s) {
-    if (pl.mfma && pp.causal)
+    if (pl.mfma)
         return launch_verify_dk<D, 1>(pl, pp, s);
     switch (pl.R) {
         case 1: return launch_partial_dr<D, 1>(pl, pp, s);

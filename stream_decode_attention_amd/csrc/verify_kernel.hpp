@@ -130,9 +130,12 @@ verify_partial_mfma(const int32_t* lens, const uint16_t* kc, const uint16_t* vc,
     // the merge still reads, for every row, slots that partition exactly the
     // keys that row attends.
     const int csh = __builtin_ctz(chunk);     // chunk is a power of two
-    auto tiles_raw = [&](int len) { return (clamp_len_add(len, p.T, S_max) + chunk - 1) >> csh; };
+    // keys a row may attend: j < ctx + i + 1 for a causal chunk (row i), j < len
+    // for a decode call (and a non-causal chunk)
+    const int tok_add = p.causal ? p.T : 0;
+    auto tiles_raw = [&](int len) { return (clamp_len_add(len, tok_add, S_max) + chunk - 1) >> csh; };
     auto short_tail = [&](int len) {
-        const int lim = clamp_len_add(len, p.T, S_max);
+        const int lim = clamp_len_add(len, tok_add, S_max);
         const int na = (lim + chunk - 1) >> csh;
         return na >= 2 && 4 * (lim - ((na - 1) << csh)) <= chunk;
     };
@@ -177,7 +180,7 @@ verify_partial_mfma(const int32_t* lens, const uint16_t* kc, const uint16_t* vc,
         const int c = u % na;
         const int kvh = u / na;
         const int len = s_len[b];
-        const int lim_head = clamp_len_add(len, p.T, S_max);
+        const int lim_head = clamp_len_add(len, tok_add, S_max);
         const bool folded = c == na - 1 && fold && short_tail(len);   // also takes the tile after it
         const int t0 = c << csh;
         const int t1 = folded ? lim_head : min(t0 + chunk, S_max);
@@ -189,8 +192,8 @@ verify_partial_mfma(const int32_t* lens, const uint16_t* kc, const uint16_t* vc,
         const bool row_ok = n < p.RT;
         const int nr = row_ok ? n : 0;
         const int i = (nr * g_magic) >> 16;   // nr / G
-        const int lim_n = row_ok ? min(clamp_len_add(len, i + 1, S_max), t1) : 0;
-        const int lim_min = min(clamp_len_add(len, 1, S_max), t1);   // row i = 0 attends the fewest keys
+        const int lim_n = row_ok ? min(clamp_len_add(len, p.causal ? i + 1 : 0, S_max), t1) : 0;
+        const int lim_min = min(clamp_len_add(len, p.causal ? 1 : 0, S_max), t1);   // row i = 0 attends the fewest
         const uint16_t* qrow = qp + ((size_t)(b * p.T + i) * p.Hq + kvh * p.G + (nr - i * p.G)) * D + h * 8;
         uint4 qv[KS];
 #pragma unroll

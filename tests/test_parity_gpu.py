@@ -196,7 +196,8 @@ def test_persistent_walk_graph_replay_follows_device_lengths():
 # ------------------------------------------------------------- size extremes
 
 def test_row_with_more_tiles_than_one_merge_batch():
-    """1250 tiles in one row: the merge folds them in five batches of 256."""
+    """1250 tiles in one row: the merge folds them in batches of 64 (16 tile
+    lanes of four slots), 20 rounds."""
     c = workloads.make_case(2, 4, 1, 128, 40000, [40000, 17000], seed=41)
     ref = oracle.decode_attention(c["q"], c["k"], c["v"], c["lens"], c["scale"])
     assert_f32_close(run_decode(c, chunk=32), ref)
