@@ -52,10 +52,9 @@ constexpr int kVerifyWaves = 4;
 constexpr int kVerifyMaxRows = 32;
 
 // LDS of the cross-wave combine, in floats: per wave RT rows of D + 4 floats
-// (the pad staggers the rows over the banks), then (m, l) per wave and row,
-// then one weight per wave and row.
+// (the pad staggers the rows over the banks), then (m, l) per wave and row.
 __host__ __device__ constexpr int verify_comb_floats(int RT, int D) {
-    return kVerifyWaves * RT * (D + 4) + kVerifyWaves * RT * 2 + RT * kVerifyWaves;
+    return kVerifyWaves * RT * (D + 4) + kVerifyWaves * RT * 2;
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
@@ -118,7 +117,6 @@ verify_partial_mfma(const int32_t* lens, const uint16_t* kc, const uint16_t* vc,
     constexpr int CST = D + 4;                                   // combine row stride (floats)
     float* c_acc = smem;                                         // [waves][RT][CST]  (aliases the V tiles)
     float* c_ml = smem + (size_t)kVerifyWaves * p.RT * CST;      // [waves][RT][2]
-    float* c_wt = c_ml + kVerifyWaves * p.RT * 2;                // [RT][waves]
     int* s_len = reinterpret_cast<int*>(reinterpret_cast<char*>(smem) + p.lds_main);
 
     // One work item per attended tile (keys j < ctx + T) of every (b, kvh);
@@ -360,45 +358,42 @@ verify_partial_mfma(const int32_t* lens, const uint16_t* kc, const uint16_t* vc,
         }
         __syncthreads();
         const size_t tile_row0 = ((size_t)(b * Hkv + kvh) * p.NC + c) * p.RT;
-        // per row: the waves' common maximum, their weights and the summed l
-        if (tid < p.RT) {
-            float M = kNegInf;
-#pragma unroll
-            for (int w = 0; w < kVerifyWaves; ++w) M = fmaxf(M, c_ml[(w * p.RT + tid) * 2]);
-            float L = 0.f;
-#pragma unroll
-            for (int w = 0; w < kVerifyWaves; ++w) {
-                const float wt = M == kNegInf ? 0.f : fast_exp2(c_ml[(w * p.RT + tid) * 2] - M);
-                c_wt[tid * kVerifyWaves + w] = wt;
-                L = __builtin_fmaf(wt, c_ml[(w * p.RT + tid) * 2 + 1], L);
-            }
-            p.ws_ml[(tile_row0 + tid) * 2 + 0] = M;
-            p.ws_ml[(tile_row0 + tid) * 2 + 1] = L;
-            if (folded) {                   // the folded tile's slot: an empty state
-                p.ws_ml[(tile_row0 + p.RT + tid) * 2 + 0] = kNegInf;
-                p.ws_ml[(tile_row0 + p.RT + tid) * 2 + 1] = 0.f;
-            }
-        }
-        if (folded)
-            for (int idx = tid; idx < p.RT * (D / 4); idx += blockDim.x)
-                *reinterpret_cast<float4*>(p.ws_acc + (tile_row0 + p.RT) * D + idx * 4) = make_float4(0.f, 0.f, 0.f, 0.f);
-        __syncthreads();
+        // each thread takes four dims of one row and joins the waves itself:
+        // their common maximum, weights and summed l come from the row's
+        // (m, l) in LDS (recomputed per thread, so no further barrier); the
+        // thread holding a row's first dims writes the row's (M, L)
         for (int idx = tid; idx < p.RT * (D / 4); idx += blockDim.x) {
             const int r = idx / (D / 4);
             const int d = (idx - r * (D / 4)) * 4;
+            float M = kNegInf;
+#pragma unroll
+            for (int w = 0; w < kVerifyWaves; ++w) M = fmaxf(M, c_ml[(w * p.RT + r) * 2]);
+            float L = 0.f;
             float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
             for (int w = 0; w < kVerifyWaves; ++w) {
-                const float wt = c_wt[r * kVerifyWaves + w];
+                const float wt = M == kNegInf ? 0.f : fast_exp2(c_ml[(w * p.RT + r) * 2] - M);
                 const float4 a = *reinterpret_cast<const float4*>(c_acc + ((size_t)w * p.RT + r) * CST + d);
+                L = __builtin_fmaf(wt, c_ml[(w * p.RT + r) * 2 + 1], L);
                 A.x = __builtin_fmaf(wt, a.x, A.x);
                 A.y = __builtin_fmaf(wt, a.y, A.y);
                 A.z = __builtin_fmaf(wt, a.z, A.z);
                 A.w = __builtin_fmaf(wt, a.w, A.w);
             }
             *reinterpret_cast<float4*>(p.ws_acc + (tile_row0 + r) * D + d) = A;
+            if (d == 0) {
+                p.ws_ml[(tile_row0 + r) * 2 + 0] = M;
+                p.ws_ml[(tile_row0 + r) * 2 + 1] = L;
+                if (folded) {               // the folded tile's slot: an empty state
+                    p.ws_ml[(tile_row0 + p.RT + r) * 2 + 0] = kNegInf;
+                    p.ws_ml[(tile_row0 + p.RT + r) * 2 + 1] = 0.f;
+                }
+            }
         }
-        __syncthreads();                    // LDS is rewritten by the next item
+        if (folded)
+            for (int idx = tid; idx < p.RT * (D / 4); idx += blockDim.x)
+                *reinterpret_cast<float4*>(p.ws_acc + (tile_row0 + p.RT) * D + idx * 4) = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (item + P < n_items) __syncthreads();   // LDS is rewritten by the next item (uniform test)
     }
 }
 
