@@ -372,8 +372,9 @@ split_kv_partial(const int32_t* lens, const uint16_t* kc, const uint16_t* vc, co
 
     // Sum the lane groups of the wave, combine the key waves of the workgroup
     // in LDS and write the tile's partial state. Every wave calls this once per
-    // work item, in the same order (two workgroup barriers).
-    auto finish = [&](const Tile& tl) {
+    // work item, in the same order (a workgroup barrier, and a second one when
+    // another item follows: `more`, uniform).
+    auto finish = [&](const Tile& tl, bool more) {
         l_run = across_groups_sum<LPK>(l_run);
         // acc summed over the key groups and scattered over the four 16-lane
         // rows: row q ends with dims db*8 + q and db*8 + 4 + q of every slot
@@ -439,7 +440,7 @@ split_kv_partial(const int32_t* lens, const uint16_t* kc, const uint16_t* vc, co
                 p.ws_ml[(tile_row0 + r) * 2 + 1] = L;
             }
         }
-        __syncthreads();                    // LDS is rewritten by the next item's combine
+        if (more) __syncthreads();          // LDS is rewritten by the next item's combine (uniform)
     };
 
     // ---- one stream of sub-tiles across this workgroup's work items
@@ -502,7 +503,7 @@ split_kv_partial(const int32_t* lens, const uint16_t* kc, const uint16_t* vc, co
                 if (DECATTN_PREFETCH_FENCE) __builtin_amdgcn_sched_barrier(0);
             }
         }
-        finish(tl);
+        finish(tl, false);
         return;
     }
 
@@ -555,7 +556,7 @@ split_kv_partial(const int32_t* lens, const uint16_t* kc, const uint16_t* vc, co
                 if (s0 + u < spt_real && base < ct.lim_all) compute(qc, limc, kb[u], vb[u], base, 0x7FFFFFFF);
             }
         }
-        finish(ct);
+        finish(ct, c_item + P < n_items);
         c_item += P;
         if (c_item >= n_items) break;
         ct = lt;                            // the load pointer is already in this item
