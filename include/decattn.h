@@ -134,11 +134,12 @@ int decode_attn_noalloc(const void* q, const void* k_cache, const void* v_cache,
  *   out        [B][T][Hq][D]
  *   workspace  >= decattn_workspace_bytes(B, T, Hq, Hkv, D, S_max, chunk)
  * Other arguments as decode_attn. Row (i, h) equals decode_attn on the same
- * cache with seq_lens = ctx + i + 1 and the same chunk: bit for bit when the
- * vector kernel runs (T*G > 32 rows per kv head, or chunk not a multiple of
- * 128), and to fp32 rounding (|diff| <= 1e-4 of O(1) outputs) when the
- * matrix-core kernel runs (T*G <= 32 and chunk a multiple of 128, which the
- * default chunk is), since that kernel sums q.k in a different order. */
+ * cache with seq_lens = ctx + i + 1 and the same chunk: bit for bit when both
+ * calls run on the same kernel, and to fp32 rounding (|diff| <= 1e-4 of O(1)
+ * outputs) otherwise, since the two kernels sum q.k in different orders. The
+ * matrix-core kernel runs a chunk call when T*G <= 32 rows per kv head and
+ * chunk is a multiple of 128 (the default chunk is), and a decode call when
+ * G >= 8 and chunk is a multiple of 128; the vector kernel runs the others. */
 int chunk_attn(const void* q, const void* k_cache, const void* v_cache,
                const int32_t* ctx_lens,
                int B, int T, int Hq, int Hkv, int D, int S_max, float scale,

@@ -30,6 +30,11 @@
 //
 // Work distribution, lengths and buffer-resource loads as split_kv_partial
 // (persistent grid over attended tiles, keys past a limit read as zeros).
+//
+// Decode mode (causal = 0): every row attends j < seq_len. Decode calls with
+// eight or more query heads per kv head run here, where the dot-product
+// kernel's vector work per key (G rows x D dims of scores and p.V) would
+// outlast the data it waits for.
 #pragma once
 
 #include "partial_kernel.hpp"
