@@ -204,6 +204,16 @@ def test_row_with_more_tiles_than_one_merge_batch():
     assert_bf16_close(run_decode(c, chunk=32, out_dtype=torch.bfloat16), ref)
 
 
+def test_row_with_more_tiles_than_one_merge_batch_d64():
+    """D = 64: 32 tile lanes of four slots, 128 tiles per batch; 1000 tiles in
+    the first row (eight rounds, the last one partial), 129 in the second
+    (one tile into the second round), and a row of 0 keys."""
+    c = workloads.make_case(3, 6, 2, 64, 16000, [16000, 2064, 0], seed=42)
+    ref = oracle.decode_attention(c["q"], c["k"], c["v"], c["lens"], c["scale"])
+    assert_f32_close(run_decode(c, chunk=16), ref)
+    assert_bf16_close(run_decode(c, chunk=16, out_dtype=torch.bfloat16), ref)
+
+
 def test_largest_batch():
     """B = 4096 (the most lengths the kernels stage in LDS), lengths 0..16."""
     B = 4096
