@@ -306,10 +306,10 @@ int run_merge(const Plan& pl, const int32_t* lens, int causal, void* out, int ou
     mp.T = pl.T; mp.S_max = pl.S_max; mp.chunk = pl.chunk; mp.causal = causal;
     const dim3 grid(pl.Hq, pl.T, pl.B);
     if (pl.D == 64)
-        hipLaunchKernelGGL(lse_merge<64>, grid, dim3(kMergeThreads), 0, s, ws_ml, ws_acc, lens, pl.G, pl.Hkv, pl.NC,
+        hipLaunchKernelGGL(lse_merge<64>, grid, dim3(merge_threads(64)), 0, s, ws_ml, ws_acc, lens, pl.G, pl.Hkv, pl.NC,
                            pl.RT, mp);
     else
-        hipLaunchKernelGGL(lse_merge<128>, grid, dim3(kMergeThreads), 0, s, ws_ml, ws_acc, lens, pl.G, pl.Hkv, pl.NC,
+        hipLaunchKernelGGL(lse_merge<128>, grid, dim3(merge_threads(128)), 0, s, ws_ml, ws_acc, lens, pl.G, pl.Hkv, pl.NC,
                            pl.RT, mp);
     return hipGetLastError() == hipSuccess ? DECATTN_OK : DECATTN_ERR_HIP;
 }

@@ -14,10 +14,10 @@
 // up to the first wait (a tile index past the workspace is clamped into it
 // and its values dropped by a select), so the waves start their loads after
 // few instruction fetches.
-// 512 threads: thread (cl, q4) owns 4 dims (one 16-byte load) of the tiles
-// c = cl, cl + NCL, ...; it folds them into a running (m, l, acc) with the
-// same rule; the tile lanes of a wave are joined by lane swaps and the eight
-// waves through LDS, each in a fixed order, so the result does not depend on
+// Thread (cl, q4) owns 4 dims (one 16-byte load) of the tiles c = cl,
+// cl + 8, ...; it folds them into a running (m, l, acc) with the same rule;
+// the tile lanes of a wave are joined by lane swaps and the waves (2 or 4)
+// through LDS, each in a fixed order, so the result does not depend on
 // scheduling.
 #pragma once
 
@@ -34,16 +34,24 @@ struct MergeParams {
     int T, S_max, chunk, causal;
 };
 
-constexpr int kMergeThreads = 512;
-constexpr int kMergeUnroll = 4;        // tiles per thread per batch: 64 (D = 128) or 128 (D = 64) per row
+// Threads per row: 8 tile lanes of D / 4 threads (128 at D = 64, 256 at
+// D = 128), each loading 8 tiles per batch, so 64 tiles per round trip. On
+// MI355X this is about 0.2 us faster per call than 512 threads of 4 tiles:
+// fewer waves to start and to join through LDS.
+// One wave of 16 tiles per thread (no LDS join) took 0.4 us longer on short
+// calls and 1.5 us longer on a 32-tile row: its 48 loads issue one after
+// another from one wave.
+__host__ __device__ constexpr int merge_threads(int D) { return 2 * D; }
+constexpr int kMergeUnroll = 8;
 
 // ws_ml [B][Hkv][NC][RT][2], ws_acc [B][Hkv][NC][RT][D], lens [B]; one
 // workgroup per output row, grid (Hq, T, B).
 template <int D>
-__global__ void __launch_bounds__(kMergeThreads)
+__global__ void __launch_bounds__(merge_threads(D))
 lse_merge(const float* ws_ml_, const float* ws_acc_, const int32_t* lens, int G, int Hkv, int NC, int RT,
           const MergeParams p) {
     constexpr int QPR = D / 4;                    // float4 quads per row
+    constexpr int kMergeThreads = merge_threads(D);
     constexpr int NCL = kMergeThreads / QPR;      // tile lanes working in parallel
     __shared__ float4 s_acc[kMergeThreads / 64][QPR];
     __shared__ float s_m[kMergeThreads / 64];
@@ -98,9 +106,10 @@ lse_merge(const float* ws_ml_, const float* ws_acc_, const int32_t* lens, int G,
     const size_t row = ((size_t)b * p.T + i) * (size_t)gridDim.x + h;   // (b, i, h) flattened
 
     if (na == 0) {
-        if (tid < D) {
-            if (p.out_bf16) reinterpret_cast<uint16_t*>(p.out)[row * D + tid] = 0;
-            else reinterpret_cast<float*>(p.out)[row * D + tid] = 0.f;
+#pragma unroll
+        for (int d = tid; d < D; d += kMergeThreads) {
+            if (p.out_bf16) reinterpret_cast<uint16_t*>(p.out)[row * D + d] = 0;
+            else reinterpret_cast<float*>(p.out)[row * D + d] = 0.f;
         }
         return;
     }
@@ -141,7 +150,7 @@ lse_merge(const float* ws_ml_, const float* ws_acc_, const int32_t* lens, int G,
     }
     // Tile lanes of one wave (4 at D = 64 in its 16-lane rows, 2 at D = 128 in
     // its halves) are joined with lane swaps, in the same order for every
-    // lane; then the 8 waves' states are joined through LDS in wave order.
+    // lane; then the waves' states are joined through LDS in wave order.
     auto join = [&](const f32x2& mm, const f32x2& ll, const f32x2& ax, const f32x2& ay, const f32x2& az,
                     const f32x2& aw) {
         // the two states (m, l, acc) in .x and .y; an empty state (m = -inf)
