@@ -35,11 +35,6 @@ constexpr int kMaxT = 16;
 constexpr int kMaxB = 4096;                // lengths are staged in LDS
 constexpr int kMaxRowsPerWave = 8;
 constexpr int kMaxWavesPerBlock = 8;       // matches __launch_bounds__(512)
-#ifndef DECATTN_MAX_KEY_WAVES
-#define DECATTN_MAX_KEY_WAVES 4
-#endif
-constexpr int kMaxKeyWaves = DECATTN_MAX_KEY_WAVES;   // waves splitting one tile's keys
-static_assert((kMaxKeyWaves & (kMaxKeyWaves - 1)) == 0, "the partial kernel splits its waves by shifts");
 constexpr size_t kMaxLdsBytes = 64 * 1024;
 constexpr int kMinChunk = 16;
 // Decode calls (T = 1) with at least this many query heads per kv head run on

@@ -68,6 +68,11 @@ namespace decattn {
 
 constexpr int kKeysPerWave = DECATTN_KEYS_PER_WAVE;   // keys a wave handles per sub-tile (KPW)
 constexpr int kNumBuf = DECATTN_NBUF;                 // sub-tiles in registers: 1 computed + (NBUF-1) in flight
+#ifndef DECATTN_MAX_KEY_WAVES
+#define DECATTN_MAX_KEY_WAVES 4
+#endif
+constexpr int kMaxKeyWaves = DECATTN_MAX_KEY_WAVES;   // waves splitting one tile's keys (nwk <= this)
+static_assert((kMaxKeyWaves & (kMaxKeyWaves - 1)) == 0, "the partial kernel splits its waves by shifts");
 static_assert(kNumBuf >= 2, "the load pointer must run ahead of the compute pointer");
 
 struct PartialParams {
@@ -418,21 +423,34 @@ split_kv_partial(const int32_t* lens, const uint16_t* kc, const uint16_t* vc, co
             const int r = (tl.rblk * p.rg_per_block + rg2) * R + jr;
             if (r >= p.RT) continue;
             const int base_slot = rg2 * p.nwk * R + jr;     // slot of key wave 0 for this row
-            float M = kNegInf;
-            for (int w = 0; w < p.nwk; ++w) M = fmaxf(M, s_ml[(base_slot + w * R) * 2]);
+            // all key waves' state read at once: waves w >= nwk read wave
+            // nwk - 1's slot again (same maximum) and get weight 0, which adds
+            // exactly nothing, so the sums are those of the nwk waves in order
+            float mw[kMaxKeyWaves], lw[kMaxKeyWaves];
+            float4 aw[kMaxKeyWaves];
+#pragma unroll
+            for (int w = 0; w < kMaxKeyWaves; ++w) {
+                const int sl = base_slot + min(w, p.nwk - 1) * R;
+                const float2 ml = *reinterpret_cast<const float2*>(s_ml + sl * 2);
+                mw[w] = ml.x;
+                lw[w] = ml.y;
+                aw[w] = *reinterpret_cast<const float4*>(s_acc + (size_t)sl * D + d);
+            }
+            float M = mw[0];
+#pragma unroll
+            for (int w = 1; w < kMaxKeyWaves; ++w) M = fmaxf(M, mw[w]);
+            // no key in any wave: weights against 0 are 2^-inf = 0
+            const float Mu = (M == kNegInf) ? 0.f : M;
             float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
             float L = 0.f;
-            if (M != kNegInf) {
-                for (int w = 0; w < p.nwk; ++w) {
-                    const int sl = base_slot + w * R;
-                    const float wt = fast_exp2(s_ml[sl * 2] - M);
-                    const float4 a = *reinterpret_cast<const float4*>(s_acc + (size_t)sl * D + d);
-                    A.x = __builtin_fmaf(wt, a.x, A.x);
-                    A.y = __builtin_fmaf(wt, a.y, A.y);
-                    A.z = __builtin_fmaf(wt, a.z, A.z);
-                    A.w = __builtin_fmaf(wt, a.w, A.w);
-                    L = __builtin_fmaf(wt, s_ml[sl * 2 + 1], L);
-                }
+#pragma unroll
+            for (int w = 0; w < kMaxKeyWaves; ++w) {
+                const float wt = w < p.nwk ? fast_exp2(mw[w] - Mu) : 0.f;
+                A.x = __builtin_fmaf(wt, aw[w].x, A.x);
+                A.y = __builtin_fmaf(wt, aw[w].y, A.y);
+                A.z = __builtin_fmaf(wt, aw[w].z, A.z);
+                A.w = __builtin_fmaf(wt, aw[w].w, A.w);
+                L = __builtin_fmaf(wt, lw[w], L);
             }
             *reinterpret_cast<float4*>(p.ws_acc + (tile_row0 + r) * D + d) = A;
             if (d == 0) {
