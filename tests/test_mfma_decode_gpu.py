@@ -35,6 +35,16 @@ def test_ragged_lengths_both_modes(D, chunk):
     assert_bf16_close(run_decode(c, chunk=chunk, out_dtype=torch.bfloat16), ref)
 
 
+def test_tile_counts_around_one_merge_batch():
+    """128-key tiles on the matrix cores: rows of 64 and 65 tiles (the last
+    holding one key) around the merge's 64 tiles per round trip."""
+    lens = [64 * 128, 64 * 128 + 1, 3000]
+    c = workloads.make_case(len(lens), G, 1, 128, 64 * 128 + 128, lens, seed=305)
+    ref = oracle.decode_attention(c["q"], c["k"], c["v"], c["lens"], c["scale"])
+    assert_f32_close(run_decode(c, chunk=128), ref)
+    assert_bf16_close(run_decode(c, chunk=128, out_dtype=torch.bfloat16), ref)
+
+
 @pytest.mark.parametrize("D", [64, 128])
 def test_single_key_returns_v0_bit_exactly(D):
     c = workloads.make_case(2, G * 2, 2, D, 256, [1, 1], seed=310 + D)

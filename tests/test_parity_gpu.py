@@ -196,8 +196,8 @@ def test_persistent_walk_graph_replay_follows_device_lengths():
 # ------------------------------------------------------------- size extremes
 
 def test_row_with_more_tiles_than_one_merge_batch():
-    """1250 tiles in one row: the merge folds them in batches of 64 (16 tile
-    lanes of four slots), 20 rounds."""
+    """1250 tiles in one row: the merge folds them in batches of 64 (8 tile
+    lanes of eight slots), 20 rounds."""
     c = workloads.make_case(2, 4, 1, 128, 40000, [40000, 17000], seed=41)
     ref = oracle.decode_attention(c["q"], c["k"], c["v"], c["lens"], c["scale"])
     assert_f32_close(run_decode(c, chunk=32), ref)
@@ -205,10 +205,21 @@ def test_row_with_more_tiles_than_one_merge_batch():
 
 
 def test_row_with_more_tiles_than_one_merge_batch_d64():
-    """D = 64: 32 tile lanes of four slots, 128 tiles per batch; 1000 tiles in
-    the first row (eight rounds, the last one partial), 129 in the second
-    (one tile into the second round), and a row of 0 keys."""
+    """D = 64: 1000 tiles in the first row (16 batches of 64, the last one
+    partial), 129 in the second (one tile into the third batch), and a row of
+    0 keys."""
     c = workloads.make_case(3, 6, 2, 64, 16000, [16000, 2064, 0], seed=42)
+    ref = oracle.decode_attention(c["q"], c["k"], c["v"], c["lens"], c["scale"])
+    assert_f32_close(run_decode(c, chunk=16), ref)
+    assert_bf16_close(run_decode(c, chunk=16, out_dtype=torch.bfloat16), ref)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_tile_counts_around_one_merge_batch(D):
+    """The merge takes 64 tiles per round trip: rows of 63, 64 and 65 tiles
+    (the 65th holding one key), 128 and 129, next to an empty row."""
+    lens = [63 * 16 - 5, 64 * 16, 64 * 16 + 1, 128 * 16, 128 * 16 + 1, 0]
+    c = workloads.make_case(len(lens), 4, 2, D, 2064, lens, seed=43 + D)
     ref = oracle.decode_attention(c["q"], c["k"], c["v"], c["lens"], c["scale"])
     assert_f32_close(run_decode(c, chunk=16), ref)
     assert_bf16_close(run_decode(c, chunk=16, out_dtype=torch.bfloat16), ref)
