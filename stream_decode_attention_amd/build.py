@@ -27,10 +27,11 @@ FLAGS = [
     "-ffp-contract=off",
     # no packed fp32 (v_pk_*_f32) code generation
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # the leading scalar kernel arguments (up to 9) are preloaded into SGPRs
-    # at wave launch instead of being read from the kernel-argument segment
-    # first: about 0.2 us less per launch of the merge kernel on MI355X
-    "-mllvm", "-amdgpu-kernarg-preload-count=9",
+    # the leading scalar kernel arguments (up to 11, within the 16 SGPRs the
+    # hardware preloads) are preloaded into SGPRs at wave launch instead of
+    # being read from the kernel-argument segment first: about 0.2 us less per
+    # launch of the merge kernel on MI355X
+    "-mllvm", "-amdgpu-kernarg-preload-count=11",
     "-I", os.path.join(ROOT, "include"),
 ]
 

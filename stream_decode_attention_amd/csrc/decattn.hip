@@ -209,14 +209,30 @@ hipError_t launch_partial_dr(const Plan& pl, const PartialParams& pp, hipStream_
 
 template <int D, int KB>
 hipError_t launch_verify_dk(const Plan& pl, const PartialParams& pp, hipStream_t s) {
-    const void* fn = reinterpret_cast<const void*>(&verify_partial_mfma<D, KB>);
+    const long long items = (long long)pl.B * pl.Hkv * pl.NC;   // every possible tile
+    const int g_magic = (65536 + pl.G - 1) / pl.G;     // r / G = (r * g_magic) >> 16 for r < 8192
+    const int tok_add = pp.causal ? pl.T : 0;          // keys past the context a causal chunk adds (T = 1 if 0)
+    // one workgroup per possible tile when they all fit on the device at once
+    // (grid NC x Hkv x B; tiles past the length exit at once): no lengths
+    // staged, no counting pass; the persistent walk would give every
+    // workgroup one item and fold nothing there either, so both compute the
+    // same tiles in the same way
+    const void* fn1 = reinterpret_cast<const void*>(&verify_partial_mfma<D, KB, true>);
+    const long long res1 = resident_blocks(fn1, 64 * kVerifyWaves, pl.mfma_lds_bytes);
+    if (res1 <= 0) return hipErrorInvalidDeviceFunction;
+    if (items <= res1) {
+        hipLaunchKernelGGL((verify_partial_mfma<D, KB, true>), dim3((unsigned)pl.NC, (unsigned)pl.Hkv, (unsigned)pl.B),
+                           dim3(64 * kVerifyWaves), pl.mfma_lds_bytes, s, pp.lens, pp.k, pp.v, pp.q, pl.S_max,
+                           pl.chunk, pl.Hkv, g_magic, pl.G, tok_add, pp);
+        return hipGetLastError();
+    }
+    const void* fn = reinterpret_cast<const void*>(&verify_partial_mfma<D, KB, false>);
     long long grid = resident_blocks(fn, 64 * kVerifyWaves, pl.mfma_lds_bytes);
     if (grid <= 0) return hipErrorInvalidDeviceFunction;
-    const long long items = (long long)pl.B * pl.Hkv * pl.NC;   // upper bound
     if (grid > items) grid = items;
-    const int g_magic = (65536 + pl.G - 1) / pl.G;     // r / G = (r * g_magic) >> 16 for r < 8192
-    hipLaunchKernelGGL((verify_partial_mfma<D, KB>), dim3((unsigned)grid), dim3(64 * kVerifyWaves),
-                       pl.mfma_lds_bytes, s, pp.lens, pp.k, pp.v, pp.q, pl.S_max, pl.chunk, pl.Hkv, g_magic, pp);
+    hipLaunchKernelGGL((verify_partial_mfma<D, KB, false>), dim3((unsigned)grid), dim3(64 * kVerifyWaves),
+                       pl.mfma_lds_bytes, s, pp.lens, pp.k, pp.v, pp.q, pl.S_max, pl.chunk, pl.Hkv, g_magic, pl.G,
+                       tok_add, pp);
     return hipGetLastError();
 }
 

@@ -88,11 +88,16 @@ __device__ __forceinline__ uint2 lds_read_tr16_b64(const char* p) {
 }
 
 // Leading scalar arguments as for split_kv_partial (preloaded into SGPRs;
-// r / G = (r * g_magic) >> 16).
-template <int D, int KB>
+// r / G = (r * g_magic) >> 16), then what the query addresses and key limits
+// need, also preloaded: G query heads per kv head, and tok_add = T for a
+// causal chunk of T tokens (row i attends j < len + i + 1) or 0 for a decode
+// call (T = 1, every row attends j < len). These 14 dwords are all the
+// hardware preloads, so nothing before the first loads waits for the
+// kernel-argument segment.
+template <int D, int KB, bool ONE_ROUND>
 __global__ void __launch_bounds__(256)
 verify_partial_mfma(const int32_t* lens, const uint16_t* kc, const uint16_t* vc, const uint16_t* qp, int S_max,
-                    int chunk, int Hkv, int g_magic, const PartialParams p) {
+                    int chunk, int Hkv, int g_magic, int G, int tok_add, const PartialParams p) {
     constexpr int KS = D / 16;              // 16-dim steps of the score product
     constexpr int DB = D / 32;              // 32-dim blocks of the output
     constexpr int WK = 32 * KB;             // keys per wave per sub-tile
@@ -119,9 +124,11 @@ verify_partial_mfma(const int32_t* lens, const uint16_t* kc, const uint16_t* vc,
     // 16*(g%2) + 4*(i%4)..+3; the step, block and 8-key half add constants)
     const int v_st_off = (lane / LPK) * VROW + (lane % LPK) * 16;
     const int v_tr_off = (4 * h + ((lane & 15) >> 2)) * VROW + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+    const int T = tok_add > 0 ? tok_add : 1;                     // query tokens
+    const int RT = T * G;                                        // rows per kv head
     constexpr int CST = D + 4;                                   // combine row stride (floats)
     float* c_acc = smem;                                         // [waves][RT][CST]  (aliases the V tiles)
-    float* c_ml = smem + (size_t)kVerifyWaves * p.RT * CST;      // [waves][RT][2]
+    float* c_ml = smem + (size_t)kVerifyWaves * RT * CST;      // [waves][RT][2]
     int* s_len = reinterpret_cast<int*>(reinterpret_cast<char*>(smem) + p.lds_main);
 
     // One work item per attended tile (keys j < ctx + T) of every (b, kvh);
@@ -133,9 +140,9 @@ verify_partial_mfma(const int32_t* lens, const uint16_t* kc, const uint16_t* vc,
     // the merge still reads, for every row, slots that partition exactly the
     // keys that row attends.
     const int csh = __builtin_ctz(chunk);     // chunk is a power of two
+    const bool causal = tok_add != 0;         // a causal chunk (tok_add = T >= 1) or a decode call (0)
     // keys a row may attend: j < ctx + i + 1 for a causal chunk (row i), j < len
     // for a decode call (and a non-causal chunk)
-    const int tok_add = p.causal ? p.T : 0;
     auto tiles_raw = [&](int len) { return (clamp_len_add(len, tok_add, S_max) + chunk - 1) >> csh; };
     auto short_tail = [&](int len) {
         const int lim = clamp_len_add(len, tok_add, S_max);
@@ -143,64 +150,29 @@ verify_partial_mfma(const int32_t* lens, const uint16_t* kc, const uint16_t* vc,
         return na >= 2 && 4 * (lim - ((na - 1) << csh)) <= chunk;
     };
 
-    // ---- lengths into LDS; count attended tiles, with and without folding
-    int my_raw = 0, my_short = 0;
-    for (int i = tid; i < p.B; i += blockDim.x) {
-        const int len = lens[i];
-        s_len[i] = len;
-        my_raw += tiles_raw(len);
-        my_short += short_tail(len) ? 1 : 0;
-    }
-    my_raw = wave_sum_i(my_raw);
-    my_short = wave_sum_i(my_short);
-    if (lane == 0) {
-        s_count[wave] = my_raw;
-        s_count[kVerifyWaves + wave] = my_short;
-    }
-    __syncthreads();
-    int n_raw = 0, n_short = 0;
-#pragma unroll
-    for (int w = 0; w < kVerifyWaves; ++w) {
-        n_raw += s_count[w];
-        n_short += s_count[kVerifyWaves + w];
-    }
-    const int P = (int)gridDim.x;
-    const bool fold = (n_raw * Hkv + P - 1) / P > ((n_raw - n_short) * Hkv + P - 1) / P;
-    const int n_items = (fold ? n_raw - n_short : n_raw) * Hkv;
-    auto tiles_of = [&](int b) { return tiles_raw(s_len[b]) - (fold && short_tail(s_len[b]) ? 1 : 0); };
-    int b_cur = 0, pre_cur = 0;
-
+    // This lane's row (n) and its query slice for the B operand. Lanes past
+    // the last row load row 0 (all loads issue back to back with no branch)
+    // and are masked by a key limit of 0.
+    const bool row_ok = n < RT;
+    const int nr = row_ok ? n : 0;
+    const int i = (nr * g_magic) >> 16;   // nr / G
     const float qs = p.qscale;
-    for (int item = blockIdx.x; item < n_items; item += P) {
-        // locate (b, kvh, tile); items are b-major, the walk only moves forward
-        while (item >= pre_cur + tiles_of(b_cur) * Hkv) {
-            pre_cur += tiles_of(b_cur) * Hkv;
-            ++b_cur;
-        }
-        const int b = b_cur;
-        const int na = tiles_of(b);
-        const int u = item - pre_cur;
-        const int c = u % na;
-        const int kvh = u / na;
-        const int len = s_len[b];
+    auto load_q = [&](int b, int kvh, uint4 (&qv)[KS]) {
+        const uint16_t* qrow = qp + ((size_t)(b * T + i) * (G * Hkv) + kvh * G + (nr - i * G)) * D + h * 8;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qv[ks] = *reinterpret_cast<const uint4*>(qrow + ks * 16);
+    };
+
+    // One work item: tile c of (b, kvh), which holds at least one attended
+    // key; a folded item also takes the tile after it. `more`: the workgroup
+    // has another item, whose combine rewrites the LDS.
+    auto process = [&](int b, int kvh, int c, int len, bool folded, const uint4 (&qv)[KS], bool more) {
         const int lim_head = clamp_len_add(len, tok_add, S_max);
-        const bool folded = c == na - 1 && fold && short_tail(len);   // also takes the tile after it
         const int t0 = c << csh;
         const int t1 = folded ? lim_head : min(t0 + chunk, S_max);
         const int lim_all = min(lim_head, t1);
-
-        // this lane's row (n) and its key limit; query slice for the B operand.
-        // Lanes past the last row load row 0 (all loads issue back to back with
-        // no branch) and are masked by a key limit of 0.
-        const bool row_ok = n < p.RT;
-        const int nr = row_ok ? n : 0;
-        const int i = (nr * g_magic) >> 16;   // nr / G
-        const int lim_n = row_ok ? min(clamp_len_add(len, p.causal ? i + 1 : 0, S_max), t1) : 0;
-        const int lim_min = min(clamp_len_add(len, p.causal ? 1 : 0, S_max), t1);   // row i = 0 attends the fewest
-        const uint16_t* qrow = qp + ((size_t)(b * p.T + i) * p.Hq + kvh * p.G + (nr - i * p.G)) * D + h * 8;
-        uint4 qv[KS];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qv[ks] = *reinterpret_cast<const uint4*>(qrow + ks * 16);
+        const int lim_n = row_ok ? min(clamp_len_add(len, causal ? i + 1 : 0, S_max), t1) : 0;
+        const int lim_min = min(clamp_len_add(len, causal ? 1 : 0, S_max), t1);   // row i = 0 attends the fewest
 
         const size_t head_base = (size_t)(b * Hkv + kvh) * S_max * D;
         const uint32_t range = (uint32_t)lim_all * D * 2;
@@ -353,33 +325,33 @@ verify_partial_mfma(const int32_t* lens, const uint16_t* kc, const uint16_t* vc,
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
                     const int dim = db * 32 + 8 * g4 + 4 * h;
-                    *reinterpret_cast<float4*>(c_acc + ((size_t)wave * p.RT + n) * CST + dim) =
+                    *reinterpret_cast<float4*>(c_acc + ((size_t)wave * RT + n) * CST + dim) =
                         make_float4(acc[db][4 * g4], acc[db][4 * g4 + 1], acc[db][4 * g4 + 2], acc[db][4 * g4 + 3]);
                 }
             if (h == 0) {
-                c_ml[(wave * p.RT + n) * 2 + 0] = m_run;
-                c_ml[(wave * p.RT + n) * 2 + 1] = l_run;
+                c_ml[(wave * RT + n) * 2 + 0] = m_run;
+                c_ml[(wave * RT + n) * 2 + 1] = l_run;
             }
         }
         __syncthreads();
-        const size_t tile_row0 = ((size_t)(b * Hkv + kvh) * p.NC + c) * p.RT;
+        const size_t tile_row0 = ((size_t)(b * Hkv + kvh) * p.NC + c) * RT;
         // each thread takes four dims of one row and joins the waves itself:
         // their common maximum, weights and summed l come from the row's
         // (m, l) in LDS (recomputed per thread, so no further barrier); the
         // thread holding a row's first dims writes the row's (M, L)
-        for (int idx = tid; idx < p.RT * (D / 4); idx += blockDim.x) {
+        for (int idx = tid; idx < RT * (D / 4); idx += blockDim.x) {
             const int r = idx / (D / 4);
             const int d = (idx - r * (D / 4)) * 4;
             float M = kNegInf;
 #pragma unroll
-            for (int w = 0; w < kVerifyWaves; ++w) M = fmaxf(M, c_ml[(w * p.RT + r) * 2]);
+            for (int w = 0; w < kVerifyWaves; ++w) M = fmaxf(M, c_ml[(w * RT + r) * 2]);
             float L = 0.f;
             float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
             for (int w = 0; w < kVerifyWaves; ++w) {
-                const float wt = M == kNegInf ? 0.f : fast_exp2(c_ml[(w * p.RT + r) * 2] - M);
-                const float4 a = *reinterpret_cast<const float4*>(c_acc + ((size_t)w * p.RT + r) * CST + d);
-                L = __builtin_fmaf(wt, c_ml[(w * p.RT + r) * 2 + 1], L);
+                const float wt = M == kNegInf ? 0.f : fast_exp2(c_ml[(w * RT + r) * 2] - M);
+                const float4 a = *reinterpret_cast<const float4*>(c_acc + ((size_t)w * RT + r) * CST + d);
+                L = __builtin_fmaf(wt, c_ml[(w * RT + r) * 2 + 1], L);
                 A.x = __builtin_fmaf(wt, a.x, A.x);
                 A.y = __builtin_fmaf(wt, a.y, A.y);
                 A.z = __builtin_fmaf(wt, a.z, A.z);
@@ -390,15 +362,75 @@ verify_partial_mfma(const int32_t* lens, const uint16_t* kc, const uint16_t* vc,
                 p.ws_ml[(tile_row0 + r) * 2 + 0] = M;
                 p.ws_ml[(tile_row0 + r) * 2 + 1] = L;
                 if (folded) {               // the folded tile's slot: an empty state
-                    p.ws_ml[(tile_row0 + p.RT + r) * 2 + 0] = kNegInf;
-                    p.ws_ml[(tile_row0 + p.RT + r) * 2 + 1] = 0.f;
+                    p.ws_ml[(tile_row0 + RT + r) * 2 + 0] = kNegInf;
+                    p.ws_ml[(tile_row0 + RT + r) * 2 + 1] = 0.f;
                 }
             }
         }
         if (folded)
-            for (int idx = tid; idx < p.RT * (D / 4); idx += blockDim.x)
-                *reinterpret_cast<float4*>(p.ws_acc + (tile_row0 + p.RT) * D + idx * 4) = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (item + P < n_items) __syncthreads();   // LDS is rewritten by the next item (uniform test)
+            for (int idx = tid; idx < RT * (D / 4); idx += blockDim.x)
+                *reinterpret_cast<float4*>(p.ws_acc + (tile_row0 + RT) * D + idx * 4) = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (more) __syncthreads();       // LDS is rewritten by the next item (uniform test)
+    };
+
+    if constexpr (ONE_ROUND) {
+        // grid (NC, Hkv, B), every possible tile at once: the work item is the
+        // block index (no lengths staged, no counting, no folding). The
+        // length's load and the query loads (whose addresses need only the
+        // preloaded leading arguments) are issued together at wave start.
+        const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+        const int len = lens[b];
+        uint4 qv[KS];
+        load_q(b, kvh, qv);
+        asm volatile("" ::: "memory");   // both loads before the length's first use
+        if ((c << csh) >= clamp_len_add(len, tok_add, S_max)) return;   // workgroup-uniform: past the length
+        process(b, kvh, c, len, false, qv, false);
+        return;
+    }
+
+    // ---- lengths into LDS; count attended tiles, with and without folding
+    int my_raw = 0, my_short = 0;
+    for (int i = tid; i < p.B; i += blockDim.x) {
+        const int len = lens[i];
+        s_len[i] = len;
+        my_raw += tiles_raw(len);
+        my_short += short_tail(len) ? 1 : 0;
+    }
+    my_raw = wave_sum_i(my_raw);
+    my_short = wave_sum_i(my_short);
+    if (lane == 0) {
+        s_count[wave] = my_raw;
+        s_count[kVerifyWaves + wave] = my_short;
+    }
+    __syncthreads();
+    int n_raw = 0, n_short = 0;
+#pragma unroll
+    for (int w = 0; w < kVerifyWaves; ++w) {
+        n_raw += s_count[w];
+        n_short += s_count[kVerifyWaves + w];
+    }
+    const int P = (int)gridDim.x;
+    const bool fold = (n_raw * Hkv + P - 1) / P > ((n_raw - n_short) * Hkv + P - 1) / P;
+    const int n_items = (fold ? n_raw - n_short : n_raw) * Hkv;
+    auto tiles_of = [&](int b) { return tiles_raw(s_len[b]) - (fold && short_tail(s_len[b]) ? 1 : 0); };
+    int b_cur = 0, pre_cur = 0;
+
+    for (int item = blockIdx.x; item < n_items; item += P) {
+        // locate (b, kvh, tile); items are b-major, the walk only moves forward
+        while (item >= pre_cur + tiles_of(b_cur) * Hkv) {
+            pre_cur += tiles_of(b_cur) * Hkv;
+            ++b_cur;
+        }
+        const int b = b_cur;
+        const int na = tiles_of(b);
+        const int u = item - pre_cur;
+        const int c = u % na;
+        const int kvh = u / na;
+        const int len = s_len[b];
+        const bool folded = c == na - 1 && fold && short_tail(len);   // also takes the tile after it
+        uint4 qv[KS];
+        load_q(b, kvh, qv);
+        process(b, kvh, c, len, folded, qv, item + P < n_items);
     }
 }
 
