@@ -71,8 +71,10 @@ int decattn_abi_version(void);
 /* Static, NUL-terminated description of a status code (unknown codes included). */
 const char* decattn_status_str(int status);
 
-/* Keys per tile the library picks when `chunk` is 0, for these shapes.
- * Returns 0 when the shapes are invalid or unsupported. */
+/* Keys per tile the library picks when `chunk` is 0, for these shapes on the
+ * current device: a verify chunk takes 512-key tiles when all of them, but not
+ * all 256-key tiles, fit on the device at once (256 otherwise, and 256 with no
+ * device). Returns 0 when the shapes are invalid or unsupported. */
 int decattn_default_chunk(int B, int T, int Hq, int Hkv, int D, int S_max);
 
 /* Bytes of device workspace a call with these shapes needs (T = 1 for decode):

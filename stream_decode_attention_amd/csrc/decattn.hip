@@ -62,11 +62,36 @@ struct Plan {
     size_t mfma_lds_main, mfma_lds_bytes;
 };
 
-int pick_default_chunk(int B, int T, int G, int Hkv, int S_max) {
+int resident_blocks(const void* kernel, int threads, size_t lds);
+
+// Dynamic LDS of the matrix-core kernel: the larger of the four waves' V
+// tiles and the cross-wave combine area, then the B staged lengths.
+size_t verify_lds_bytes(int D, int RT, int B, size_t* main_bytes = nullptr) {
+    const size_t vt = (size_t)kVerifyWaves * 32 * verify_vrow(D);
+    const size_t comb = (size_t)verify_comb_floats(RT, D) * sizeof(float);
+    const size_t main = vt > comb ? vt : comb;
+    if (main_bytes) *main_bytes = main;
+    return main + (size_t)B * sizeof(int);
+}
+
+int pick_default_chunk(int B, int T, int G, int Hkv, int D, int S_max) {
     // verify chunks that fit the matrix-core kernel: 256-key tiles (two
     // pipelined sub-tiles per workgroup; measured fastest per call at the
-    // Llama-3.2-3B verify shape)
-    if (T > 1 && T * G <= kVerifyMaxRows) return 256;
+    // Llama-3.2-3B verify shape among calls that take the persistent walk),
+    // or 512 when every 512-key tile fits on the current device at once and
+    // not every 256-key tile does: the one-round launch then replaces the
+    // walk (no length staging or counting pass). Measured on MI355X at the
+    // Llama-3.2-3B verify shape (T = 6, 8 kv heads, 8192 keys of context:
+    // 264 tiles of 256 keys against 256 resident workgroups): 14.9 us per
+    // call against 16.1. Without a device to ask, 256.
+    if (T > 1 && T * G <= kVerifyMaxRows) {
+        const long long rows = (long long)B * Hkv;
+        const long long n256 = rows * ((S_max + 255) / 256), n512 = rows * ((S_max + 511) / 512);
+        const void* fn = D == 64 ? reinterpret_cast<const void*>(&verify_partial_mfma<64, 1, true>)
+                                 : reinterpret_cast<const void*>(&verify_partial_mfma<128, 1, true>);
+        const long long cap = resident_blocks(fn, 64 * kVerifyWaves, verify_lds_bytes(D, T * G, B));
+        return (n256 > cap && n512 <= cap) ? 512 : 256;
+    }
     // Decode: the largest tile (128 to 2048 keys) that still leaves at least
     // 1024 tiles over B*Hkv rows at S_max, the only length the host knows.
     // Larger tiles cut partial-state traffic (about G*(D+2)*4 bytes per tile
@@ -87,7 +112,7 @@ int make_plan(int B, int T, int Hq, int Hkv, int D, int S_max, int chunk, Plan* 
     if (D != 64 && D != 128) return DECATTN_ERR_UNSUPPORTED;
     const int G = Hq / Hkv;
     if (G > kMaxG || T > kMaxT) return DECATTN_ERR_UNSUPPORTED;
-    if (chunk == 0) chunk = pick_default_chunk(B, T, G, Hkv, S_max);
+    if (chunk == 0) chunk = pick_default_chunk(B, T, G, Hkv, D, S_max);
     // a chunk >= S_max gives one tile per row
     if (chunk < kMinChunk || chunk > kMaxChunk || !is_pow2(chunk)) return DECATTN_ERR_UNSUPPORTED;
     const long long nc = ((long long)S_max + chunk - 1) / chunk;
@@ -124,12 +149,7 @@ int make_plan(int B, int T, int Hq, int Hkv, int D, int S_max, int chunk, Plan* 
     // one 32-key block per wave: a 128-key sub-tile per workgroup, and room
     // in registers for the next sub-tile's loads while one is computed
     p.mfma_kb = 1;
-    {
-        const size_t vt = (size_t)kVerifyWaves * (32 * p.mfma_kb) * verify_vrow(D);
-        const size_t comb = (size_t)verify_comb_floats(p.RT, D) * sizeof(float);
-        p.mfma_lds_main = (vt > comb ? vt : comb);
-        p.mfma_lds_bytes = p.mfma_lds_main + lds_lens;
-    }
+    p.mfma_lds_bytes = verify_lds_bytes(D, p.RT, B, &p.mfma_lds_main);
 
     const size_t tiles_rows = (size_t)B * Hkv * p.NC * p.RT;
     p.ml_bytes = round_up(tiles_rows * 2 * sizeof(float), kAlign);

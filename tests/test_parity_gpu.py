@@ -65,13 +65,18 @@ def test_workload4_batched_ragged_full_size_every_row():
     assert torch.equal(rne.view(torch.int16), out16.view(torch.int16))
 
 
-def test_workload5_verify_chunk_vs_oracle_and_sequential_decodes():
+@pytest.mark.parametrize("chunk", [None, 256])
+def test_workload5_verify_chunk_vs_oracle_and_sequential_decodes(chunk):
+    """The default tile (512 keys on MI355X: every tile in one round of
+    workgroups) and 256-key tiles (264 tiles on 256 resident workgroups: the
+    persistent walk, which folds the short last tiles)."""
     c = workloads.make_config(5)
     ref = oracle.chunk_attention(c["q"], c["k"], c["v"], c["lens"], c["scale"])
     tensors = (dev_bits(c["q"]), dev_bits(c["k"]), dev_bits(c["v"]))
-    out32 = run_chunk(c, tensors=tensors)
+    kw = {} if chunk is None else {"chunk": chunk}
+    out32 = run_chunk(c, tensors=tensors, **kw)
     assert_f32_close(out32, ref)
-    out16 = run_chunk(c, tensors=tensors, out_dtype=torch.bfloat16)
+    out16 = run_chunk(c, tensors=tensors, out_dtype=torch.bfloat16, **kw)
     assert_bf16_close(out16, ref)
     # six sequential decode calls: token i with seq_len = ctx + i + 1. The
     # verify chunk runs on the matrix cores, the decode calls on the vector
@@ -82,6 +87,18 @@ def test_workload5_verify_chunk_vs_oracle_and_sequential_decodes():
         dec = run_decode(ci, tensors=(dev_bits(ci["q"]), tensors[1], tensors[2]))
         d = (dec - out32[:, i]).abs().max().item()
         assert d <= 1e-4, f"token {i}: chunk row and its decode call differ by {d}"
+
+
+def test_verify_default_chunk_follows_one_round_capacity():
+    """The default verify tile is 512 keys exactly when every 512-key tile, but
+    not every 256-key tile, fits in one round of workgroups (one matrix-core
+    workgroup per compute unit at D = 128)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    Hkv = 8
+    for S in (4096 + 6, 8192 + 6, 16384 + 6, 65536):
+        n256, n512 = Hkv * -(-S // 256), Hkv * -(-S // 512)
+        expect = 512 if (n256 > cus and n512 <= cus) else 256
+        assert sda.default_chunk(1, 6, 3 * Hkv, Hkv, 128, S) == expect, S
 
 
 @pytest.mark.parametrize("T,G,chunk", [(6, 3, 64), (16, 3, 256), (4, 8, 32)])
