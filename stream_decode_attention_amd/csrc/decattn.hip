@@ -128,8 +128,7 @@ int make_plan(int B, int T, int Hq, int Hkv, int D, int S_max, int chunk, Plan* 
     p.chunk = chunk; p.NC = (int)nc; p.RT = T * G;
     p.NR = (p.RT + kMaxRowsPerWave - 1) / kMaxRowsPerWave;
     p.R = (p.RT + p.NR - 1) / p.NR;
-    int nwk = chunk / kKeysPerWave;
-    p.nwk = nwk < 1 ? 1 : (nwk > kMaxKeyWaves ? kMaxKeyWaves : nwk);
+    p.nwk = key_waves_for(chunk);       // the partial kernel derives the same count
     const size_t lds_per_rg = (size_t)p.nwk * p.R * (D + 2) * sizeof(float);
     const size_t lds_lens = (size_t)B * sizeof(int);
     int rgb = kMaxWavesPerBlock / p.nwk;
@@ -200,6 +199,7 @@ hipError_t launch_partial_dr(const Plan& pl, const PartialParams& pp, hipStream_
     const int threads = 64 * pl.nwk * pl.rg_per_block;
     const long long items = (long long)pl.B * pl.Hkv * pl.n_row_blocks * pl.NC;   // every possible tile
     const int g_magic = (65536 + pl.G - 1) / pl.G;     // r / G = (r * g_magic) >> 16 for r < 8192
+    const int tok_add = pp.causal ? pl.T : 0;          // keys past the context a causal chunk adds (T = 1 if 0)
     // one workgroup per possible work item when they all fit on the device at
     // once: each knows its tile from its index (grid NC x Hkv x B, one row
     // block) and reads only its own row's length (no staging, counting or
@@ -214,7 +214,7 @@ hipError_t launch_partial_dr(const Plan& pl, const PartialParams& pp, hipStream_
     if (items <= res1 && pl.n_row_blocks == 1 && pl.chunk <= kNumBuf * pl.nwk * kKeysPerWave) {
         hipLaunchKernelGGL((split_kv_partial<D, R, true>), dim3((unsigned)pl.NC, (unsigned)pl.Hkv, (unsigned)pl.B),
                            dim3(threads), pl.lds_bytes, s, pp.lens, pp.k, pp.v, pp.q, pl.S_max, pl.chunk, pl.Hkv,
-                           g_magic, pp);
+                           g_magic, pl.G, tok_add, pp);
         return hipGetLastError();
     }
     // persistent: one wave of resident workgroups walks all attended tiles
@@ -223,7 +223,7 @@ hipError_t launch_partial_dr(const Plan& pl, const PartialParams& pp, hipStream_
     if (grid <= 0) return hipErrorInvalidDeviceFunction;
     if (grid > items) grid = items;
     hipLaunchKernelGGL((split_kv_partial<D, R, false>), dim3((unsigned)grid), dim3(threads), pl.lds_bytes, s, pp.lens,
-                       pp.k, pp.v, pp.q, pl.S_max, pl.chunk, pl.Hkv, g_magic, pp);
+                       pp.k, pp.v, pp.q, pl.S_max, pl.chunk, pl.Hkv, g_magic, pl.G, tok_add, pp);
     return hipGetLastError();
 }
 

@@ -73,6 +73,14 @@ constexpr int kNumBuf = DECATTN_NBUF;                 // sub-tiles in registers:
 #endif
 constexpr int kMaxKeyWaves = DECATTN_MAX_KEY_WAVES;   // waves splitting one tile's keys (nwk <= this)
 static_assert((kMaxKeyWaves & (kMaxKeyWaves - 1)) == 0, "the partial kernel splits its waves by shifts");
+static_assert((kKeysPerWave & (kKeysPerWave - 1)) == 0, "keys per wave is a power of two");
+
+// Key waves per tile for a tile of `chunk` keys (a power of two): one per
+// kKeysPerWave keys, at least one and at most kMaxKeyWaves. The host sizes the
+// workgroup with it and the kernel derives its wave layout from it.
+__host__ __device__ constexpr int key_waves_for(int chunk) {
+    return chunk / kKeysPerWave < 1 ? 1 : (chunk / kKeysPerWave > kMaxKeyWaves ? kMaxKeyWaves : chunk / kKeysPerWave);
+}
 static_assert(kNumBuf >= 2, "the load pointer must run ahead of the compute pointer");
 
 struct PartialParams {
@@ -180,7 +188,7 @@ __device__ __forceinline__ void gather_all_i(int x, int (&out)[8]) {
 template <int D, int R, bool ONE_ROUND>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(DECATTN_WAVES_PER_EU)))
 split_kv_partial(const int32_t* lens, const uint16_t* kc, const uint16_t* vc, const uint16_t* qp, int S_max,
-                 int chunk, int Hkv, int g_magic, const PartialParams p) {
+                 int chunk, int Hkv, int g_magic, int G, int tok_add, const PartialParams p) {
     constexpr int LPK = D / 8;              // lanes per key row
     constexpr int KPL = 64 / LPK;           // keys per wave-wide load
     constexpr int NSTEP = kKeysPerWave / KPL;
@@ -196,8 +204,15 @@ split_kv_partial(const int32_t* lens, const uint16_t* kc, const uint16_t* vc, co
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int kw = wave & (p.nwk - 1);      // nwk is a power of two
-    const int rgl = wave >> __builtin_ctz(p.nwk);
+    // the shape, from preloaded arguments only: tok_add = T for a causal chunk
+    // of T tokens, 0 for a decode call (T = 1)
+    const int T = tok_add > 0 ? tok_add : 1;
+    const int RT = T * G;                   // rows per kv head
+    const int Hq = G * Hkv;
+    const bool causal = tok_add != 0;
+    const int nwk = key_waves_for(chunk);   // a power of two
+    const int kw = wave & (nwk - 1);
+    const int rgl = wave >> __builtin_ctz(nwk);
     const int kk = lane / LPK;              // key slot inside one load
     const int db = lane % LPK;              // 8-dim block of this lane
     const int own = db >> SET_BITS;         // the row this lane completes
@@ -206,8 +221,8 @@ split_kv_partial(const int32_t* lens, const uint16_t* kc, const uint16_t* vc, co
 
     // ---- lengths into LDS; count the tiles that hold attended keys
     float* s_acc = smem;                                    // [rgb][nwk][R][D]
-    float* s_ml = smem + (size_t)p.rg_per_block * p.nwk * R * D;   // [rgb][nwk][R][2]
-    int* s_len = reinterpret_cast<int*>(s_ml + (size_t)p.rg_per_block * p.nwk * R * 2);   // [B]
+    float* s_ml = smem + (size_t)p.rg_per_block * nwk * R * D;   // [rgb][nwk][R][2]
+    int* s_len = reinterpret_cast<int*>(s_ml + (size_t)p.rg_per_block * nwk * R * 2);   // [B]
     const int per_tile = Hkv * p.n_row_blocks;              // work items per (b, tile)
     int n_items = 0;
     if constexpr (!ONE_ROUND) {
@@ -215,7 +230,7 @@ split_kv_partial(const int32_t* lens, const uint16_t* kc, const uint16_t* vc, co
         for (int i = tid; i < p.B; i += blockDim.x) {
             const int len = lens[i];
             s_len[i] = len;
-            const int lim = clamp_len_add(len, p.causal ? p.T : 0, S_max);
+            const int lim = clamp_len_add(len, tok_add, S_max);
             my_tiles += (lim + chunk - 1) >> __builtin_ctz(chunk);   // chunk is a power of two
         }
         my_tiles = wave_sum_i(my_tiles);
@@ -233,7 +248,7 @@ split_kv_partial(const int32_t* lens, const uint16_t* kc, const uint16_t* vc, co
     int b_cur = 0, pre_cur = 0;
     auto tiles_of = [&](int b) {
         const int len = s_len[b];
-        return (clamp_len_add(len, p.causal ? p.T : 0, S_max) + chunk - 1) >> __builtin_ctz(chunk);
+        return (clamp_len_add(len, tok_add, S_max) + chunk - 1) >> __builtin_ctz(chunk);
     };
 
     struct Tile {
@@ -255,7 +270,7 @@ split_kv_partial(const int32_t* lens, const uint16_t* kc, const uint16_t* vc, co
         tl.len = s_len[b_cur];
         tl.t0 = tl.c * chunk;
         tl.t1 = min(tl.t0 + chunk, S_max);
-        tl.lim_all = min(clamp_len_add(tl.len, p.causal ? p.T : 0, S_max), tl.t1);
+        tl.lim_all = min(clamp_len_add(tl.len, tok_add, S_max), tl.t1);
         return tl;
     };
 
@@ -271,17 +286,17 @@ split_kv_partial(const int32_t* lens, const uint16_t* kc, const uint16_t* vc, co
 #pragma unroll
         for (int j = 0; j < RP; ++j) {
             const int r0 = rg * R + j;
-            const bool ok = j < R && r0 < p.RT;
+            const bool ok = j < R && r0 < RT;
             const int r = ok ? r0 : 0;
             const int i = (r * g_magic) >> 16;      // r / G
-            const int h = tl.kvh * p.G + (r - i * p.G);
-            if (j == own && ok) my_lim = min(clamp_len_add(tl.len, p.causal ? i + 1 : 0, S_max), tl.t1);
-            qraw[j] = *reinterpret_cast<const uint4*>(qp + ((size_t)(tl.b * p.T + i) * p.Hq + h) * D + db * 8);
+            const int h = tl.kvh * G + (r - i * G);
+            if (j == own && ok) my_lim = min(clamp_len_add(tl.len, causal ? i + 1 : 0, S_max), tl.t1);
+            qraw[j] = *reinterpret_cast<const uint4*>(qp + ((size_t)(tl.b * T + i) * Hq + h) * D + db * 8);
         }
     };
 
     const uint32_t lane_off = (uint32_t)(kk * D + db * 8) * 2;
-    const int sub_stride = p.nwk * kKeysPerWave;
+    const int sub_stride = nwk * kKeysPerWave;
     const float qs = p.qscale;
 
     // K/V of a tile's (b, kvh): rows [0, lim_all) are in range, the rest read as 0
@@ -392,7 +407,7 @@ split_kv_partial(const int32_t* lens, const uint16_t* kc, const uint16_t* vc, co
         float red[RP * 2];
         across_groups_sum_scatter<LPK>(flat, red);
 
-        const int slot = (rgl * p.nwk + kw) * R;
+        const int slot = (rgl * nwk + kw) * R;
         const int q = lane >> 4;
         if (LPK == 16 || (kk & 1) == 0) {
 #pragma unroll
@@ -414,15 +429,15 @@ split_kv_partial(const int32_t* lens, const uint16_t* kc, const uint16_t* vc, co
         // four dims per thread, the key waves folded in a fixed order
         constexpr int Q4 = D / 4;
         const int total = p.rg_per_block * R * Q4;
-        const size_t tile_row0 = ((size_t)(tl.b * Hkv + tl.kvh) * p.NC + tl.c) * p.RT;
+        const size_t tile_row0 = ((size_t)(tl.b * Hkv + tl.kvh) * p.NC + tl.c) * RT;
         for (int idx = tid; idx < total; idx += blockDim.x) {
             const int rg2 = idx / (R * Q4);
             const int rem = idx - rg2 * (R * Q4);
             const int jr = rem / Q4;
             const int d = (rem - jr * Q4) * 4;
             const int r = (tl.rblk * p.rg_per_block + rg2) * R + jr;
-            if (r >= p.RT) continue;
-            const int base_slot = rg2 * p.nwk * R + jr;     // slot of key wave 0 for this row
+            if (r >= RT) continue;
+            const int base_slot = rg2 * nwk * R + jr;     // slot of key wave 0 for this row
             // all key waves' state read at once: waves w >= nwk read wave
             // nwk - 1's slot again (same maximum) and get weight 0, which adds
             // exactly nothing, so the sums are those of the nwk waves in order
@@ -430,7 +445,7 @@ split_kv_partial(const int32_t* lens, const uint16_t* kc, const uint16_t* vc, co
             float4 aw[kMaxKeyWaves];
 #pragma unroll
             for (int w = 0; w < kMaxKeyWaves; ++w) {
-                const int sl = base_slot + min(w, p.nwk - 1) * R;
+                const int sl = base_slot + min(w, nwk - 1) * R;
                 const float2 ml = *reinterpret_cast<const float2*>(s_ml + sl * 2);
                 mw[w] = ml.x;
                 lw[w] = ml.y;
@@ -445,7 +460,7 @@ split_kv_partial(const int32_t* lens, const uint16_t* kc, const uint16_t* vc, co
             float L = 0.f;
 #pragma unroll
             for (int w = 0; w < kMaxKeyWaves; ++w) {
-                const float wt = w < p.nwk ? fast_exp2(mw[w] - Mu) : 0.f;
+                const float wt = w < nwk ? fast_exp2(mw[w] - Mu) : 0.f;
                 A.x = __builtin_fmaf(wt, aw[w].x, A.x);
                 A.y = __builtin_fmaf(wt, aw[w].y, A.y);
                 A.z = __builtin_fmaf(wt, aw[w].z, A.z);
@@ -481,7 +496,8 @@ split_kv_partial(const int32_t* lens, const uint16_t* kc, const uint16_t* vc, co
         tl.rblk = 0;
         tl.t0 = tl.c * chunk;
         tl.t1 = min(tl.t0 + chunk, S_max);
-        const int len = lens[tl.b];
+        int len = lens[tl.b];
+        asm volatile("" ::: "memory");      // the length's load leaves first
         const int spt_real = (chunk + sub_stride - 1) / sub_stride;
         const int spt = (spt_real + kNumBuf - 1) / kNumBuf * kNumBuf;
         uint4 qc[RP];
@@ -499,15 +515,19 @@ split_kv_partial(const int32_t* lens, const uint16_t* kc, const uint16_t* vc, co
         };
 #pragma unroll
         for (int u = 0; u < kNumBuf; ++u) load(rs, kb[u], vb[u], slot_base(u, tl.t1));
+        // keep those loads ahead of the length's first use: the length passes
+        // through here, so nothing computed from it (the exit test for a tile
+        // past the length, and the wait for its round trip) moves above them
+        asm volatile("" : "+s"(len) : : "memory");
 
         tl.len = len;
-        tl.lim_all = min(clamp_len_add(len, p.causal ? p.T : 0, S_max), tl.t1);
+        tl.lim_all = min(clamp_len_add(len, tok_add, S_max), tl.t1);
         if (tl.t0 >= tl.lim_all) return;    // workgroup-uniform: a tile past the length
         {
             const int rg = tl.rblk * p.rg_per_block + rgl;
             const int r0 = rg * R + own;
-            const int i = ((r0 < p.RT ? r0 : 0) * g_magic) >> 16;   // r0 / G
-            limc = (own < R && r0 < p.RT) ? min(clamp_len_add(len, p.causal ? i + 1 : 0, S_max), tl.t1) : 0;
+            const int i = ((r0 < RT ? r0 : 0) * g_magic) >> 16;   // r0 / G
+            limc = (own < R && r0 < RT) ? min(clamp_len_add(len, causal ? i + 1 : 0, S_max), tl.t1) : 0;
         }
         rs = make_tile_rsrc(tl);
         reset_state();
