@@ -317,9 +317,8 @@ int run_partial(const Plan& pl, const void* q, const void* k, const void* v, con
     pp.lens = lens;
     pp.ws_ml = static_cast<float*>(ws);
     pp.ws_acc = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.ml_bytes);
-    pp.T = pl.T; pp.Hq = pl.Hq; pp.Hkv = pl.Hkv; pp.G = pl.G; pp.S_max = pl.S_max;
-    pp.chunk = pl.chunk; pp.NC = pl.NC; pp.RT = pl.RT; pp.causal = causal;
-    pp.nwk = pl.nwk; pp.rg_per_block = pl.rg_per_block; pp.n_row_blocks = pl.n_row_blocks;
+    pp.NC = pl.NC; pp.causal = causal;
+    pp.rg_per_block = pl.rg_per_block; pp.n_row_blocks = pl.n_row_blocks;
     pp.B = pl.B;
     pp.lds_main = (int)pl.mfma_lds_main;
     pp.qscale = log2_scale(scale);

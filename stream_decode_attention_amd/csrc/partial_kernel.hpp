@@ -83,15 +83,19 @@ __host__ __device__ constexpr int key_waves_for(int chunk) {
 }
 static_assert(kNumBuf >= 2, "the load pointer must run ahead of the compute pointer");
 
+// What the partial kernels read after their first loads (the pointers and
+// shapes those loads need come as leading scalar arguments, preloaded into
+// SGPRs). The host also carries the inputs and the causal flag here, which
+// it passes on as leading arguments.
 struct PartialParams {
-    const uint16_t* q;      // bf16 [B][T][Hq][D]
-    const uint16_t* k;      // bf16 [B][Hkv][S_max][D]
-    const uint16_t* v;
-    const int32_t* lens;    // [B]: seq_lens (decode) or ctx_lens (causal)
+    const uint16_t* q;      // bf16 [B][T][Hq][D]            (host side)
+    const uint16_t* k;      // bf16 [B][Hkv][S_max][D]       (host side)
+    const uint16_t* v;      //                                (host side)
+    const int32_t* lens;    // [B]: seq_lens (decode) or ctx_lens (causal)   (host side)
     float* ws_ml;           // [B][Hkv][NC][RT][2]  (m in log2 units, l)
     float* ws_acc;          // [B][Hkv][NC][RT][D]
-    int T, Hq, Hkv, G, S_max, chunk, NC, RT, causal;
-    int nwk;                // key waves per workgroup
+    int NC;                 // tiles per row (slots in the workspace)
+    int causal;             // (host side) 1: causal chunk, 0: decode
     int rg_per_block;       // row groups per workgroup
     int n_row_blocks;       // workgroups per tile along the row axis
     float qscale;           // scale * log2(e); magnitude at least FLT_MIN, sign of scale
