@@ -198,7 +198,6 @@ template <int D, int R>
 hipError_t launch_partial_dr(const Plan& pl, const PartialParams& pp, hipStream_t s) {
     const int threads = 64 * pl.nwk * pl.rg_per_block;
     const long long items = (long long)pl.B * pl.Hkv * pl.n_row_blocks * pl.NC;   // every possible tile
-    const int g_magic = (65536 + pl.G - 1) / pl.G;     // r / G = (r * g_magic) >> 16 for r < 8192
     const int tok_add = pp.causal ? pl.T : 0;          // keys past the context a causal chunk adds (T = 1 if 0)
     // one workgroup per possible work item when they all fit on the device at
     // once: each knows its tile from its index (grid NC x Hkv x B, one row
@@ -214,7 +213,7 @@ hipError_t launch_partial_dr(const Plan& pl, const PartialParams& pp, hipStream_
     if (items <= res1 && pl.n_row_blocks == 1 && pl.chunk <= kNumBuf * pl.nwk * kKeysPerWave) {
         hipLaunchKernelGGL((split_kv_partial<D, R, true>), dim3((unsigned)pl.NC, (unsigned)pl.Hkv, (unsigned)pl.B),
                            dim3(threads), pl.lds_bytes, s, pp.lens, pp.k, pp.v, pp.q, pl.S_max, pl.chunk, pl.Hkv,
-                           g_magic, pl.G, tok_add, pp);
+                           g_magic_for(pl.G), pl.G, tok_add, pp);
         return hipGetLastError();
     }
     // persistent: one wave of resident workgroups walks all attended tiles
@@ -223,14 +222,14 @@ hipError_t launch_partial_dr(const Plan& pl, const PartialParams& pp, hipStream_
     if (grid <= 0) return hipErrorInvalidDeviceFunction;
     if (grid > items) grid = items;
     hipLaunchKernelGGL((split_kv_partial<D, R, false>), dim3((unsigned)grid), dim3(threads), pl.lds_bytes, s, pp.lens,
-                       pp.k, pp.v, pp.q, pl.S_max, pl.chunk, pl.Hkv, g_magic, pl.G, tok_add, pp);
+                       pp.k, pp.v, pp.q, pl.S_max, pl.chunk, pl.Hkv, pl.B, pl.G, tok_add, pp);
     return hipGetLastError();
 }
 
 template <int D, int KB>
 hipError_t launch_verify_dk(const Plan& pl, const PartialParams& pp, hipStream_t s) {
     const long long items = (long long)pl.B * pl.Hkv * pl.NC;   // every possible tile
-    const int g_magic = (65536 + pl.G - 1) / pl.G;     // r / G = (r * g_magic) >> 16 for r < 8192
+    const int g_magic = g_magic_for(pl.G);             // r / G = (r * g_magic) >> 16 for r < 8192
     const int tok_add = pp.causal ? pl.T : 0;          // keys past the context a causal chunk adds (T = 1 if 0)
     // one workgroup per possible tile when they all fit on the device at once
     // (grid NC x Hkv x B; tiles past the length exit at once): no lengths

@@ -83,6 +83,13 @@ __host__ __device__ constexpr int key_waves_for(int chunk) {
 }
 static_assert(kNumBuf >= 2, "the load pointer must run ahead of the compute pointer");
 
+// ceil(2^16 / G) for 1 <= G <= 8: r / G = (r * g_magic) >> 16 exactly for
+// every r < 8192 (a select chain, no division)
+__host__ __device__ constexpr int g_magic_for(int G) {
+    return G <= 4 ? (G <= 2 ? (G == 1 ? 65536 : 32768) : (G == 3 ? 21846 : 16384))
+                  : (G <= 6 ? (G == 5 ? 13108 : 10923) : (G == 7 ? 9363 : 8192));
+}
+
 // What the partial kernels read after their first loads (the pointers and
 // shapes those loads need come as leading scalar arguments, preloaded into
 // SGPRs). The host also carries the inputs and the causal flag here, which
@@ -182,17 +189,20 @@ __device__ __forceinline__ void gather_all_i(int x, int (&out)[8]) {
 // first K/V loads are written over the whole tile (keys up to t1 lie inside
 // the cache) so that they need no length; keys past the length are masked by
 // select (scores to -inf, V to 0), never by a multiply, since stale slots may
-// hold any bits. (The compiler still waits for the length before issuing
-// them. Forcing them ahead of it saved about 0.1 us per call at full length
-// and cost more when most tiles lie past the length, whose loads then fetch
-// data for nothing.)
+// hold any bits. The length's load leaves first and the length is not used
+// before those loads are issued.
 // The pointers and shapes the first loads depend on are leading scalar
-// arguments (preloaded into SGPRs at wave launch); g_magic = ceil(2^16 / G)
-// gives r / G = (r * g_magic) >> 16 exactly for every row index r < 8192.
+// arguments (preloaded into SGPRs at wave launch): lens, K, V, q, S_max,
+// chunk, Hkv, gm_or_B, G, and tok_add (T for a causal chunk of T tokens, 0
+// for a decode call, whose T is 1). gm_or_B is g_magic = ceil(2^16 / G) for
+// the one-round launch (row / G as a multiply-shift before its first loads;
+// it never needs the batch size) and the batch size B for the persistent walk
+// (which stages every length first and derives g_magic from G off that path):
+// the 14 dwords are all that the hardware preloads.
 template <int D, int R, bool ONE_ROUND>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(DECATTN_WAVES_PER_EU)))
 split_kv_partial(const int32_t* lens, const uint16_t* kc, const uint16_t* vc, const uint16_t* qp, int S_max,
-                 int chunk, int Hkv, int g_magic, int G, int tok_add, const PartialParams p) {
+                 int chunk, int Hkv, int gm_or_B, int G, int tok_add, const PartialParams p) {
     constexpr int LPK = D / 8;              // lanes per key row
     constexpr int KPL = 64 / LPK;           // keys per wave-wide load
     constexpr int NSTEP = kKeysPerWave / KPL;
@@ -214,6 +224,8 @@ split_kv_partial(const int32_t* lens, const uint16_t* kc, const uint16_t* vc, co
     const int RT = T * G;                   // rows per kv head
     const int Hq = G * Hkv;
     const bool causal = tok_add != 0;
+    const int g_magic = ONE_ROUND ? gm_or_B : g_magic_for(G);   // r / G = (r * g_magic) >> 16
+    const int B = ONE_ROUND ? 0 : gm_or_B;  // batch rows (persistent walk only)
     const int nwk = key_waves_for(chunk);   // a power of two
     const int kw = wave & (nwk - 1);
     const int rgl = wave >> __builtin_ctz(nwk);
@@ -231,12 +243,19 @@ split_kv_partial(const int32_t* lens, const uint16_t* kc, const uint16_t* vc, co
     int n_items = 0;
     if constexpr (!ONE_ROUND) {
         int my_tiles = 0;
-        for (int i = tid; i < p.B; i += blockDim.x) {
-            const int len = lens[i];
+        auto count_len = [&](int i, int len) {
             s_len[i] = len;
             const int lim = clamp_len_add(len, tok_add, S_max);
             my_tiles += (lim + chunk - 1) >> __builtin_ctz(chunk);   // chunk is a power of two
-        }
+        };
+        // Each thread's first length is loaded before anything waits (B is
+        // preloaded); the fields of p and the workgroup size the walk needs
+        // are used right after it, so their scalar loads return under the
+        // length's round trip instead of one after another ahead of it.
+        const int len0 = tid < B ? lens[tid] : 0;
+        asm volatile("" :: "s"(p.rg_per_block), "s"(p.n_row_blocks), "s"((int)blockDim.x));
+        if (tid < B) count_len(tid, len0);
+        for (int i = tid + (int)blockDim.x; i < B; i += blockDim.x) count_len(i, lens[i]);
         my_tiles = wave_sum_i(my_tiles);
         if (lane == 0) s_count[wave] = my_tiles;
         __syncthreads();
