@@ -83,6 +83,8 @@ SHAPES = [
     (8, 1600, 960),       # SmolLM2-360M q/k/v at B = 8: 15 blocks over 8 waves
     (1, 16383, 256),      # one row short of the matrix cores at B = 1 (bf16)
     (1, 16390, 200),      # the matrix cores at B = 1: ragged rows, a partial block
+    (1, 2047, 2048),      # few long rows (64 lanes each), an odd row count
+    (1, 4095, 14336),     # Llama-3-8B down-projection width at B = 1: two rounds of loads per row
 ]
 
 
@@ -137,7 +139,8 @@ def _codes(shape, seed):
                                    (2, 77, 976), (4, 960, 2560), (8, 77, 1024), (8, 64, 14336), (2, 3, 16),
                                    (3, 77, 976), (5, 3, 16), (8, 33, 208),
                                    (3, 8200, 208), (8, 8193, 16),    # two 16-row tiles per workgroup from N = 8192
-                                   (8, 1600, 960)])                  # 7.5 blocks of 128 k over 8 waves
+                                   (8, 1600, 960),                   # 7.5 blocks of 128 k over 8 waves
+                                   (1, 1001, 4096), (1, 4095, 14336)])   # few long rows, odd counts
 def test_gemv_int8_integer_data_is_exact(B, N, K):
     q = _codes((N, K), 730 + K)
     s = (2.0 ** np.random.default_rng(731).integers(-8, 1, size=N)).astype(np.float32)
