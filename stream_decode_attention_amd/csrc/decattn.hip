@@ -11,6 +11,7 @@
 #include <cstdint>
 #include <cstring>
 #include <mutex>
+#include <type_traits>
 #include <utility>
 #include <vector>
 
@@ -334,12 +335,25 @@ int run_merge(const Plan& pl, const int32_t* lens, int causal, void* out, int ou
     mp.out_bf16 = out_dtype == DECATTN_OUT_BF16;
     mp.T = pl.T; mp.S_max = pl.S_max; mp.chunk = pl.chunk; mp.causal = causal;
     const dim3 grid(pl.Hq, pl.T, pl.B);
-    if (pl.D == 64)
-        hipLaunchKernelGGL(lse_merge<64>, grid, dim3(merge_threads(64)), 0, s, ws_ml, ws_acc, lens, pl.G, pl.Hkv, pl.NC,
-                           pl.RT, mp);
-    else
-        hipLaunchKernelGGL(lse_merge<128>, grid, dim3(merge_threads(128)), 0, s, ws_ml, ws_acc, lens, pl.G, pl.Hkv, pl.NC,
-                           pl.RT, mp);
+    // slots of the merge's first batch: ceil(NC / 8) tile lanes' worth,
+    // rounded up to a power of two, at most kMergeUnroll
+    const int need = (pl.NC + 7) / 8;
+    const int nu0 = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
+    auto launch = [&](auto d_tag, auto nu_tag) {
+        constexpr int DD = decltype(d_tag)::value, NU = decltype(nu_tag)::value;
+        hipLaunchKernelGGL((lse_merge<DD, NU>), grid, dim3(merge_threads(DD)), 0, s, ws_ml, ws_acc, lens, pl.G, pl.Hkv,
+                           pl.NC, pl.RT, mp);
+    };
+    auto by_nu = [&](auto d_tag) {
+        switch (nu0) {
+            case 1: launch(d_tag, std::integral_constant<int, 1>{}); break;
+            case 2: launch(d_tag, std::integral_constant<int, 2>{}); break;
+            case 4: launch(d_tag, std::integral_constant<int, 4>{}); break;
+            default: launch(d_tag, std::integral_constant<int, 8>{}); break;
+        }
+    };
+    if (pl.D == 64) by_nu(std::integral_constant<int, 64>{});
+    else by_nu(std::integral_constant<int, 128>{});
     return hipGetLastError() == hipSuccess ? DECATTN_OK : DECATTN_ERR_HIP;
 }
 

@@ -45,8 +45,11 @@ __host__ __device__ constexpr int merge_threads(int D) { return 2 * D; }
 constexpr int kMergeUnroll = 8;
 
 // ws_ml [B][Hkv][NC][RT][2], ws_acc [B][Hkv][NC][RT][D], lens [B]; one
-// workgroup per output row, grid (Hq, T, B).
-template <int D>
+// workgroup per output row, grid (Hq, T, B). NU0: slots of the first batch,
+// ceil(NC / 8) rounded up to 1, 2, 4 or 8 by the host (a slot past every
+// row's tiles loads a clamped duplicate that the select drops), so that the
+// first batch is straight-line code.
+template <int D, int NU0>
 __global__ void __launch_bounds__(merge_threads(D))
 lse_merge(const float* ws_ml_, const float* ws_acc_, const int32_t* lens, int G, int Hkv, int NC, int RT,
           const MergeParams p) {
@@ -93,7 +96,8 @@ lse_merge(const float* ws_ml_, const float* ws_acc_, const int32_t* lens, int G,
     };
     // the first batch: only slots that can hold a tile of the workspace (a
     // slot u past ceil(NC / NCL) lies past every row's tiles)
-    fetch(cl, min(kMergeUnroll, (NC + NCL - 1) / NCL));
+    static_assert(NU0 >= 1 && NU0 <= kMergeUnroll, "first-batch slots");
+    fetch(cl, NU0);
     // keep those loads ahead of the length's: without this the compiler
     // moves the exit test for an empty row (and the length's round trip)
     // above them
