@@ -29,7 +29,7 @@
  *    check returns a status and launches nothing. Device-resident lengths are
  *    not validated (that would need a host sync): the kernels clamp them to
  *    [0, S_max], and a row with no keys outputs zeros.
- *  - Supported: D in {64, 128}; G = Hq / Hkv in 1..8; T in 1..16; chunk 0
+ *  - Supported: D in {64, 128}; G = Hq / Hkv in 1..8; Hq <= 2^24; T in 1..16; chunk 0
  *    (library default) or a power of two in [16, 2^20] (a chunk >= S_max
  *    means one tile per row); B <= 4096; one kv head's cache, plus 512 keys
  *    of slack, within a 32-bit byte range: (S_max + 512) * D * 2 < 2^32, i.e.

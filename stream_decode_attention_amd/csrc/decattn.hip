@@ -33,6 +33,7 @@ namespace {
 
 constexpr int kMaxG = 8;
 constexpr int kMaxT = 16;
+constexpr int kMaxHq = 1 << 24;            // the merge divides head indices by G with a 32-bit multiply-high
 constexpr int kMaxB = 4096;                // lengths are staged in LDS
 constexpr int kMaxRowsPerWave = 8;
 constexpr int kMaxWavesPerBlock = 8;       // matches __launch_bounds__(512)
@@ -112,7 +113,7 @@ int make_plan(int B, int T, int Hq, int Hkv, int D, int S_max, int chunk, Plan* 
     if (Hq % Hkv != 0) return DECATTN_ERR_INVALID_ARG;
     if (D != 64 && D != 128) return DECATTN_ERR_UNSUPPORTED;
     const int G = Hq / Hkv;
-    if (G > kMaxG || T > kMaxT) return DECATTN_ERR_UNSUPPORTED;
+    if (G > kMaxG || T > kMaxT || Hq > kMaxHq) return DECATTN_ERR_UNSUPPORTED;
     if (chunk == 0) chunk = pick_default_chunk(B, T, G, Hkv, D, S_max);
     // a chunk >= S_max gives one tile per row
     if (chunk < kMinChunk || chunk > kMaxChunk || !is_pow2(chunk)) return DECATTN_ERR_UNSUPPORTED;
@@ -337,12 +338,14 @@ int run_merge(const Plan& pl, const int32_t* lens, int causal, void* out, int ou
     const dim3 grid(pl.Hq, pl.T, pl.B);
     // slots of the merge's first batch: ceil(NC / 8) tile lanes' worth,
     // rounded up to a power of two, at most kMergeUnroll
+    // ceil(2^32 / G) (G >= 2; unused at G = 1): h / G = mulhi(h, g_recip) for h < 2^28
+    const uint32_t g_recip = pl.G == 1 ? 0u : (uint32_t)(((1ull << 32) + pl.G - 1) / pl.G);
     const int need = (pl.NC + 7) / 8;
     const int nu0 = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
     auto launch = [&](auto d_tag, auto nu_tag) {
         constexpr int DD = decltype(d_tag)::value, NU = decltype(nu_tag)::value;
         hipLaunchKernelGGL((lse_merge<DD, NU>), grid, dim3(merge_threads(DD)), 0, s, ws_ml, ws_acc, lens, pl.G, pl.Hkv,
-                           pl.NC, pl.RT, mp);
+                           pl.NC, pl.RT, g_recip, mp);
     };
     auto by_nu = [&](auto d_tag) {
         switch (nu0) {

@@ -52,7 +52,7 @@ constexpr int kMergeUnroll = 8;
 template <int D, int NU0>
 __global__ void __launch_bounds__(merge_threads(D))
 lse_merge(const float* ws_ml_, const float* ws_acc_, const int32_t* lens, int G, int Hkv, int NC, int RT,
-          const MergeParams p) {
+          uint32_t g_recip, const MergeParams p) {
     constexpr int QPR = D / 4;                    // float4 quads per row
     constexpr int kMergeThreads = merge_threads(D);
     constexpr int NCL = kMergeThreads / QPR;      // tile lanes working in parallel
@@ -61,7 +61,9 @@ lse_merge(const float* ws_ml_, const float* ws_acc_, const int32_t* lens, int G,
     __shared__ float s_l[kMergeThreads / 64];
 
     const int h = blockIdx.x, i = blockIdx.y, b = blockIdx.z;
-    const int kvh = h / G;
+    // h / G as a multiply-high by g_recip = ceil(2^32 / G) (exact for
+    // h < 2^28, G <= 8); for G = 1 the host passes 0 and the select adds h
+    const int kvh = (int)__umulhi((uint32_t)h, g_recip) + (g_recip == 0u ? h : 0);
     const int r = i * G + (h - kvh * G);
 
     const size_t head0 = (size_t)(b * Hkv + kvh) * NC * RT;   // tile 0, row 0

@@ -521,7 +521,7 @@ split_kv_partial(const int32_t* lens, const uint16_t* kc, const uint16_t* vc, co
         tl.t1 = min(tl.t0 + chunk, S_max);
         int len = lens[tl.b];
         asm volatile("" ::: "memory");      // the length's load leaves first
-        const int spt_real = (chunk + sub_stride - 1) / sub_stride;
+        const int spt_real = (chunk + sub_stride - 1) >> __builtin_ctz(sub_stride);   // both powers of two
         const int spt = (spt_real + kNumBuf - 1) / kNumBuf * kNumBuf;
         uint4 qc[RP];
         int limc;
@@ -571,7 +571,7 @@ split_kv_partial(const int32_t* lens, const uint16_t* kc, const uint16_t* vc, co
     int c_item = blockIdx.x;
     if (c_item >= n_items) return;          // workgroup-uniform
     const int P = (int)gridDim.x;
-    const int spt_real = (chunk + sub_stride - 1) / sub_stride;
+    const int spt_real = (chunk + sub_stride - 1) >> __builtin_ctz(sub_stride);   // both powers of two
     const int spt = (spt_real + kNumBuf - 1) / kNumBuf * kNumBuf;
 
     uint4 kb[kNumBuf][NSTEP], vb[kNumBuf][NSTEP];

@@ -310,3 +310,11 @@ def test_binding_rejects_host_tensors_before_calling_the_library():
     ws = torch.zeros((4096,), dtype=torch.uint8)
     with pytest.raises(ValueError, match="device tensor"):
         sda.decode_attn(q, kv, kv, lens, 0.125, q.clone(), ws)
+
+
+def test_query_head_count_limit(lib):
+    """Hq up to 2^24 is accepted (the merge divides head indices by G with a
+    32-bit multiply-high, exact below 2^28); one group more is refused."""
+    assert sda.workspace_bytes(1, 1, 1 << 24, 1 << 21, 64, 16, 16) > 0
+    assert sda.workspace_bytes(1, 1, (1 << 24) + 8, ((1 << 24) + 8) // 8, 64, 16, 16) == 0
+    assert sda.default_chunk(1, 1, (1 << 24) + 8, ((1 << 24) + 8) // 8, 64, 16) == 0
