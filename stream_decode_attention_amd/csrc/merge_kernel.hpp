@@ -21,6 +21,8 @@
 // scheduling.
 #pragma once
 
+#include <type_traits>
+
 #include "device_common.hpp"
 
 namespace decattn {
@@ -122,10 +124,11 @@ lse_merge(const float* ws_ml_, const float* ws_acc_, const int32_t* lens, int G,
 
     float m_t = kNegInf, l_t = 0.f;
     float4 a_t = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int c0 = cl; c0 < na; c0 += NCL * kMergeUnroll) {
-        if (c0 != cl) fetch(c0, kMergeUnroll);
+    // fold slots u < NU of the batch at c0 into (m_t, l_t, a_t)
+    auto fold = [&](int c0, auto nu_tag) {
+        constexpr int NU = decltype(nu_tag)::value;
 #pragma unroll
-        for (int u = 0; u < kMergeUnroll; ++u) {
+        for (int u = 0; u < NU; ++u) {
             if (c0 + u * NCL >= na) {       // not this row's tile: drop (select, no arithmetic)
                 mv[u] = kNegInf;
                 lv[u] = 0.f;
@@ -134,7 +137,7 @@ lse_merge(const float* ws_ml_, const float* ws_acc_, const int32_t* lens, int G,
         }
         float mb = mv[0];
 #pragma unroll
-        for (int u = 1; u < kMergeUnroll; ++u) mb = fmaxf(mb, mv[u]);
+        for (int u = 1; u < NU; ++u) mb = fmaxf(mb, mv[u]);
         // An empty tile state (m = -inf, l = 0, acc = 0) adds nothing: while this
         // lane has seen only such tiles its maximum stays -inf and the weights
         // are taken against 0, which makes them all 0 (never 2^(-inf + inf)).
@@ -144,7 +147,7 @@ lse_merge(const float* ws_ml_, const float* ws_acc_, const int32_t* lens, int G,
         l_t *= sc;
         a_t.x *= sc; a_t.y *= sc; a_t.z *= sc; a_t.w *= sc;
 #pragma unroll
-        for (int u = 0; u < kMergeUnroll; ++u) {
+        for (int u = 0; u < NU; ++u) {
             const float wt = fast_exp2(mv[u] - m_use);
             l_t = __builtin_fmaf(wt, lv[u], l_t);
             a_t.x = __builtin_fmaf(wt, av[u].x, a_t.x);
@@ -153,6 +156,15 @@ lse_merge(const float* ws_ml_, const float* ws_acc_, const int32_t* lens, int G,
             a_t.w = __builtin_fmaf(wt, av[u].w, a_t.w);
         }
         m_t = m_new;
+    };
+    if constexpr (NU0 < kMergeUnroll) {
+        // NU0 * NCL slots cover the workspace's NC tiles: one batch, NU0 slots
+        fold(cl, std::integral_constant<int, NU0>{});
+    } else {
+        for (int c0 = cl; c0 < na; c0 += NCL * kMergeUnroll) {
+            if (c0 != cl) fetch(c0, kMergeUnroll);
+            fold(c0, std::integral_constant<int, kMergeUnroll>{});
+        }
     }
     // Tile lanes of one wave (4 at D = 64 in its 16-lane rows, 2 at D = 128 in
     // its halves) are joined with lane swaps, in the same order for every
