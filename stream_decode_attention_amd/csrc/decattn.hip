@@ -344,10 +344,17 @@ int run_merge(const Plan& pl, const int32_t* lens, int causal, void* out, int ou
     const int nu0 = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
     auto launch = [&](auto d_tag, auto nu_tag) {
         constexpr int DD = decltype(d_tag)::value, NU = decltype(nu_tag)::value;
-        hipLaunchKernelGGL((lse_merge<DD, NU>), grid, dim3(merge_threads(DD)), 0, s, ws_ml, ws_acc, lens, pl.G, pl.Hkv,
-                           pl.NC, pl.RT, g_recip, mp);
+        hipLaunchKernelGGL((lse_merge<DD, NU, merge_threads(DD) / 64>), grid, dim3(merge_threads(DD)), 0, s, ws_ml,
+                           ws_acc, lens, pl.G, pl.Hkv, pl.NC, pl.RT, g_recip, mp);
     };
     auto by_nu = [&](auto d_tag) {
+        constexpr int DD = decltype(d_tag)::value;
+        if (pl.NC * (DD / 4) <= 64) {
+            // one wave's tile lanes hold every tile slot: one wave per row
+            hipLaunchKernelGGL((lse_merge<DD, 1, 1>), grid, dim3(64), 0, s, ws_ml, ws_acc, lens, pl.G, pl.Hkv,
+                               pl.NC, pl.RT, g_recip, mp);
+            return;
+        }
         switch (nu0) {
             case 1: launch(d_tag, std::integral_constant<int, 1>{}); break;
             case 2: launch(d_tag, std::integral_constant<int, 2>{}); break;

@@ -50,13 +50,15 @@ constexpr int kMergeUnroll = 8;
 // workgroup per output row, grid (Hq, T, B). NU0: slots of the first batch,
 // ceil(NC / 8) rounded up to 1, 2, 4 or 8 by the host (a slot past every
 // row's tiles loads a clamped duplicate that the select drops), so that the
-// first batch is straight-line code.
-template <int D, int NU0>
-__global__ void __launch_bounds__(merge_threads(D))
+// first batch is straight-line code. NWT: waves per row, 2 * D / 64, or one
+// when one wave's tile lanes (64 / (D / 4)) hold every tile slot; it then
+// needs no join through LDS and no barrier.
+template <int D, int NU0, int NWT>
+__global__ void __launch_bounds__(64 * NWT)
 lse_merge(const float* ws_ml_, const float* ws_acc_, const int32_t* lens, int G, int Hkv, int NC, int RT,
           uint32_t g_recip, const MergeParams p) {
     constexpr int QPR = D / 4;                    // float4 quads per row
-    constexpr int kMergeThreads = merge_threads(D);
+    constexpr int kMergeThreads = 64 * NWT;
     constexpr int NCL = kMergeThreads / QPR;      // tile lanes working in parallel
     __shared__ float4 s_acc[kMergeThreads / 64][QPR];
     __shared__ float s_m[kMergeThreads / 64];
@@ -192,6 +194,24 @@ lse_merge(const float* ws_ml_, const float* ws_acc_, const int32_t* lens, int G,
     constexpr int NW = kMergeThreads / 64;
     const int wave = tid >> 6;
     const int lane = tid & 63;
+    if constexpr (NW == 1) {
+        // every lane holds the row's state: lanes < QPR store their 4 dims
+        if (tid < QPR) {
+            const float inv = 1.f / l_t;
+            const float o0 = a_t.x * inv, o1 = a_t.y * inv, o2 = a_t.z * inv, o3 = a_t.w * inv;
+            const size_t o = row * D + tid * 4;
+            if (p.out_bf16) {
+                uint16_t* ob = reinterpret_cast<uint16_t*>(p.out) + o;
+                const uint2 packed = make_uint2(
+                    (uint32_t)f32_to_bf16_rne(o0) | ((uint32_t)f32_to_bf16_rne(o1) << 16),
+                    (uint32_t)f32_to_bf16_rne(o2) | ((uint32_t)f32_to_bf16_rne(o3) << 16));
+                *reinterpret_cast<uint2*>(ob) = packed;
+            } else {
+                *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + o) = make_float4(o0, o1, o2, o3);
+            }
+        }
+        return;
+    }
     if (lane < QPR) {
         s_acc[wave][lane] = a_t;
         if (lane == 0) {
