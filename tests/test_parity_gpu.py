@@ -242,6 +242,19 @@ def test_tile_counts_around_one_merge_batch(D):
     assert_bf16_close(run_decode(c, chunk=16, out_dtype=torch.bfloat16), ref)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_one_wave_merge_with_an_empty_row(D):
+    """Two or four tile slots per row (S_max = 64, 32-key tiles at D = 128;
+    S_max = 128 at D = 64): the merge runs one wave per row, whose zero fill of
+    an empty row takes two passes at D = 128."""
+    S = 64 if D == 128 else 128
+    lens = [0, 1, 40, S]
+    c = workloads.make_case(len(lens), 6, 2, D, S, lens, seed=44 + D)
+    ref = oracle.decode_attention(c["q"], c["k"], c["v"], c["lens"], c["scale"])
+    out32, out16 = _both_modes(c, ref, chunk=32)
+    assert torch.count_nonzero(out32[0]) == 0 and torch.count_nonzero(out16[0].float()) == 0
+
+
 def test_largest_batch():
     """B = 4096 (the most lengths the kernels stage in LDS), lengths 0..16."""
     B = 4096
