@@ -202,7 +202,7 @@ hipError_t launch_partial_dr(const Plan& pl, const PartialParams& pp, hipStream_
     const long long items = (long long)pl.B * pl.Hkv * pl.n_row_blocks * pl.NC;   // every possible tile
     const int tok_add = pp.causal ? pl.T : 0;          // keys past the context a causal chunk adds (T = 1 if 0)
     // one workgroup per possible work item when they all fit on the device at
-    // once: each knows its tile from its index (grid NC x Hkv x B, one row
+    // once: each knows its tile from its index (grid Hkv x NC x B, one row
     // block) and reads only its own row's length (no staging, counting or
     // barrier; tiles past the length exit); measured 0.6-0.7 us faster per
     // call than the persistent walk on the single-sequence decode layers
@@ -213,7 +213,7 @@ hipError_t launch_partial_dr(const Plan& pl, const PartialParams& pp, hipStream_
     // measured on: a one-tile-per-row call on this loop ran 1.7x slower than
     // on the persistent walk)
     if (items <= res1 && pl.n_row_blocks == 1 && pl.chunk <= kNumBuf * pl.nwk * kKeysPerWave) {
-        hipLaunchKernelGGL((split_kv_partial<D, R, true>), dim3((unsigned)pl.NC, (unsigned)pl.Hkv, (unsigned)pl.B),
+        hipLaunchKernelGGL((split_kv_partial<D, R, true>), dim3((unsigned)pl.Hkv, (unsigned)pl.NC, (unsigned)pl.B),
                            dim3(threads), pl.lds_bytes, s, pp.lens, pp.k, pp.v, pp.q, pl.S_max, pl.chunk, pl.Hkv,
                            g_magic_for(pl.G), pl.G, tok_add, pp);
         return hipGetLastError();
@@ -234,7 +234,7 @@ hipError_t launch_verify_dk(const Plan& pl, const PartialParams& pp, hipStream_t
     const int g_magic = g_magic_for(pl.G);             // r / G = (r * g_magic) >> 16 for r < 8192
     const int tok_add = pp.causal ? pl.T : 0;          // keys past the context a causal chunk adds (T = 1 if 0)
     // one workgroup per possible tile when they all fit on the device at once
-    // (grid NC x Hkv x B; tiles past the length exit at once): no lengths
+    // (grid Hkv x NC x B; tiles past the length exit at once): no lengths
     // staged, no counting pass; the persistent walk would give every
     // workgroup one item and fold nothing there either, so both compute the
     // same tiles in the same way
@@ -242,7 +242,7 @@ hipError_t launch_verify_dk(const Plan& pl, const PartialParams& pp, hipStream_t
     const long long res1 = resident_blocks(fn1, 64 * kVerifyWaves, pl.mfma_lds_bytes);
     if (res1 <= 0) return hipErrorInvalidDeviceFunction;
     if (items <= res1) {
-        hipLaunchKernelGGL((verify_partial_mfma<D, KB, true>), dim3((unsigned)pl.NC, (unsigned)pl.Hkv, (unsigned)pl.B),
+        hipLaunchKernelGGL((verify_partial_mfma<D, KB, true>), dim3((unsigned)pl.Hkv, (unsigned)pl.NC, (unsigned)pl.B),
                            dim3(64 * kVerifyWaves), pl.mfma_lds_bytes, s, pp.lens, pp.k, pp.v, pp.q, pl.S_max,
                            pl.chunk, pl.Hkv, g_magic, pl.G, tok_add, pp);
         return hipGetLastError();
@@ -335,7 +335,7 @@ int run_merge(const Plan& pl, const int32_t* lens, int causal, void* out, int ou
     mp.out = out;
     mp.out_bf16 = out_dtype == DECATTN_OUT_BF16;
     mp.T = pl.T; mp.S_max = pl.S_max; mp.chunk = pl.chunk; mp.causal = causal;
-    const dim3 grid(pl.Hq, pl.T, pl.B);
+    const dim3 grid(pl.Hkv, pl.RT, pl.B);
     // slots of the merge's first batch: ceil(NC / 8) tile lanes' worth,
     // rounded up to a power of two, at most kMergeUnroll
     // ceil(2^32 / G) (G >= 2; unused at G = 1): h / G = mulhi(h, g_recip) for h < 2^28

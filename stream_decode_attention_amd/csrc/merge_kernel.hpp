@@ -47,7 +47,7 @@ __host__ __device__ constexpr int merge_threads(int D) { return 2 * D; }
 constexpr int kMergeUnroll = 8;
 
 // ws_ml [B][Hkv][NC][RT][2], ws_acc [B][Hkv][NC][RT][D], lens [B]; one
-// workgroup per output row, grid (Hq, T, B). NU0: slots of the first batch,
+// workgroup per output row, grid (Hkv, T * G, B). NU0: slots of the first batch,
 // ceil(NC / 8) rounded up to 1, 2, 4 or 8 by the host (a slot past every
 // row's tiles loads a clamped duplicate that the select drops), so that the
 // first batch is straight-line code. NWT: waves per row, 2 * D / 64, or one
@@ -64,11 +64,10 @@ lse_merge(const float* ws_ml_, const float* ws_acc_, const int32_t* lens, int G,
     __shared__ float s_m[kMergeThreads / 64];
     __shared__ float s_l[kMergeThreads / 64];
 
-    const int h = blockIdx.x, i = blockIdx.y, b = blockIdx.z;
-    // h / G as a multiply-high by g_recip = ceil(2^32 / G) (exact for
-    // h < 2^28, G <= 8); for G = 1 the host passes 0 and the select adds h
-    const int kvh = (int)__umulhi((uint32_t)h, g_recip) + (g_recip == 0u ? h : 0);
-    const int r = i * G + (h - kvh * G);
+    // the kv head is the fastest grid dimension, as in the one-round partial
+    // grids, so a row is merged on the XCD that wrote its tiles when Hkv is
+    // a multiple of 8
+    const int kvh = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
 
     const size_t head0 = (size_t)(b * Hkv + kvh) * NC * RT;   // tile 0, row 0
     const float* ml = ws_ml_ + head0 * 2;
@@ -110,10 +109,15 @@ lse_merge(const float* ws_ml_, const float* ws_acc_, const int32_t* lens, int G,
     asm volatile("" ::: "memory");
 
     const int len = lens[b];
+    // query token i = r / G as a multiply-high by g_recip = ceil(2^32 / G)
+    // (exact for r < 2^28, G <= 8); for G = 1 the host passes 0 and the
+    // select adds r
+    const int i = (int)__umulhi((uint32_t)r, g_recip) + (g_recip == 0u ? r : 0);
+    const int h = kvh * G + (r - i * G);
     const int n = clamp_len_add(len, p.causal ? i + 1 : 0, p.S_max);
     int na = (n + p.chunk - 1) >> __builtin_ctz(p.chunk);   // chunk is a power of two
     na = na < NC ? na : NC;
-    const size_t row = ((size_t)b * p.T + i) * (size_t)gridDim.x + h;   // (b, i, h) flattened
+    const size_t row = ((size_t)b * p.T + i) * (size_t)(Hkv * G) + h;   // (b, i, h) flattened
 
     if (na == 0) {
 #pragma unroll

@@ -183,7 +183,7 @@ __device__ __forceinline__ void gather_all_i(int x, int (&out)[8]) {
 }
 
 // ONE_ROUND: every possible work item has a workgroup of its own (the host
-// launches a grid of (tile, kv head, sequence) when they all fit on the
+// launches a grid of (kv head, tile, sequence) when they all fit on the
 // device at once and one row block holds every row), so a workgroup knows its
 // tile from its index alone, with no division. Its
 // first K/V loads are written over the whole tile (keys up to t1 lie inside
@@ -511,10 +511,10 @@ split_kv_partial(const int32_t* lens, const uint16_t* kc, const uint16_t* vc, co
     // (one spare set of query registers), and every item ends at the end of a
     // ring cycle, where it is combined.
     if constexpr (ONE_ROUND) {
-        // grid (NC, Hkv, B), one row block: the work item is the block index
+        // grid (Hkv, NC, B), one row block: the work item is the block index
         Tile tl;
-        tl.c = blockIdx.x;
-        tl.kvh = blockIdx.y;
+        tl.kvh = blockIdx.x;
+        tl.c = blockIdx.y;
         tl.b = blockIdx.z;
         tl.rblk = 0;
         tl.t0 = tl.c * chunk;

@@ -374,11 +374,11 @@ verify_partial_mfma(const int32_t* lens, const uint16_t* kc, const uint16_t* vc,
     };
 
     if constexpr (ONE_ROUND) {
-        // grid (NC, Hkv, B), every possible tile at once: the work item is the
+        // grid (Hkv, NC, B), every possible tile at once: the work item is the
         // block index (no lengths staged, no counting, no folding). The
         // length's load and the query loads (whose addresses need only the
         // preloaded leading arguments) are issued together at wave start.
-        const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+        const int kvh = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
         const int len = lens[b];
         uint4 qv[KS];
         load_q(b, kvh, qv);
