@@ -338,7 +338,7 @@ int run_merge(const Plan& pl, const int32_t* lens, int causal, void* out, int ou
     const dim3 grid(pl.Hkv, pl.RT, pl.B);
     // slots of the merge's first batch: ceil(NC / 8) tile lanes' worth,
     // rounded up to a power of two, at most kMergeUnroll
-    // ceil(2^32 / G) (G >= 2; unused at G = 1): h / G = mulhi(h, g_recip) for h < 2^28
+    // ceil(2^32 / G) (G >= 2; unused at G = 1): r / G = mulhi(r, g_recip) for r < 2^28
     const uint32_t g_recip = pl.G == 1 ? 0u : (uint32_t)(((1ull << 32) + pl.G - 1) / pl.G);
     const int need = (pl.NC + 7) / 8;
     const int nu0 = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
