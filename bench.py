@@ -309,6 +309,17 @@ def main():
     us_one = back_to_back_us(torch, stream, g_one, K, W, busy=flush)
     us_one_floor = back_to_back_us(torch, stream, g_one_floor, K, W, busy=flush)
     cold_med, cold_p10, cold_p90 = cold_us(torch, stream, g_one, max(20, args.steps // 2), flush)
+
+    # one call launched eagerly (two kernel launches on the stream, no graph):
+    # the same lone call without a graph launch's own cost
+    class Eager:
+        def __init__(self, fn):
+            self.replay = fn
+    e_one = [Eager(call(i)) for i in range(2)]
+    us_eager = back_to_back_us(torch, stream, e_one, K, W, busy=flush)
+    us_eager_floor = back_to_back_us(torch, stream, [Eager(call(i, zero_lens)) for i in range(2)], K, W,
+                                     busy=flush)
+    eager_med, eager_p10, eager_p90 = cold_us(torch, stream, e_one, max(20, args.steps // 2), flush)
     # cold inside a step's graph: each call follows a 512 MiB read (twice the
     # Infinity Cache), as a layer's attention call follows other reads in a
     # decode step; per call = graph(flush, call, flush, call, ...) minus
@@ -333,7 +344,8 @@ def main():
     achieved = kv_bytes / (us_part / 1e6) / 1e9
     log(f"workload 4: {us_call:.1f} us/call ({value:.0f} GB/s), {K} calls in one graph; partial kernel "
         f"{us_part:.1f} us = {achieved:.0f} GB/s; launch floor {us_floor:.1f} us/call; one call per "
-        f"graph {us_one:.1f} us (floor {us_one_floor:.1f}), cold {cold_med:.1f} us; cold inside a graph "
+        f"graph {us_one:.1f} us (floor {us_one_floor:.1f}), cold {cold_med:.1f} us; eager {us_eager:.1f} us "
+        f"(floor {us_eager_floor:.1f}), cold {eager_med:.1f} us; cold inside a graph "
         f"{cold_graph:.1f} us ({kv_bytes / cold_graph / 1e3:.0f} GB/s)")
 
     traffic = load_traffic(w4.name, chunk)
@@ -377,6 +389,13 @@ def main():
             "cold_us": {"median": round(cold_med, 2), "p10": round(cold_p10, 2), "p90": round(cold_p90, 2)},
             "cold_GBps": round(kv_bytes / (cold_med / 1e6) / 1e9, 1),
             "cold_frac_of_hbm_peak": round(kv_bytes / (cold_med / 1e6) / 1e9 / rf.HBM_PEAK_GBPS, 4)},
+        "one_call_eager": {
+            "what": "decode_attn launched on the stream with no graph: its two kernels back to back, warm, "
+                    "and each call after the 1 GiB flush (the host enqueues it while the flush runs)",
+            "us_per_call": round(us_eager, 2), "launch_floor_us": round(us_eager_floor, 2),
+            "cold_us": {"median": round(eager_med, 2), "p10": round(eager_p10, 2), "p90": round(eager_p90, 2)},
+            "cold_GBps": round(kv_bytes / (eager_med / 1e6) / 1e9, 1),
+            "cold_frac_of_hbm_peak": round(kv_bytes / (eager_med / 1e6) / 1e9 / rf.HBM_PEAK_GBPS, 4)},
         "cold_in_graph": {
             "us_per_call": round(cold_graph, 2), "calls_per_graph": KC, "flush_bytes": 1 << 29,
             "us_per_call_rounds": [round(x, 2) for x in cold_rounds],
