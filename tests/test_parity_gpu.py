@@ -294,6 +294,26 @@ def test_every_group_size(D, G):
     _both_modes(c, ref, chunk=64)
 
 
+@pytest.mark.parametrize("T,G,D,chunk", [(1, 2, 64, 64), (1, 8, 64, 64), (3, 2, 128, 64), (6, 3, 128, 128),
+                                         (6, 3, 128, 64)])
+def test_one_round_grids_with_many_kv_heads_and_sequences(T, G, D, chunk):
+    """The one-round grids (kv head, tile, sequence) and the merge grid (kv head,
+    group row, sequence): 12 kv heads (not a multiple of 8) over 3 sequences of
+    ragged lengths, decode and chunk calls, vector and matrix-core kernels (the
+    last case has more possible tiles than the matrix-core kernel's resident
+    workgroups: the persistent walk beside the same merge grid)."""
+    Hkv, S = 12, 512
+    lens = [S - T, 1, 300] if T > 1 else [S, 1, 300]
+    c = workloads.make_case(3, G * Hkv, Hkv, D, S, lens, T=T, seed=7 * G + T + D)
+    if T == 1:
+        ref = oracle.decode_attention(c["q"], c["k"], c["v"], c["lens"], c["scale"])
+        _both_modes(c, ref, chunk=chunk)
+    else:
+        ref = oracle.chunk_attention(c["q"], c["k"], c["v"], c["lens"], c["scale"])
+        assert_f32_close(run_chunk(c, chunk=chunk), ref)
+        assert_bf16_close(run_chunk(c, chunk=chunk, out_dtype=torch.bfloat16), ref)
+
+
 @pytest.mark.parametrize("n", [1, 31, 32, 33, 63, 64, 65, 255, 256])
 def test_length_boundaries(n):
     c = workloads.make_case(1, 6, 2, 64, 256, [n], seed=n)
