@@ -94,7 +94,12 @@ size_t decattn_workspace_bytes(int B, int T, int Hq, int Hkv, int D, int S_max, 
  *              16-byte aligned; overwritten, may be reused between calls on the
  *              same stream
  *   chunk      keys per split tile; 0 = decattn_default_chunk()
- * Launches two kernels (partial tiles, then the merge) on `stream`. */
+ * Launches two kernels (partial tiles, then the merge) on `stream`.
+ * Precision: fp32 scores, softmax statistics and accumulation. The vector
+ * kernel weights V with fp32 softmax weights; the matrix-core kernel (see
+ * chunk_attn) carries them as bf16 hi + lo parts (about 16 bits) for fp32
+ * output and as bf16 (each within 2^-9 of itself, below the output's own
+ * rounding step) for bf16 output. */
 int decode_attn(const void* q, const void* k_cache, const void* v_cache,
                 const int32_t* seq_lens,
                 int B, int Hq, int Hkv, int D, int S_max, float scale,
@@ -136,9 +141,11 @@ int decode_attn_noalloc(const void* q, const void* k_cache, const void* v_cache,
  *   out        [B][T][Hq][D]
  *   workspace  >= decattn_workspace_bytes(B, T, Hq, Hkv, D, S_max, chunk)
  * Other arguments as decode_attn. Row (i, h) equals decode_attn on the same
- * cache with seq_lens = ctx + i + 1 and the same chunk: bit for bit when both
- * calls run on the same kernel, and to fp32 rounding (|diff| <= 1e-4 of O(1)
- * outputs) otherwise, since the two kernels sum q.k in different orders. The
+ * cache with seq_lens = ctx + i + 1, the same chunk and output type: bit for
+ * bit when both calls run on the same kernel, and otherwise to fp32 rounding
+ * (|diff| <= 1e-4 of O(1) fp32 outputs; bf16 outputs within the bf16
+ * tolerance of the exact result), since the two kernels sum q.k in different
+ * orders and weight V at the precisions decode_attn states. The
  * matrix-core kernel runs a chunk call when T*G <= 32 rows per kv head and
  * chunk is a multiple of 128 (the default chunk is), and a decode call when
  * G >= 8 and chunk is a multiple of 128; the vector kernel runs the others. */

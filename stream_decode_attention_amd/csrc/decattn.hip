@@ -89,8 +89,8 @@ int pick_default_chunk(int B, int T, int G, int Hkv, int D, int S_max) {
     if (T > 1 && T * G <= kVerifyMaxRows) {
         const long long rows = (long long)B * Hkv;
         const long long n256 = rows * ((S_max + 255) / 256), n512 = rows * ((S_max + 511) / 512);
-        const void* fn = D == 64 ? reinterpret_cast<const void*>(&verify_partial_mfma<64, 1, true>)
-                                 : reinterpret_cast<const void*>(&verify_partial_mfma<128, 1, true>);
+        const void* fn = D == 64 ? reinterpret_cast<const void*>(&verify_partial_mfma<64, 1, true, true>)
+                                 : reinterpret_cast<const void*>(&verify_partial_mfma<128, 1, true, true>);
         const long long cap = resident_blocks(fn, 64 * kVerifyWaves, verify_lds_bytes(D, T * G, B));
         return (n256 > cap && n512 <= cap) ? 512 : 256;
     }
@@ -228,7 +228,7 @@ hipError_t launch_partial_dr(const Plan& pl, const PartialParams& pp, hipStream_
     return hipGetLastError();
 }
 
-template <int D, int KB>
+template <int D, int KB, bool SPLIT>
 hipError_t launch_verify_dk(const Plan& pl, const PartialParams& pp, hipStream_t s) {
     const long long items = (long long)pl.B * pl.Hkv * pl.NC;   // every possible tile
     const int g_magic = g_magic_for(pl.G);             // r / G = (r * g_magic) >> 16 for r < 8192
@@ -238,29 +238,29 @@ hipError_t launch_verify_dk(const Plan& pl, const PartialParams& pp, hipStream_t
     // staged, no counting pass; the persistent walk would give every
     // workgroup one item and fold nothing there either, so both compute the
     // same tiles in the same way
-    const void* fn1 = reinterpret_cast<const void*>(&verify_partial_mfma<D, KB, true>);
+    const void* fn1 = reinterpret_cast<const void*>(&verify_partial_mfma<D, KB, true, SPLIT>);
     const long long res1 = resident_blocks(fn1, 64 * kVerifyWaves, pl.mfma_lds_bytes);
     if (res1 <= 0) return hipErrorInvalidDeviceFunction;
     if (items <= res1) {
-        hipLaunchKernelGGL((verify_partial_mfma<D, KB, true>), dim3((unsigned)pl.Hkv, (unsigned)pl.NC, (unsigned)pl.B),
+        hipLaunchKernelGGL((verify_partial_mfma<D, KB, true, SPLIT>), dim3((unsigned)pl.Hkv, (unsigned)pl.NC, (unsigned)pl.B),
                            dim3(64 * kVerifyWaves), pl.mfma_lds_bytes, s, pp.lens, pp.k, pp.v, pp.q, pl.S_max,
                            pl.chunk, pl.Hkv, g_magic, pl.G, tok_add, pp);
         return hipGetLastError();
     }
-    const void* fn = reinterpret_cast<const void*>(&verify_partial_mfma<D, KB, false>);
+    const void* fn = reinterpret_cast<const void*>(&verify_partial_mfma<D, KB, false, SPLIT>);
     long long grid = resident_blocks(fn, 64 * kVerifyWaves, pl.mfma_lds_bytes);
     if (grid <= 0) return hipErrorInvalidDeviceFunction;
     if (grid > items) grid = items;
-    hipLaunchKernelGGL((verify_partial_mfma<D, KB, false>), dim3((unsigned)grid), dim3(64 * kVerifyWaves),
+    hipLaunchKernelGGL((verify_partial_mfma<D, KB, false, SPLIT>), dim3((unsigned)grid), dim3(64 * kVerifyWaves),
                        pl.mfma_lds_bytes, s, pp.lens, pp.k, pp.v, pp.q, pl.S_max, pl.chunk, pl.Hkv, g_magic, pl.G,
                        tok_add, pp);
     return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_partial_d(const Plan& pl, const PartialParams& pp, hipStream_t s) {
+hipError_t launch_partial_d(const Plan& pl, const PartialParams& pp, bool split_p, hipStream_t s) {
     if (pl.mfma)
-        return launch_verify_dk<D, 1>(pl, pp, s);
+        return split_p ? launch_verify_dk<D, 1, true>(pl, pp, s) : launch_verify_dk<D, 1, false>(pl, pp, s);
     switch (pl.R) {
         case 1: return launch_partial_dr<D, 1>(pl, pp, s);
         case 2: return launch_partial_dr<D, 2>(pl, pp, s);
@@ -309,8 +309,11 @@ float log2_scale(float scale) {
     return scale < 0.f ? -qmag : qmag;
 }
 
+// split_p: the matrix-core kernel carries the softmax weights as bf16 hi + lo
+// parts in p.V (fp32 output, and the partial state of attn_partial, whose
+// output type is not known yet) or as bf16 (bf16 output)
 int run_partial(const Plan& pl, const void* q, const void* k, const void* v, const int32_t* lens,
-                float scale, int causal, void* ws, hipStream_t s) {
+                float scale, int causal, void* ws, bool split_p, hipStream_t s) {
     PartialParams pp{};
     pp.q = static_cast<const uint16_t*>(q);
     pp.k = static_cast<const uint16_t*>(k);
@@ -323,7 +326,7 @@ int run_partial(const Plan& pl, const void* q, const void* k, const void* v, con
     pp.B = pl.B;
     pp.lds_main = (int)pl.mfma_lds_main;
     pp.qscale = log2_scale(scale);
-    const hipError_t e = pl.D == 64 ? launch_partial_d<64>(pl, pp, s) : launch_partial_d<128>(pl, pp, s);
+    const hipError_t e = pl.D == 64 ? launch_partial_d<64>(pl, pp, split_p, s) : launch_partial_d<128>(pl, pp, split_p, s);
     return e == hipSuccess ? DECATTN_OK : DECATTN_ERR_HIP;
 }
 
@@ -399,7 +402,8 @@ int attention(const void* q, const void* k, const void* v, const int32_t* lens, 
     if ((st = check_common(q, k, v, lens, scale, ws, ws_bytes, pl)) != DECATTN_OK) return st;
     if ((st = check_out(out, out_dtype)) != DECATTN_OK) return st;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    if ((st = run_partial(pl, q, k, v, lens, scale, causal, ws, s)) != DECATTN_OK) return st;
+    if ((st = run_partial(pl, q, k, v, lens, scale, causal, ws, out_dtype != DECATTN_OUT_BF16, s)) != DECATTN_OK)
+        return st;
     return run_merge(pl, lens, causal, out, out_dtype, ws, s);
 }
 
@@ -668,7 +672,9 @@ int decode_attn_noalloc(const void* q, const void* k_cache, const void* v_cache,
     void* ws = scratch_for_current_device();    // the device address, never `scratch` itself
     if (!ws) return DECATTN_ERR_HIP;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    if ((st = run_partial(pl, q, k_cache, v_cache, seq_lens, scale, 0, ws, s)) != DECATTN_OK) return st;
+    if ((st = run_partial(pl, q, k_cache, v_cache, seq_lens, scale, 0, ws, out_dtype != DECATTN_OUT_BF16, s)) !=
+        DECATTN_OK)
+        return st;
     return run_merge(pl, seq_lens, 0, out, out_dtype, ws, s);
 }
 
@@ -689,7 +695,7 @@ int attn_partial(const void* q, const void* k_cache, const void* v_cache, const 
     if (st != DECATTN_OK) return st;
     if ((st = check_common(q, k_cache, v_cache, lens, scale, workspace, workspace_bytes, pl)) != DECATTN_OK)
         return st;
-    return run_partial(pl, q, k_cache, v_cache, lens, scale, causal, workspace,
+    return run_partial(pl, q, k_cache, v_cache, lens, scale, causal, workspace, true,
                        static_cast<hipStream_t>(stream));
 }
 

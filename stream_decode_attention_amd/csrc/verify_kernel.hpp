@@ -20,9 +20,12 @@
 //    16-byte writes; the A operand (V^T) is read back with the gfx950
 //    transposing LDS load (ds_read_b64_tr_b16), which hands each lane four
 //    consecutive keys at one dim, in the key order the S^T registers give P,
-//    so the B operand (P) is packed from registers as is. P is split into
-//    bf16 hi + lo parts (two MFMAs) so the product keeps about 16 bits of P
-//    (fp32 output error below 1e-4), V being exact in bf16.
+//    so the B operand (P) is packed from registers as is. Precision follows
+//    the output (SPLIT): for fp32 output P is split into bf16 hi + lo parts
+//    (two MFMAs), so the product keeps about 16 bits of P (error below 1e-4),
+//    V being exact in bf16; for bf16 output P is rounded once to bf16 (one
+//    MFMA; each weight within 2^-9 of itself, under the output's own
+//    rounding step).
 //  * the four waves of a workgroup split each sub-tile's keys (32 each);
 //    sub-tiles stream through a ring of two register buffers, and the waves
 //    are combined through LDS into the tile's partial state, written in the
@@ -94,7 +97,7 @@ __device__ __forceinline__ uint2 lds_read_tr16_b64(const char* p) {
 // call (T = 1, every row attends j < len). These 14 dwords are all the
 // hardware preloads, so nothing before the first loads waits for the
 // kernel-argument segment.
-template <int D, int KB, bool ONE_ROUND>
+template <int D, int KB, bool ONE_ROUND, bool SPLIT>
 __global__ void __launch_bounds__(256)
 verify_partial_mfma(const int32_t* lens, const uint16_t* kc, const uint16_t* vc, const uint16_t* qp, int S_max,
                     int chunk, int Hkv, int g_magic, int G, int tok_add, const PartialParams p) {
@@ -253,7 +256,8 @@ verify_partial_mfma(const int32_t* lens, const uint16_t* kc, const uint16_t* vc,
             }
             m_run = m_new;
 
-            // P = 2^(s - m), split into bf16 hi + lo, packed as B operands
+            // P = 2^(s - m) as bf16 (hi), plus the rounding remainder as bf16
+            // (lo) when SPLIT, packed as B operands
             uint4 bhi[KB][2], blo[KB][2];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
@@ -270,11 +274,12 @@ verify_partial_mfma(const int32_t* lens, const uint16_t* kc, const uint16_t* vc,
                     for (int e = 0; e < 4; ++e) {
                         const float a0 = pv[8 * j + 2 * e], a1 = pv[8 * j + 2 * e + 1];
                         hw[e] = pack_bf16x2(a0, a1);
-                        lw[e] = pack_bf16x2(a0 - __uint_as_float(hw[e] << 16),
-                                            a1 - __uint_as_float(hw[e] & 0xFFFF0000u));
+                        if constexpr (SPLIT)
+                            lw[e] = pack_bf16x2(a0 - __uint_as_float(hw[e] << 16),
+                                                a1 - __uint_as_float(hw[e] & 0xFFFF0000u));
                     }
                     bhi[kb][j] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-                    blo[kb][j] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+                    if constexpr (SPLIT) blo[kb][j] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
                 }
             }
 
@@ -293,7 +298,8 @@ verify_partial_mfma(const int32_t* lens, const uint16_t* kc, const uint16_t* vc,
                         const uint2 a1 = lds_read_tr16_b64(ap + 8 * VROW);
                         const uint4 a = make_uint4(a0.x, a0.y, a1.x, a1.y);
                         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(bhi[kb][j]), acc[db], 0, 0, 0);
-                        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(blo[kb][j]), acc[db], 0, 0, 0);
+                        if constexpr (SPLIT)
+                            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(blo[kb][j]), acc[db], 0, 0, 0);
                     }
                 }
             }
