@@ -244,7 +244,11 @@ int spec_accept(const float* logits, const float* q, const int32_t* drafts, cons
  * that time them apart or merge partial state produced elsewhere.
  * `causal` = 0 gives decode (T must be 1, lens = seq_lens); 1 gives chunk
  * (lens = ctx_lens). attn_partial writes the workspace; attn_merge reads it and
- * must be given the same shapes, lens, causal flag and chunk. */
+ * must be given the same shapes, lens, causal flag and chunk. attn_partial
+ * does not know the output type, so it keeps the fp32-output precision (on
+ * the matrix cores, softmax weights as bf16 hi + lo): the pair equals
+ * decode_attn / chunk_attn bit for bit for fp32 output, and for bf16 output
+ * wherever the vector kernel runs. */
 int attn_partial(const void* q, const void* k_cache, const void* v_cache,
                  const int32_t* lens,
                  int B, int T, int Hq, int Hkv, int D, int S_max, float scale, int causal,
