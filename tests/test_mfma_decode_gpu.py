@@ -132,3 +132,23 @@ def test_graph_replay_follows_device_lengths():
         got = out.clone()
         assert_f32_close(got, oracle.decode_attention(c["q"], c["k"], c["v"], n, c["scale"]))
         assert torch.equal(got, run_decode(c, chunk=128, lens=n, tensors=(q, k, v))), f"replay {trial}"
+
+
+def test_phases_separately_keep_the_fp32_output_precision():
+    """attn_partial does not know the output type, so on the matrix cores it
+    keeps the softmax weights as bf16 hi + lo: the pair equals decode_attn bit
+    for bit with fp32 output and stays within the bf16 tolerance with bf16."""
+    c = workloads.make_case(2, G * 2, 2, 128, 1024, [1024, 500], seed=340)
+    q, k, v = dev_bits(c["q"]), dev_bits(c["k"]), dev_bits(c["v"])
+    lens = dev_lens(c["lens"])
+    ref = oracle.decode_attention(c["q"], c["k"], c["v"], c["lens"], c["scale"])
+    ws = workspace(2, 1, G * 2, 2, 128, 1024, 128)
+    for dt in (torch.float32, torch.bfloat16):
+        out = torch.empty((2, G * 2, 128), dtype=dt, device="cuda")
+        sda.attn_partial(q, k, v, lens, c["scale"], ws, chunk=128)
+        sda.attn_merge(lens, out, ws, T=1, Hq=G * 2, Hkv=2, S_max=1024, chunk=128)
+        torch.cuda.synchronize()
+        if dt == torch.float32:
+            assert torch.equal(out, run_decode(c, chunk=128, tensors=(q, k, v)))
+        else:
+            assert_bf16_close(out, ref)
