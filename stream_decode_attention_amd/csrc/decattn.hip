@@ -339,11 +339,12 @@ int run_merge(const Plan& pl, const int32_t* lens, int causal, void* out, int ou
     mp.out_bf16 = out_dtype == DECATTN_OUT_BF16;
     mp.T = pl.T; mp.S_max = pl.S_max; mp.chunk = pl.chunk; mp.causal = causal;
     const dim3 grid(pl.Hkv, pl.RT, pl.B);
-    // slots of the merge's first batch: ceil(NC / 8) tile lanes' worth,
-    // rounded up to a power of two, at most kMergeUnroll
     // ceil(2^32 / G) (G >= 2; unused at G = 1): r / G = mulhi(r, g_recip) for r < 2^28
     const uint32_t g_recip = pl.G == 1 ? 0u : (uint32_t)(((1ull << 32) + pl.G - 1) / pl.G);
-    const int need = (pl.NC + 7) / 8;
+    // slots of the merge's first batch: ceil(NC / tile lanes), rounded up to
+    // a power of two, at most kMergeUnroll
+    const int ncl = merge_threads(pl.D) / (pl.D / 4);   // tile lanes of a workgroup
+    const int need = (pl.NC + ncl - 1) / ncl;
     const int nu0 = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
     auto launch = [&](auto d_tag, auto nu_tag) {
         constexpr int DD = decltype(d_tag)::value, NU = decltype(nu_tag)::value;

@@ -36,21 +36,22 @@ struct MergeParams {
     int T, S_max, chunk, causal;
 };
 
-// Threads per row: 8 tile lanes of D / 4 threads (128 at D = 64, 256 at
-// D = 128), each loading 8 tiles per batch, so 64 tiles per round trip. On
-// MI355X this is about 0.2 us faster per call than 512 threads of 4 tiles:
-// fewer waves to start and to join through LDS.
+// Threads per row: 256, tile lanes of D / 4 threads (16 lanes at D = 64, 8
+// at D = 128), each loading up to 8 tiles per batch. Measured on MI355X: at
+// D = 128 this is about 0.2 us faster per call than 512 threads of 4 tiles
+// (fewer waves to start and to join through LDS) and than 128 threads of 8;
+// at D = 64 it is 0.08 us faster than 128 threads on 64-tile rows.
 // One wave of 16 tiles per thread (no LDS join) took 0.4 us longer on short
 // calls and 1.5 us longer on a 32-tile row: its 48 loads issue one after
 // another from one wave.
-__host__ __device__ constexpr int merge_threads(int D) { return 2 * D; }
+__host__ __device__ constexpr int merge_threads(int) { return 256; }
 constexpr int kMergeUnroll = 8;
 
 // ws_ml [B][Hkv][NC][RT][2], ws_acc [B][Hkv][NC][RT][D], lens [B]; one
 // workgroup per output row, grid (Hkv, T * G, B). NU0: slots of the first batch,
-// ceil(NC / 8) rounded up to 1, 2, 4 or 8 by the host (a slot past every
-// row's tiles loads a clamped duplicate that the select drops), so that the
-// first batch is straight-line code. NWT: waves per row, 2 * D / 64, or one
+// ceil(NC / tile lanes) rounded up to 1, 2, 4 or 8 by the host (a slot past
+// every row's tiles loads a clamped duplicate that the select drops), so that
+// the first batch is straight-line code. NWT: waves per row, 4, or one
 // when one wave's tile lanes (64 / (D / 4)) hold every tile slot; it then
 // needs no join through LDS and no barrier.
 template <int D, int NU0, int NWT>

@@ -214,7 +214,7 @@ def test_persistent_walk_graph_replay_follows_device_lengths():
 
 def test_row_with_more_tiles_than_one_merge_batch():
     """1250 tiles in one row: the merge folds them in batches of 64 (8 tile
-    lanes of eight slots), 20 rounds."""
+    lanes of eight slots at D = 128), 20 rounds."""
     c = workloads.make_case(2, 4, 1, 128, 40000, [40000, 17000], seed=41)
     ref = oracle.decode_attention(c["q"], c["k"], c["v"], c["lens"], c["scale"])
     assert_f32_close(run_decode(c, chunk=32), ref)
@@ -222,8 +222,8 @@ def test_row_with_more_tiles_than_one_merge_batch():
 
 
 def test_row_with_more_tiles_than_one_merge_batch_d64():
-    """D = 64: 1000 tiles in the first row (16 batches of 64, the last one
-    partial), 129 in the second (one tile into the third batch), and a row of
+    """D = 64: 1000 tiles in the first row (8 batches of 128, the last one
+    partial), 129 in the second (one tile into the second batch), and a row of
     0 keys."""
     c = workloads.make_case(3, 6, 2, 64, 16000, [16000, 2064, 0], seed=42)
     ref = oracle.decode_attention(c["q"], c["k"], c["v"], c["lens"], c["scale"])
@@ -233,9 +233,10 @@ def test_row_with_more_tiles_than_one_merge_batch_d64():
 
 @pytest.mark.parametrize("D", [64, 128])
 def test_tile_counts_around_one_merge_batch(D):
-    """The merge takes 64 tiles per round trip: rows of 63, 64 and 65 tiles
-    (the 65th holding one key), 128 and 129, next to an empty row."""
-    lens = [63 * 16 - 5, 64 * 16, 64 * 16 + 1, 128 * 16, 128 * 16 + 1, 0]
+    """The merge takes 64 tiles per round trip at D = 128 and 128 at D = 64:
+    rows of 63, 64 and 65 tiles (the 65th holding one key), 127, 128 and 129,
+    next to an empty row."""
+    lens = [63 * 16 - 5, 64 * 16, 64 * 16 + 1, 127 * 16 - 3, 128 * 16, 128 * 16 + 1, 0]
     c = workloads.make_case(len(lens), 4, 2, D, 2064, lens, seed=43 + D)
     ref = oracle.decode_attention(c["q"], c["k"], c["v"], c["lens"], c["scale"])
     assert_f32_close(run_decode(c, chunk=16), ref)
