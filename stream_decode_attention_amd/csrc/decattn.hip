@@ -66,12 +66,14 @@ struct Plan {
 
 int resident_blocks(const void* kernel, int threads, size_t lds);
 
-// Dynamic LDS of the matrix-core kernel: the larger of the four waves' V
-// tiles and the cross-wave combine area, then the B staged lengths.
+// Dynamic LDS of the matrix-core kernel: the four waves' V tiles, the
+// cross-wave combine area after them (not aliased: a wave stores its state
+// without waiting for the others' last V reads; at most 108 KB at D = 128
+// and 32 rows), then the B staged lengths (at most 16 KB).
 size_t verify_lds_bytes(int D, int RT, int B, size_t* main_bytes = nullptr) {
     const size_t vt = (size_t)kVerifyWaves * 32 * verify_vrow(D);
     const size_t comb = (size_t)verify_comb_floats(RT, D) * sizeof(float);
-    const size_t main = vt > comb ? vt : comb;
+    const size_t main = vt + comb;
     if (main_bytes) *main_bytes = main;
     return main + (size_t)B * sizeof(int);
 }

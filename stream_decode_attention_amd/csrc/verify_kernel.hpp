@@ -130,8 +130,10 @@ verify_partial_mfma(const int32_t* lens, const uint16_t* kc, const uint16_t* vc,
     const int T = tok_add > 0 ? tok_add : 1;                     // query tokens
     const int RT = T * G;                                        // rows per kv head
     constexpr int CST = D + 4;                                   // combine row stride (floats)
-    float* c_acc = smem;                                         // [waves][RT][CST]  (aliases the V tiles)
-    float* c_ml = smem + (size_t)kVerifyWaves * RT * CST;      // [waves][RT][2]
+    // the combine area follows the V tiles (no aliasing), so a wave stores its
+    // state as soon as its own last sub-tile is done, with no barrier first
+    float* c_acc = smem + (size_t)kVerifyWaves * WK * VROW / sizeof(float);   // [waves][RT][CST]
+    float* c_ml = c_acc + (size_t)kVerifyWaves * RT * CST;     // [waves][RT][2]
     int* s_len = reinterpret_cast<int*>(reinterpret_cast<char*>(smem) + p.lds_main);
 
     // One work item per attended tile (keys j < ctx + T) of every (b, kvh);
@@ -319,12 +321,11 @@ verify_partial_mfma(const int32_t* lens, const uint16_t* kc, const uint16_t* vc,
             compute(vr[1], kr[1], sub + SUB);
         }
 
-        // ---- combine the waves (LDS aliases the V tiles: wait for all reads)
+        // ---- combine the waves
         {
             const f32x2 sw = swap32(l_run, l_run);
             l_run = sw.x + sw.y;
         }
-        __syncthreads();
         if (row_ok) {
 #pragma unroll
             for (int db = 0; db < DB; ++db)
